@@ -1,0 +1,169 @@
+/*
+ * sscan.h -- C ABI of libsscan, the selective state-space scan for AMD MI355X (gfx950).
+ *
+ * The scan (sources by page title and section):
+ *   "Mamba" (nnterp guide, architectures), opening paragraph and section
+ *   "The values": per channel of the mixer's inner width, a state of state_dim
+ *   numbers updated for each token as
+ *       h = exp(dt * A) * h + dt * B * x,      y = C . h + D * x,
+ *   with the step dt = softplus(dt_raw + dt_bias) per token and channel, A per
+ *   channel and state dimension, B and C from one group shared by every channel,
+ *   state_input None (zeros) on a prompt and state_output the state after the
+ *   call's last token. "Mamba" (tokentrails lineage), section "Code":
+ *   A = -exp(A_log), and the mixer's output is y * silu(z).
+ *   "Falcon-Mamba" (nnterp encyclopedia), section "Where the norms sit":
+ *   B and C pass a weightless RMS norm over state_dim before the scan.
+ *   "Mamba-2" (nnterp encyclopedia), sections "The mixer's values" and
+ *   "The block, in order": the same recurrence with one scalar decay per head
+ *   and token (decays = softplus(dt + dt_bias) * A) and a state matrix per head;
+ *   y = ssd(...) + D * x, then the gate.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA tensors)
+ *     to a contiguous, row-major, tokens-first array. Host pointers are rejected
+ *     with SSCAN_ERR_NOT_DEVICE (the pages' prior-art kernels also refuse CPU
+ *     tensors).
+ *   - Every tensor pointer must be 16-byte aligned (SSCAN_ERR_ALIGN).
+ *   - "act" tensors (x, dt_raw, z, B, C, y) are float32 or bfloat16 as the
+ *     descriptor says; dt_bias, A_log, D and every state are float32.
+ *   - The caller owns every buffer, including the workspace (size it with the
+ *     *_workspace_size query). The library allocates nothing and never
+ *     synchronizes: work is queued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and the call returns at once.
+ *   - Validation happens before anything is launched. A nonzero status means
+ *     nothing was launched (except SSCAN_ERR_HIP, which reports a failed
+ *     launch). Faults inside a kernel surface at the caller's next sync.
+ *   - Outputs must not overlap inputs (SSCAN_ERR_ALIAS), except that
+ *     sscan_step and sscan_ssd_step may update the state in place
+ *     (state_output == state_input).
+ *   - Thread-safe: the only global state is a thread-local error string and the
+ *     process-wide pointer-check switch (an atomic, see sscan_set_pointer_checks).
+ */
+#ifndef SSCAN_H
+#define SSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSCAN_ABI_VERSION 1
+
+typedef enum { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
+
+typedef enum {
+  SSCAN_OK = 0,
+  SSCAN_ERR_NULL = 1,        /* a required pointer (or the descriptor) is NULL      */
+  SSCAN_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or inconsistent */
+  SSCAN_ERR_DTYPE = 3,       /* act is not SSCAN_F32 / SSCAN_BF16                   */
+  SSCAN_ERR_UNSUPPORTED = 4, /* valid, but not a variant this build implements      */
+  SSCAN_ERR_NOT_DEVICE = 5,  /* a tensor pointer is not device memory               */
+  SSCAN_ERR_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned             */
+  SSCAN_ERR_ALIAS = 7,       /* an output overlaps an input                         */
+  SSCAN_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than the query returned   */
+  SSCAN_ERR_HIP = 9          /* the HIP runtime reported an error                   */
+} sscan_status;
+
+/* Mamba-1 problem. channels is the mixer's inner width (d_inner). ngroups must
+ * divide channels; channel c reads group c / (channels / ngroups). When
+ * ngroups > 1, channels / ngroups must be a multiple of 64. state_dim in 1..64.
+ * bc_rms_eps > 0 applies the weightless RMS norm b / sqrt(mean(b^2) + eps) to
+ * every [state_dim] vector of B and of C before the scan ("Falcon-Mamba",
+ * section "Where the norms sit"); <= 0 reads B and C as given. */
+typedef struct sscan_mamba1_desc {
+  int64_t batch, seqlen, channels, state_dim, ngroups;
+  int32_t act;        /* sscan_dtype of x, dt_raw, z, B, C and y */
+  float bc_rms_eps;
+} sscan_mamba1_desc;
+
+/* Mamba-2 (SSD) problem. nheads heads of head_dim channels each, a
+ * [head_dim, state_dim] state per head; head h reads group h / (nheads / ngroups).
+ * chunk is the interval at which a chunked scan keeps boundary states ("Mamba-2",
+ * section "The state": 256 on the pages' kernel). It does not change the result
+ * beyond rounding; 0 lets the library choose, otherwise a power of two in 16..256. */
+typedef struct sscan_ssd_desc {
+  int64_t batch, seqlen, nheads, head_dim, state_dim, ngroups, chunk;
+  int32_t act;
+  int32_t reserved;   /* must be 0 */
+} sscan_ssd_desc;
+
+/* Bytes of workspace sscan_mamba1_fwd needs for this problem (0 if none). */
+size_t sscan_mamba1_workspace_size(const sscan_mamba1_desc* desc);
+
+/* Mamba-1 selective scan over a prompt ("Mamba", opening paragraph and section
+ * "The values"; "Falcon-Mamba", section "Where the norms sit").
+ *   x, dt_raw     [batch, seqlen, channels]  act
+ *   dt_bias       [channels]                 f32
+ *   A_log         [channels, state_dim]      f32   (A = -exp(A_log))
+ *   B, C          [batch, seqlen, ngroups, state_dim] act
+ *   D             [channels]                 f32
+ *   z             [batch, seqlen, channels]  act, or NULL: no gate; else y *= silu(z)
+ *   state_input   [batch, channels, state_dim] f32, or NULL: start from zeros
+ *   y             [batch, seqlen, channels]  act  (out)
+ *   state_output  [batch, channels, state_dim] f32 (out): the state after the last token
+ *   states        [batch, seqlen, channels, state_dim] f32 (out) or NULL: the state after
+ *                 every token; states[:, -1] equals state_output bit for bit.
+ *   workspace     device buffer of workspace_bytes >= sscan_mamba1_workspace_size()
+ * seqlen may be 0: then state_output = state_input (or zeros) and y is untouched. */
+sscan_status sscan_mamba1_fwd(const sscan_mamba1_desc* desc, const void* x, const void* dt_raw,
+                              const float* dt_bias, const float* A_log, const void* B, const void* C,
+                              const float* D, const void* z, const float* state_input, void* y,
+                              float* state_output, float* states, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Mamba-1 one-token decode step ("Mamba", section "The state": the state is
+ * handed from state_output to the next step's state_input, and the step updates
+ * the state before it reads y). desc->seqlen must be 1. Shapes as
+ * sscan_mamba1_fwd with seqlen 1; state_input is required and state_output may
+ * equal it (update in place). */
+sscan_status sscan_step(const sscan_mamba1_desc* desc, const float* state_input, float* state_output,
+                        const void* x, const void* dt_raw, const float* dt_bias, const float* A_log,
+                        const void* B, const void* C, const float* D, const void* z, void* y,
+                        void* stream);
+
+/* Bytes of workspace sscan_ssd_fwd needs for this problem (0 if none). */
+size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
+
+/* Mamba-2 SSD scan over a prompt ("Mamba-2", sections "The mixer's values",
+ * "The block, in order", "The hidden attention" and "The state").
+ *   x, z          [batch, seqlen, nheads, head_dim] act (z NULL: no gate)
+ *   dt_raw        [batch, seqlen, nheads]   act
+ *   dt_bias, A_log, D [nheads]              f32
+ *   B, C          [batch, seqlen, ngroups, state_dim] act
+ *   state_input   [batch, nheads, head_dim, state_dim] f32 or NULL (zeros)
+ *   y             [batch, seqlen, nheads, head_dim] act (out): ssd(...) + D*x, gated if z
+ *   state_output  [batch, nheads, head_dim, state_dim] f32 (out)
+ *   states        [batch, seqlen, nheads, head_dim, state_dim] f32 (out) or NULL
+ * The state is stored value side (head_dim) first and state_dim innermost: entry
+ * [b, h, p, n] is the pages' [b, h, key n, value p]. */
+sscan_status sscan_ssd_fwd(const sscan_ssd_desc* desc, const void* x, const void* dt_raw,
+                           const float* dt_bias, const float* A_log, const void* B, const void* C,
+                           const float* D, const void* z, const float* state_input, void* y,
+                           float* state_output, float* states, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Mamba-2 one-token decode step: sscan_ssd_fwd with seqlen 1, state_input
+ * required, state_output may equal state_input ("Mamba-2", section "The state":
+ * on a decode step the update comes before the read). */
+sscan_status sscan_ssd_step(const sscan_ssd_desc* desc, const float* state_input, float* state_output,
+                            const void* x, const void* dt_raw, const float* dt_bias, const float* A_log,
+                            const void* B, const void* C, const float* D, const void* z, void* y,
+                            void* stream);
+
+/* Text of a status code (static storage). */
+const char* sscan_status_string(int status);
+/* Detail of the last failing call on this thread (thread-local storage). */
+const char* sscan_last_error(void);
+/* SSCAN_ABI_VERSION of the library. */
+int sscan_abi_version(void);
+/* 1 (default): check that tensor pointers are device memory on every call
+ * (hipPointerGetAttributes); 0: skip that check (shape, alignment and alias
+ * checks still run). Process-wide; returns the previous setting. */
+int sscan_set_pointer_checks(int enabled);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSCAN_H */

@@ -1,0 +1,243 @@
+"""Thin ctypes binding of libsscan (include/sscan.h).
+
+Argument marshalling only: shapes are read off the tensors to fill the
+descriptor, outputs and the workspace are allocated with torch when the caller
+does not pass them, device pointers and the current HIP stream are handed to
+the C ABI, and a nonzero status raises SscanError. Every step of the scan runs
+in libsscan's HIP kernels; if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsscan.so")
+
+F32, BF16 = 0, 1
+STATUS_NAMES = ["SSCAN_OK", "SSCAN_ERR_NULL", "SSCAN_ERR_SHAPE", "SSCAN_ERR_DTYPE", "SSCAN_ERR_UNSUPPORTED",
+                "SSCAN_ERR_NOT_DEVICE", "SSCAN_ERR_ALIGN", "SSCAN_ERR_ALIAS", "SSCAN_ERR_WORKSPACE", "SSCAN_ERR_HIP"]
+EXPORTS = ["sscan_mamba1_workspace_size", "sscan_mamba1_fwd", "sscan_step", "sscan_ssd_workspace_size",
+           "sscan_ssd_fwd", "sscan_ssd_step", "sscan_status_string", "sscan_last_error", "sscan_abi_version",
+           "sscan_set_pointer_checks"]
+
+
+class Mamba1Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int64),
+                ("state_dim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("act", ctypes.c_int32),
+                ("bc_rms_eps", ctypes.c_float)]
+
+
+class SSDDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("state_dim", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("act", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SscanError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__("%s: %s" % (name, detail))
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsscan (ctypes.CDLL) with argument types set. Raises if not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsscan.so is not built at %s; run __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    M1 = ctypes.POINTER(Mamba1Desc)
+    SD = ctypes.POINTER(SSDDesc)
+    L.sscan_mamba1_workspace_size.argtypes = [M1]
+    L.sscan_mamba1_workspace_size.restype = S
+    L.sscan_mamba1_fwd.argtypes = [M1] + [P] * 13 + [S, P]
+    L.sscan_mamba1_fwd.restype = I
+    L.sscan_step.argtypes = [M1] + [P] * 12
+    L.sscan_step.restype = I
+    L.sscan_ssd_workspace_size.argtypes = [SD]
+    L.sscan_ssd_workspace_size.restype = S
+    L.sscan_ssd_fwd.argtypes = [SD] + [P] * 13 + [S, P]
+    L.sscan_ssd_fwd.restype = I
+    L.sscan_ssd_step.argtypes = [SD] + [P] * 12
+    L.sscan_ssd_step.restype = I
+    L.sscan_status_string.argtypes = [I]
+    L.sscan_status_string.restype = ctypes.c_char_p
+    L.sscan_last_error.argtypes = []
+    L.sscan_last_error.restype = ctypes.c_char_p
+    L.sscan_abi_version.argtypes = []
+    L.sscan_abi_version.restype = I
+    L.sscan_set_pointer_checks.argtypes = [I]
+    L.sscan_set_pointer_checks.restype = I
+    _lib = L
+    return L
+
+
+def check(status: int):
+    if status != 0:
+        raise SscanError(status, lib().sscan_last_error().decode())
+
+
+def set_pointer_checks(enabled: bool) -> bool:
+    return bool(lib().sscan_set_pointer_checks(1 if enabled else 0))
+
+
+def _act_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libsscan takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _f32(name, t):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    return t
+
+
+def _same(name, t, dtype):
+    if t is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s like x, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream().cuda_stream
+
+
+def mamba1_desc(x, B, bc_rms_eps=0.0):
+    b, L, Dc = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return Mamba1Desc(b, L, Dc, N, G, _act_code(x), float(bc_rms_eps))
+
+
+def ssd_desc(x, B, chunk=0):
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return SSDDesc(b, L, H, P, N, G, int(chunk), _act_code(x), 0)
+
+
+def sscan_mamba1_workspace_size(desc: Mamba1Desc) -> int:
+    return int(lib().sscan_mamba1_workspace_size(ctypes.byref(desc)))
+
+
+def sscan_ssd_workspace_size(desc: SSDDesc) -> int:
+    return int(lib().sscan_ssd_workspace_size(ctypes.byref(desc)))
+
+
+def sscan_mamba1_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, y=None,
+                     state_output=None, states=None, workspace=None, bc_rms_eps=0.0, want_states=False,
+                     stream=None):
+    """Mamba-1 scan over a prompt. x, dt_raw, z: [b, L, Dc]; B, C: [b, L, G, N].
+    Returns (y, state_output, states or None)."""
+    desc = mamba1_desc(x, B, bc_rms_eps)
+    for n, t in (("dt_raw", dt_raw), ("B", B), ("C", C), ("z", z)):
+        _same(n, t, x.dtype)
+    for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
+        _f32(n, t)
+    b, L, Dc = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    if state_output is None:
+        state_output = torch.empty((b, Dc, N), dtype=torch.float32, device=x.device)
+    if states is None and want_states:
+        states = torch.empty((b, L, Dc, N), dtype=torch.float32, device=x.device)
+    ws_bytes = sscan_mamba1_workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().sscan_mamba1_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(state_input), _ptr(y), _ptr(state_output),
+                                 _ptr(states), _ptr(workspace), wb, _stream(stream)))
+    return y, state_output, states
+
+
+def sscan_step(state_input, x, dt_raw, dt_bias, A_log, B, C, D, z=None, y=None, state_output=None,
+               bc_rms_eps=0.0, stream=None):
+    """Mamba-1 one-token decode step. x, dt_raw, z: [b, 1, Dc]; B, C: [b, 1, G, N]; state [b, Dc, N].
+    state_output may be state_input (in place). Returns (y, state_output)."""
+    desc = mamba1_desc(x, B, bc_rms_eps)
+    for n, t in (("dt_raw", dt_raw), ("B", B), ("C", C), ("z", z)):
+        _same(n, t, x.dtype)
+    for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
+        _f32(n, t)
+    if y is None:
+        y = torch.empty_like(x)
+    if state_output is None:
+        state_output = torch.empty_like(state_input)
+    check(lib().sscan_step(ctypes.byref(desc), _ptr(state_input), _ptr(state_output), _ptr(x), _ptr(dt_raw),
+                           _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                           _stream(stream)))
+    return y, state_output
+
+
+def sscan_ssd_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, y=None, state_output=None,
+                  states=None, workspace=None, chunk=0, want_states=False, stream=None):
+    """Mamba-2 SSD over a prompt. x, z: [b, L, H, P]; dt_raw: [b, L, H]; B, C: [b, L, G, N].
+    Returns (y, state_output [b, H, P, N], states [b, L, H, P, N] or None)."""
+    desc = ssd_desc(x, B, chunk)
+    for n, t in (("dt_raw", dt_raw), ("B", B), ("C", C), ("z", z)):
+        _same(n, t, x.dtype)
+    for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
+        _f32(n, t)
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    if state_output is None:
+        state_output = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    if states is None and want_states:
+        states = torch.empty((b, L, H, P, N), dtype=torch.float32, device=x.device)
+    ws_bytes = sscan_ssd_workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().sscan_ssd_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B),
+                              _ptr(C), _ptr(D), _ptr(z), _ptr(state_input), _ptr(y), _ptr(state_output),
+                              _ptr(states), _ptr(workspace), wb, _stream(stream)))
+    return y, state_output, states
+
+
+def sscan_ssd_step(state_input, x, dt_raw, dt_bias, A_log, B, C, D, z=None, y=None, state_output=None,
+                   stream=None):
+    """Mamba-2 one-token decode step. x, z: [b, 1, H, P]; dt_raw [b, 1, H]; state [b, H, P, N]."""
+    desc = ssd_desc(x, B, 0)
+    for n, t in (("dt_raw", dt_raw), ("B", B), ("C", C), ("z", z)):
+        _same(n, t, x.dtype)
+    for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
+        _f32(n, t)
+    if y is None:
+        y = torch.empty_like(x)
+    if state_output is None:
+        state_output = torch.empty_like(state_input)
+    check(lib().sscan_ssd_step(ctypes.byref(desc), _ptr(state_input), _ptr(state_output), _ptr(x), _ptr(dt_raw),
+                               _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                               _stream(stream)))
+    return y, state_output
+
+
+def ssd_state_key_first(state: torch.Tensor) -> torch.Tensor:
+    """The pages' [b, H, key (state_dim), value (head_dim)] view of a [b, H, P, N] state."""
+    return state.transpose(-1, -2)

@@ -1,0 +1,329 @@
+// api.cpp -- the C ABI of libsscan: argument validation and kernel dispatch.
+// Every check runs before anything is launched; see include/sscan.h.
+#include "sscan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_pointer_checks{1};
+
+sscan_status fail(sscan_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sscan_status ok() {
+  g_last_error.clear();
+  return SSCAN_OK;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+struct Buf {
+  const char* name;
+  const void* p;
+  size_t bytes;
+  bool out;
+};
+
+bool is_device_ptr(const void* p) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+bool overlap(const Buf& a, const Buf& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes, b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Null, alignment, alias and device checks over a list of buffers. `required`
+// buffers must be non-null when they have bytes. inplace_out / inplace_in name one
+// output/input pair that may be the same buffer (exactly, not partially).
+sscan_status check_buffers(const Buf* bufs, int n, const bool* required, const void* inplace_out,
+                           const void* inplace_in) {
+  for (int i = 0; i < n; ++i) {
+    if (bufs[i].bytes == 0) continue;
+    if (!bufs[i].p) {
+      if (required[i]) return fail(SSCAN_ERR_NULL, "%s is NULL", bufs[i].name);
+      continue;
+    }
+    if ((uintptr_t)bufs[i].p % 16 != 0)
+      return fail(SSCAN_ERR_ALIGN, "%s (%p) is not 16-byte aligned", bufs[i].name, bufs[i].p);
+  }
+  for (int i = 0; i < n; ++i) {
+    if (!bufs[i].out) continue;
+    for (int j = 0; j < n; ++j) {
+      if (i == j || !overlap(bufs[i], bufs[j])) continue;
+      if (bufs[j].out && j < i) continue;  // reported once per pair
+      // in place means the very same buffer: identical base pointer and size
+      const bool allowed = inplace_out && inplace_out == inplace_in && bufs[i].p == inplace_out &&
+                           bufs[j].p == inplace_in && bufs[i].bytes == bufs[j].bytes;
+      if (!allowed) return fail(SSCAN_ERR_ALIAS, "%s overlaps %s", bufs[i].name, bufs[j].name);
+    }
+  }
+  if (g_pointer_checks.load(std::memory_order_relaxed)) {
+    for (int i = 0; i < n; ++i) {
+      if (!bufs[i].p || bufs[i].bytes == 0) continue;
+      if (!is_device_ptr(bufs[i].p))
+        return fail(SSCAN_ERR_NOT_DEVICE, "%s (%p) is not device memory", bufs[i].name, bufs[i].p);
+    }
+  }
+  return SSCAN_OK;
+}
+
+sscan_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SSCAN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+sscan_status check_mamba1_desc(const sscan_mamba1_desc* d, bool step) {
+  if (!d) return fail(SSCAN_ERR_NULL, "descriptor is NULL");
+  if (d->batch < 0 || d->seqlen < 0 || d->channels <= 0 || d->state_dim <= 0 || d->ngroups <= 0)
+    return fail(SSCAN_ERR_SHAPE, "need batch >= 0, seqlen >= 0, channels, state_dim, ngroups > 0");
+  if (d->batch >= kMaxDim || d->seqlen >= kMaxDim || d->channels >= kMaxDim)
+    return fail(SSCAN_ERR_SHAPE, "a size exceeds 2^31");
+  if (d->channels % d->ngroups != 0) return fail(SSCAN_ERR_SHAPE, "ngroups must divide channels");
+  if (step && d->seqlen != 1) return fail(SSCAN_ERR_SHAPE, "sscan_step needs seqlen == 1");
+  if (d->act != SSCAN_F32 && d->act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
+  if (d->state_dim > 64) return fail(SSCAN_ERR_UNSUPPORTED, "Mamba-1 state_dim must be <= 64");
+  if (d->ngroups > 1 && (d->channels / d->ngroups) % 64 != 0)
+    return fail(SSCAN_ERR_UNSUPPORTED, "with ngroups > 1, channels / ngroups must be a multiple of 64");
+  if (d->batch > 65535) return fail(SSCAN_ERR_UNSUPPORTED, "batch must be <= 65535");
+  return SSCAN_OK;
+}
+
+sscan_status check_ssd_desc(const sscan_ssd_desc* d, bool step) {
+  if (!d) return fail(SSCAN_ERR_NULL, "descriptor is NULL");
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->head_dim <= 0 || d->state_dim <= 0 ||
+      d->ngroups <= 0)
+    return fail(SSCAN_ERR_SHAPE, "need batch >= 0, seqlen >= 0, nheads, head_dim, state_dim, ngroups > 0");
+  if (d->batch >= kMaxDim || d->seqlen >= kMaxDim || d->nheads * d->head_dim >= kMaxDim)
+    return fail(SSCAN_ERR_SHAPE, "a size exceeds 2^31");
+  if (d->nheads % d->ngroups != 0) return fail(SSCAN_ERR_SHAPE, "ngroups must divide nheads");
+  if (d->chunk != 0 && (d->chunk < 16 || d->chunk > 256 || (d->chunk & (d->chunk - 1)) != 0))
+    return fail(SSCAN_ERR_SHAPE, "chunk must be 0 or a power of two in 16..256");
+  if (d->reserved != 0) return fail(SSCAN_ERR_SHAPE, "reserved must be 0");
+  if (step && d->seqlen != 1) return fail(SSCAN_ERR_SHAPE, "sscan_ssd_step needs seqlen == 1");
+  if (d->act != SSCAN_F32 && d->act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
+  if (d->state_dim > 128) return fail(SSCAN_ERR_UNSUPPORTED, "SSD state_dim must be <= 128");
+  if (d->ngroups > 1 && ((d->nheads / d->ngroups) * d->head_dim) % 64 != 0)
+    return fail(SSCAN_ERR_UNSUPPORTED,
+                "with ngroups > 1, (nheads / ngroups) * head_dim must be a multiple of 64");
+  if (d->batch > 65535) return fail(SSCAN_ERR_UNSUPPORTED, "batch must be <= 65535");
+  return SSCAN_OK;
+}
+
+sscan::SSDArgs ssd_args(const sscan_ssd_desc* d) {
+  sscan::SSDArgs a{};
+  a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads; a.P = d->head_dim; a.N = d->state_dim;
+  a.G = d->ngroups; a.chunk = d->chunk; a.bf16 = d->act == SSCAN_BF16;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_abi_version(void) { return SSCAN_ABI_VERSION; }
+
+int sscan_set_pointer_checks(int enabled) { return g_pointer_checks.exchange(enabled ? 1 : 0); }
+
+const char* sscan_last_error(void) { return g_last_error.c_str(); }
+
+const char* sscan_status_string(int st) {
+  switch (st) {
+    case SSCAN_OK: return "ok";
+    case SSCAN_ERR_NULL: return "null pointer";
+    case SSCAN_ERR_SHAPE: return "invalid shape";
+    case SSCAN_ERR_DTYPE: return "invalid dtype";
+    case SSCAN_ERR_UNSUPPORTED: return "unsupported variant";
+    case SSCAN_ERR_NOT_DEVICE: return "not device memory";
+    case SSCAN_ERR_ALIGN: return "misaligned pointer";
+    case SSCAN_ERR_ALIAS: return "output overlaps input";
+    case SSCAN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSCAN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t sscan_mamba1_workspace_size(const sscan_mamba1_desc* d) {
+  if (check_mamba1_desc(d, false) != SSCAN_OK) return 0;
+  return sscan::mamba1_plan(d->batch, d->seqlen, d->channels, d->state_dim).ws_bytes;
+}
+
+sscan_status sscan_mamba1_fwd(const sscan_mamba1_desc* d, const void* x, const void* dt_raw,
+                              const float* dt_bias, const float* A_log, const void* B, const void* C,
+                              const float* D, const void* z, const float* state_input, void* y,
+                              float* state_output, float* states, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  sscan_status st = check_mamba1_desc(d, false);
+  if (st != SSCAN_OK) return st;
+  const int64_t b = d->batch, L = d->seqlen, Dc = d->channels, N = d->state_dim, G = d->ngroups;
+  const size_t es = d->act == SSCAN_BF16 ? 2 : 4;
+  const sscan::Mamba1Plan plan = sscan::mamba1_plan(b, L, Dc, N);
+  const size_t act_bytes = (size_t)(b * L * Dc) * es, bc_bytes = (size_t)(b * L * G * N) * es;
+  const size_t st_bytes = (size_t)(b * Dc * N) * 4;
+  const Buf bufs[] = {
+      {"x", x, act_bytes, false},
+      {"dt_raw", dt_raw, act_bytes, false},
+      {"dt_bias", dt_bias, (size_t)Dc * 4, false},
+      {"A_log", A_log, (size_t)(Dc * N) * 4, false},
+      {"B", B, bc_bytes, false},
+      {"C", C, bc_bytes, false},
+      {"D", D, (size_t)Dc * 4, false},
+      {"z", z, act_bytes, false},
+      {"state_input", state_input, st_bytes, false},
+      {"y", y, act_bytes, true},
+      {"state_output", state_output, st_bytes, true},
+      {"states", states, (size_t)(b * L * Dc * N) * 4, true},
+      {"workspace", workspace, plan.ws_bytes, true},
+  };
+  const bool req[] = {true, true, true, true, true, true, true, false, false, true, true, false, true};
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(SSCAN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  st = check_buffers(bufs, 13, req, nullptr, nullptr);
+  if (st != SSCAN_OK) return st;
+  sscan::Mamba1Args a{};
+  a.batch = b; a.L = L; a.Dc = Dc; a.N = N; a.G = G; a.bf16 = d->act == SSCAN_BF16;
+  a.bc_eps = d->bc_rms_eps > 0.0f ? d->bc_rms_eps : 0.0f;
+  a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
+  a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = states;
+  return hip_status(sscan::launch_mamba1_fwd(a, plan, workspace, (hipStream_t)stream), "sscan_mamba1_fwd launch");
+}
+
+sscan_status sscan_step(const sscan_mamba1_desc* d, const float* state_input, float* state_output,
+                        const void* x, const void* dt_raw, const float* dt_bias, const float* A_log,
+                        const void* B, const void* C, const float* D, const void* z, void* y, void* stream) {
+  sscan_status st = check_mamba1_desc(d, true);
+  if (st != SSCAN_OK) return st;
+  const int64_t b = d->batch, Dc = d->channels, N = d->state_dim, G = d->ngroups;
+  const size_t es = d->act == SSCAN_BF16 ? 2 : 4;
+  const size_t act_bytes = (size_t)(b * Dc) * es, st_bytes = (size_t)(b * Dc * N) * 4;
+  const Buf bufs[] = {
+      {"x", x, act_bytes, false},
+      {"dt_raw", dt_raw, act_bytes, false},
+      {"dt_bias", dt_bias, (size_t)Dc * 4, false},
+      {"A_log", A_log, (size_t)(Dc * N) * 4, false},
+      {"B", B, (size_t)(b * G * N) * es, false},
+      {"C", C, (size_t)(b * G * N) * es, false},
+      {"D", D, (size_t)Dc * 4, false},
+      {"z", z, act_bytes, false},
+      {"state_input", state_input, st_bytes, false},
+      {"y", y, act_bytes, true},
+      {"state_output", state_output, st_bytes, true},
+  };
+  const bool req[] = {true, true, true, true, true, true, true, false, true, true, true};
+  st = check_buffers(bufs, 11, req, state_output, state_input);
+  if (st != SSCAN_OK) return st;
+  sscan::Mamba1Args a{};
+  a.batch = b; a.L = 1; a.Dc = Dc; a.N = N; a.G = G; a.bf16 = d->act == SSCAN_BF16;
+  a.bc_eps = d->bc_rms_eps > 0.0f ? d->bc_rms_eps : 0.0f;
+  a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
+  a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = nullptr;
+  return hip_status(sscan::launch_mamba1_step(a, (hipStream_t)stream), "sscan_step launch");
+}
+
+size_t sscan_ssd_workspace_size(const sscan_ssd_desc* d) {
+  if (check_ssd_desc(d, false) != SSCAN_OK) return 0;
+  const sscan::SSDArgs a = ssd_args(d);
+  size_t w = sscan::ssd_tokenloop_ws(a);
+  if (sscan::ssd_chunk_supported(a)) {
+    const size_t wc = sscan::ssd_chunk_ws(a);
+    if (wc > w) w = wc;
+  }
+  return w;
+}
+
+sscan_status sscan_ssd_fwd(const sscan_ssd_desc* d, const void* x, const void* dt_raw, const float* dt_bias,
+                           const float* A_log, const void* B, const void* C, const float* D, const void* z,
+                           const float* state_input, void* y, float* state_output, float* states,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  sscan_status st = check_ssd_desc(d, false);
+  if (st != SSCAN_OK) return st;
+  sscan::SSDArgs a = ssd_args(d);
+  const int64_t b = a.batch, L = a.L, H = a.H, P = a.P, N = a.N, G = a.G;
+  const size_t es = a.bf16 ? 2 : 4;
+  const size_t act_bytes = (size_t)(b * L * H * P) * es, bc_bytes = (size_t)(b * L * G * N) * es;
+  const size_t st_bytes = (size_t)(b * H * P * N) * 4;
+  const bool chunk = states == nullptr && sscan::ssd_chunk_supported(a);
+  const size_t need = chunk ? sscan::ssd_chunk_ws(a) : sscan::ssd_tokenloop_ws(a);
+  const Buf bufs[] = {
+      {"x", x, act_bytes, false},
+      {"dt_raw", dt_raw, (size_t)(b * L * H) * es, false},
+      {"dt_bias", dt_bias, (size_t)H * 4, false},
+      {"A_log", A_log, (size_t)H * 4, false},
+      {"B", B, bc_bytes, false},
+      {"C", C, bc_bytes, false},
+      {"D", D, (size_t)H * 4, false},
+      {"z", z, act_bytes, false},
+      {"state_input", state_input, st_bytes, false},
+      {"y", y, act_bytes, true},
+      {"state_output", state_output, st_bytes, true},
+      {"states", states, (size_t)(b * L * H * P * N) * 4, true},
+      {"workspace", workspace, need, true},
+  };
+  const bool req[] = {true, true, true, true, true, true, true, false, false, true, true, false, true};
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SSCAN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  st = check_buffers(bufs, 13, req, nullptr, nullptr);
+  if (st != SSCAN_OK) return st;
+  a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
+  a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = states;
+  const hipError_t e = chunk ? sscan::launch_ssd_chunk(a, workspace, (hipStream_t)stream)
+                             : sscan::launch_ssd_tokenloop(a, workspace, (hipStream_t)stream);
+  return hip_status(e, "sscan_ssd_fwd launch");
+}
+
+sscan_status sscan_ssd_step(const sscan_ssd_desc* d, const float* state_input, float* state_output, const void* x,
+                            const void* dt_raw, const float* dt_bias, const float* A_log, const void* B,
+                            const void* C, const float* D, const void* z, void* y, void* stream) {
+  sscan_status st = check_ssd_desc(d, true);
+  if (st != SSCAN_OK) return st;
+  sscan::SSDArgs a = ssd_args(d);
+  const int64_t b = a.batch, H = a.H, P = a.P, N = a.N, G = a.G;
+  const size_t es = a.bf16 ? 2 : 4;
+  const size_t act_bytes = (size_t)(b * H * P) * es, st_bytes = (size_t)(b * H * P * N) * 4;
+  const Buf bufs[] = {
+      {"x", x, act_bytes, false},
+      {"dt_raw", dt_raw, (size_t)(b * H) * es, false},
+      {"dt_bias", dt_bias, (size_t)H * 4, false},
+      {"A_log", A_log, (size_t)H * 4, false},
+      {"B", B, (size_t)(b * G * N) * es, false},
+      {"C", C, (size_t)(b * G * N) * es, false},
+      {"D", D, (size_t)H * 4, false},
+      {"z", z, act_bytes, false},
+      {"state_input", state_input, st_bytes, false},
+      {"y", y, act_bytes, true},
+      {"state_output", state_output, st_bytes, true},
+  };
+  const bool req[] = {true, true, true, true, true, true, true, false, true, true, true};
+  st = check_buffers(bufs, 11, req, state_output, state_input);
+  if (st != SSCAN_OK) return st;
+  a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
+  a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = nullptr;
+  return hip_status(sscan::launch_ssd_step(a, (hipStream_t)stream), "sscan_ssd_step launch");
+}
+
+}  // extern "C"

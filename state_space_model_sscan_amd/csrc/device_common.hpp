@@ -1,0 +1,49 @@
+// device_common.hpp -- small device helpers shared by the libsscan kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sscan {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 <-> f32. Loads are exact; stores round to nearest even (NaN stays NaN).
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Act;
+template <> struct Act<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <> struct Act<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
+// log1p(e) for e in [0, 1] is log(u) with u = fl(1 + e), corrected by the
+// rounding error of u: log(1 + e) = log(u) - ((u - 1) - e) / u to first order;
+// (u - 1) - e is exact. softplus(-inf) = 0 exactly (a zero step).
+__device__ __forceinline__ float softplus(float v) {
+  const float e = fast_exp2(-fabsf(v) * kLog2e);
+  const float u = 1.0f + e;
+  const float corr = (u - 1.0f) - e;
+  const float l = fast_log2(u) * kLn2 - corr * fast_rcp(u);
+  return fmaxf(v, 0.0f) + l;
+}
+
+// silu(z) = z / (1 + e^-z); z -> -inf gives -0, z -> +inf gives z.
+__device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
+
+}  // namespace sscan

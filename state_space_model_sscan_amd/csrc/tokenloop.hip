@@ -1,0 +1,119 @@
+// tokenloop.hip -- host side of the token-loop scan: slicing plan and launches.
+// The kernels are in tokenloop_impl.hpp, instantiated in tl_*.hip.
+#include "tokenloop_impl.hpp"
+
+namespace sscan {
+
+extern template void dispatch_scan<float, false>(const TLK&, int64_t, bool, bool, hipStream_t);
+extern template void dispatch_scan<float, true>(const TLK&, int64_t, bool, bool, hipStream_t);
+extern template void dispatch_scan<uint16_t, false>(const TLK&, int64_t, bool, bool, hipStream_t);
+extern template void dispatch_scan<uint16_t, true>(const TLK&, int64_t, bool, bool, hipStream_t);
+extern template void dispatch_step<float, false>(const TLK&, int64_t, bool, hipStream_t);
+extern template void dispatch_step<float, true>(const TLK&, int64_t, bool, hipStream_t);
+extern template void dispatch_step<uint16_t, false>(const TLK&, int64_t, bool, hipStream_t);
+extern template void dispatch_step<uint16_t, true>(const TLK&, int64_t, bool, hipStream_t);
+
+// seqlen 0: the state passes through (or is zero).
+__global__ void copy_or_zero_kernel(const float* src, float* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+// Slices for the token-loop prompt scan (a pure function of the shape).
+Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N) {
+  Mamba1Plan p{1, L > 0 ? L : 1, 0};
+  const int64_t waves = batch * ((Dc + 63) / 64);
+  const int64_t target = 2048;  // two waves per SIMD on 256 CUs x 4 SIMDs
+  int64_t ns = waves > 0 ? (target + waves - 1) / waves : 1;
+  const int64_t max_ns = L / 128 > 1 ? L / 128 : 1;  // slices of at least 128 tokens
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  if (ns > 1) {
+    int64_t len = (L + ns - 1) / ns;
+    len = (len + 63) / 64 * 64;
+    ns = (L + len - 1) / len;
+    p.slice_len = len;
+  }
+  p.nslices = ns;
+  p.ws_bytes = ns > 1 ? (size_t)(batch * ns * Dc * (N + 1)) * sizeof(float) : 0;
+  return p;
+}
+
+static void run_tokenloop(TLK k, int64_t batch, bool bf16, bool ssd, bool gate, bool states,
+                          const Mamba1Plan& plan, void* ws, hipStream_t s) {
+  k.nslices = (int)plan.nslices;
+  k.slice_len = (int)plan.slice_len;
+  if (plan.nslices > 1) {
+    k.ws_h = (float*)ws;
+    k.ws_sdt = (float*)ws + batch * plan.nslices * k.Dc * k.N;
+  }
+  if (bf16) {
+    if (ssd) dispatch_scan<uint16_t, true>(k, batch, gate, states, s);
+    else dispatch_scan<uint16_t, false>(k, batch, gate, states, s);
+  } else {
+    if (ssd) dispatch_scan<float, true>(k, batch, gate, states, s);
+    else dispatch_scan<float, false>(k, batch, gate, states, s);
+  }
+}
+
+static TLK make_k(const void* x, const void* dt, const float* dt_bias, const float* A_log, const void* B,
+                  const void* C, const float* D, const void* z, const float* h0, void* y, float* h_out,
+                  float* states) {
+  TLK k{};
+  k.x = x; k.dt = dt; k.dt_bias = dt_bias; k.A_log = A_log; k.B = B; k.C = C;
+  k.D = D; k.z = z; k.h0 = h0; k.y = y; k.h_out = h_out; k.states = states;
+  return k;
+}
+
+static hipError_t zero_length(const float* h0, float* h_out, int64_t nst, hipStream_t s) {
+  if (nst > 0)
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, h0, h_out,
+                       nst);
+  return hipGetLastError();
+}
+
+hipError_t launch_mamba1_fwd(const Mamba1Args& a, const Mamba1Plan& plan, void* ws, hipStream_t s) {
+  if (a.L == 0 || a.batch == 0) return zero_length(a.h0, a.h_out, a.batch * a.Dc * a.N, s);
+  TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, a.states);
+  k.L = a.L; k.Dc = a.Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = a.Dc / a.G;
+  k.bc_eps = a.bc_eps; k.H = a.Dc; k.P = 1;
+  run_tokenloop(k, a.batch, a.bf16, false, a.z != nullptr, a.states != nullptr, plan, ws, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mamba1_step(const Mamba1Args& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, nullptr);
+  k.L = 1; k.Dc = a.Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = a.Dc / a.G;
+  k.bc_eps = a.bc_eps; k.H = a.Dc; k.P = 1; k.nslices = 1; k.slice_len = 1;
+  if (a.bf16) dispatch_step<uint16_t, false>(k, a.batch, a.z != nullptr, s);
+  else dispatch_step<float, false>(k, a.batch, a.z != nullptr, s);
+  return hipGetLastError();
+}
+
+// SSD through the token loop (any dtype, state_dim up to 128, per-token states).
+size_t ssd_tokenloop_ws(const SSDArgs& a) { return mamba1_plan(a.batch, a.L, a.H * a.P, a.N).ws_bytes; }
+
+hipError_t launch_ssd_tokenloop(const SSDArgs& a, void* ws, hipStream_t s) {
+  const int64_t Dc = a.H * a.P;
+  if (a.L == 0 || a.batch == 0) return zero_length(a.h0, a.h_out, a.batch * Dc * a.N, s);
+  TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, a.states);
+  k.L = a.L; k.Dc = Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = Dc / a.G;
+  k.bc_eps = 0.0f; k.H = a.H; k.P = a.P;
+  run_tokenloop(k, a.batch, a.bf16, true, a.z != nullptr, a.states != nullptr, mamba1_plan(a.batch, a.L, Dc, a.N),
+                ws, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_step(const SSDArgs& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  const int64_t Dc = a.H * a.P;
+  TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, nullptr);
+  k.L = 1; k.Dc = Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = Dc / a.G;
+  k.bc_eps = 0.0f; k.H = a.H; k.P = a.P; k.nslices = 1; k.slice_len = 1;
+  if (a.bf16) dispatch_step<uint16_t, true>(k, a.batch, a.z != nullptr, s);
+  else dispatch_step<float, true>(k, a.batch, a.z != nullptr, s);
+  return hipGetLastError();
+}
+
+}  // namespace sscan

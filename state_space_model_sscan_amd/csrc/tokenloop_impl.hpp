@@ -1,0 +1,277 @@
+// tokenloop_impl.hpp -- token-loop selective scan kernels for gfx950: Mamba-1, and
+// Mamba-2 SSD as its special case with one decay per head.
+//
+// The recurrence ("Mamba", nnterp guide, opening paragraph and section "The
+// values"; "Mamba", tokentrails lineage, section "Code"): per channel c and
+// state entry n,
+//     dt  = softplus(dt_raw + dt_bias[c])
+//     h_n = exp(dt * A[c, n]) * h_n + dt * B_n * x,     A = -exp(A_log)
+//     y   = sum_n C_n h_n + D[c] * x,  then y * silu(z) when a gate is given.
+// "Falcon-Mamba" (section "Where the norms sit"): optional weightless RMS norm
+// of every [state_dim] vector of B and C before the scan.
+//
+// SSD mode ("Mamba-2", section "The mixer's values"): channel ch = h*P + p of
+// head h holds the state row [p, :]; per head and token one step
+// dt = softplus(dt_raw[b,t,h] + dt_bias[h]) and one decay exp(dt * A_h),
+// A_h = -exp(A_log[h]), shared by every p and n; D per head. The stored state
+// [b, H, P, N] is [b, channels, N] with channels = H*P.
+//
+// Mapping: one lane per channel, its state_dim entries in registers; one wave
+// (64 lanes) per block of 64 channels of one batch row. B and C of a token are
+// shared by every channel of the group, so the wave stages them (fp32, normed)
+// in LDS once per tile of tokens and every lane reads them by broadcast.
+// exp(dt*A) is computed as exp2(dt * A*log2(e)) with A*log2(e) kept per lane.
+//
+// Sequence parallelism: the tokens of a batch row are cut into `nslices`
+// slices. Pass 1 scans every slice but the last from a zero state and stores
+// its end state and the sum of its steps; pass 2 starts slice s from
+//     h = decay(slice j) * h + end_state(slice j),  j = 0 .. s-1,
+// where the decay over slice j is exp(A * sum of dt over j), and scans it again,
+// writing y, the optional per-token states and, for the last slice, the final
+// state. Both passes restate the recurrence exactly; only rounding differs.
+#pragma once
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sscan {
+
+struct TLK {
+  const void* x;
+  const void* dt;
+  const float* dt_bias;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* h0;
+  void* y;
+  float* h_out;
+  float* states;
+  float* ws_h;    // [batch, nslices, Dc, N]
+  float* ws_sdt;  // [batch, nslices, Dc]
+  int64_t L, Dc;
+  int N, G, nslices, slice_len;
+  int64_t per_group;  // channels per B/C group
+  float bc_eps;
+  int64_t H, P;       // SSD mode: heads and head_dim (Dc = H * P)
+};
+
+// Tokens of B/C staged per LDS fill (at most the wave width, 64).
+template <int NP> constexpr int tile_for() { return NP <= 32 ? 64 : (NP <= 64 ? 32 : 16); }
+
+template <typename T, int NP, int TILE>
+__device__ __forceinline__ void stage_bc(const TLK& k, int64_t row_tok, int g, float (*sB)[NP],
+                                         float (*sC)[NP], int slot, bool want_c) {
+  const T* Bp = (const T*)k.B + (row_tok * k.G + g) * k.N;
+  const T* Cp = (const T*)k.C + (row_tok * k.G + g) * k.N;
+  float ssb = 0.0f, ssc = 0.0f;
+  for (int n = 0; n < NP; ++n) {
+    const float bv = n < k.N ? Act<T>::ld(Bp + n) : 0.0f;
+    const float cv = (want_c && n < k.N) ? Act<T>::ld(Cp + n) : 0.0f;
+    sB[slot][n] = bv;
+    if (want_c) sC[slot][n] = cv;
+    ssb = fmaf(bv, bv, ssb);
+    ssc = fmaf(cv, cv, ssc);
+  }
+  if (k.bc_eps > 0.0f) {
+    const float ib = 1.0f / sqrtf(ssb / (float)k.N + k.bc_eps);
+    const float ic = 1.0f / sqrtf(ssc / (float)k.N + k.bc_eps);
+    for (int n = 0; n < NP; ++n) {
+      sB[slot][n] *= ib;
+      if (want_c) sC[slot][n] *= ic;
+    }
+  }
+}
+
+template <typename T, int NP, bool SSD, bool GATE, bool STATES, bool PASS1>
+__global__ __launch_bounds__(64) void tokenloop_scan_kernel(TLK k) {
+  constexpr int TILE = tile_for<NP>();
+  __shared__ float sB[TILE][NP];
+  __shared__ float sC[TILE][NP];
+  const int lane = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t c = c0 + lane;
+  const bool active = c < k.Dc;
+  const int64_t cc = active ? c : k.Dc - 1;
+  const int s = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int64_t t_begin = (int64_t)s * k.slice_len;
+  const int64_t t_end = min(k.L, t_begin + (int64_t)k.slice_len);
+  const int g = (int)(c0 / k.per_group);  // the host guarantees one group per wave
+  const int64_t hd = SSD ? cc / k.P : cc;  // parameter index: head or channel
+
+  float A2[SSD ? 1 : NP], h[NP];
+  if (SSD) {
+    A2[0] = -expf(k.A_log[hd]) * kLog2e;
+  } else {
+#pragma unroll
+    for (int n = 0; n < NP; ++n) A2[SSD ? 0 : n] = n < k.N ? -expf(k.A_log[cc * k.N + n]) * kLog2e : 0.0f;
+  }
+#pragma unroll
+  for (int n = 0; n < NP; ++n) h[n] = (!PASS1 && k.h0 && n < k.N) ? k.h0[(b * k.Dc + cc) * k.N + n] : 0.0f;
+  if (!PASS1) {
+    for (int j = 0; j < s; ++j) {
+      const int64_t base = (b * k.nslices + j) * k.Dc + cc;
+      const float sdt = k.ws_sdt[base];
+      const float dec0 = SSD ? fast_exp2(A2[0] * sdt) : 0.0f;
+#pragma unroll
+      for (int n = 0; n < NP; ++n)
+        if (n < k.N) h[n] = fmaf(SSD ? dec0 : fast_exp2(A2[SSD ? 0 : n] * sdt), h[n], k.ws_h[base * k.N + n]);
+    }
+  }
+
+  const float bias = k.dt_bias[hd];
+  const float Dv = PASS1 ? 0.0f : k.D[hd];
+  const T* xp = (const T*)k.x;
+  const T* dp = (const T*)k.dt;
+  const T* zp = (const T*)k.z;
+  T* yp = (T*)k.y;
+  const int64_t dt_stride = SSD ? k.H : k.Dc;
+  float sdt = 0.0f;
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TILE) {
+    const int nt = (int)min((int64_t)TILE, t_end - t0);
+    __syncthreads();
+    if (lane < nt) stage_bc<T, NP, TILE>(k, b * k.L + t0 + lane, g, sB, sC, lane, !PASS1);
+    __syncthreads();
+    for (int i = 0; i < nt; ++i) {
+      const int64_t row = b * k.L + t0 + i;
+      const int64_t idx = row * k.Dc + cc;
+      const float xv = Act<T>::ld(xp + idx);
+      const float dtv = softplus(Act<T>::ld(dp + row * dt_stride + hd) + bias);
+      const float dtx = dtv * xv;
+      const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
+      if (PASS1) {
+        sdt += dtv;
+#pragma unroll
+        for (int n = 0; n < NP; ++n)
+          h[n] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : n]), h[n], dtx * sB[i][n]);
+      } else {
+        float yv = Dv * xv;
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          h[n] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : n]), h[n], dtx * sB[i][n]);
+          yv = fmaf(sC[i][n], h[n], yv);
+        }
+        if (STATES && active) {
+#pragma unroll
+          for (int n = 0; n < NP; ++n)
+            if (n < k.N) k.states[idx * k.N + n] = h[n];
+        }
+        if (GATE) yv *= silu(Act<T>::ld(zp + idx));
+        if (active) Act<T>::st(yp + idx, yv);
+      }
+    }
+  }
+
+  if (PASS1) {
+    if (active) {
+      const int64_t base = (b * k.nslices + s) * k.Dc + c;
+#pragma unroll
+      for (int n = 0; n < NP; ++n)
+        if (n < k.N) k.ws_h[base * k.N + n] = h[n];
+      k.ws_sdt[base] = sdt;
+    }
+  } else if (s == k.nslices - 1 && active) {
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+      if (n < k.N) k.h_out[(b * k.Dc + c) * k.N + n] = h[n];
+  }
+}
+
+// One token per call: lane = channel; the state is read, updated, then y is read
+// from the updated state ("Mamba", section "The state").
+template <typename T, int NP, bool SSD, bool GATE>
+__global__ __launch_bounds__(64) void tokenloop_step_kernel(TLK k) {
+  const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  if (c >= k.Dc) return;
+  const int g = (int)(c / k.per_group);
+  const int64_t hd = SSD ? c / k.P : c;
+  const int64_t sidx = (b * k.Dc + c) * k.N;
+  const T* Bp = (const T*)k.B + (b * k.G + g) * k.N;
+  const T* Cp = (const T*)k.C + (b * k.G + g) * k.N;
+  float ib = 1.0f, ic = 1.0f;
+  if (k.bc_eps > 0.0f) {
+    float sb = 0.0f, sc = 0.0f;
+    for (int n = 0; n < k.N; ++n) {
+      const float bv = Act<T>::ld(Bp + n), cv = Act<T>::ld(Cp + n);
+      sb = fmaf(bv, bv, sb);
+      sc = fmaf(cv, cv, sc);
+    }
+    ib = 1.0f / sqrtf(sb / (float)k.N + k.bc_eps);
+    ic = 1.0f / sqrtf(sc / (float)k.N + k.bc_eps);
+  }
+  const int64_t idx = b * k.Dc + c;  // seqlen 1
+  const float xv = Act<T>::ld((const T*)k.x + idx);
+  const float dtv = softplus(Act<T>::ld((const T*)k.dt + b * (SSD ? k.H : k.Dc) + hd) + k.dt_bias[hd]);
+  const float dtx = dtv * xv;
+  const float dec0 = SSD ? fast_exp2(dtv * (-expf(k.A_log[hd]) * kLog2e)) : 0.0f;
+  float yv = k.D[hd] * xv;
+  float h[NP];
+#pragma unroll
+  for (int n = 0; n < NP; ++n) {
+    if (n < k.N) {
+      const float dec = SSD ? dec0 : fast_exp2(dtv * (-expf(k.A_log[c * k.N + n]) * kLog2e));
+      h[n] = fmaf(dec, k.h0[sidx + n], dtx * (Act<T>::ld(Bp + n) * ib));
+      yv = fmaf(Act<T>::ld(Cp + n) * ic, h[n], yv);
+    }
+  }
+  if (GATE) yv *= silu(Act<T>::ld((const T*)k.z + idx));
+  Act<T>::st((T*)k.y + idx, yv);
+#pragma unroll
+  for (int n = 0; n < NP; ++n)
+    if (n < k.N) k.h_out[sidx + n] = h[n];
+}
+
+
+static int padded_n(int64_t N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : N <= 64 ? 64 : 128; }
+
+template <typename T, int NP, bool SSD>
+static void launch_scan(const TLK& k, int64_t batch, bool gate, bool states, hipStream_t s) {
+  const dim3 blk(64);
+  const int64_t cb = (k.Dc + 63) / 64;
+  if (k.nslices > 1) {
+    const dim3 grid1((unsigned)cb, (unsigned)(k.nslices - 1), (unsigned)batch);
+    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, true>), grid1, blk, 0, s, k);
+  }
+  const dim3 grid((unsigned)cb, (unsigned)k.nslices, (unsigned)batch);
+  if (gate && states)
+    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, true, true, false>), grid, blk, 0, s, k);
+  else if (gate)
+    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, true, false, false>), grid, blk, 0, s, k);
+  else if (states)
+    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, true, false>), grid, blk, 0, s, k);
+  else
+    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, false>), grid, blk, 0, s, k);
+}
+
+template <typename T, bool SSD>
+void dispatch_scan(const TLK& k, int64_t batch, bool gate, bool states, hipStream_t s) {
+  switch (padded_n(k.N)) {
+    case 8: launch_scan<T, 8, SSD>(k, batch, gate, states, s); break;
+    case 16: launch_scan<T, 16, SSD>(k, batch, gate, states, s); break;
+    case 32: launch_scan<T, 32, SSD>(k, batch, gate, states, s); break;
+    case 64: launch_scan<T, 64, SSD>(k, batch, gate, states, s); break;
+    default: launch_scan<T, 128, SSD>(k, batch, gate, states, s); break;
+  }
+}
+
+template <typename T, bool SSD>
+void dispatch_step(const TLK& k, int64_t batch, bool gate, hipStream_t s) {
+  const dim3 grid((unsigned)((k.Dc + 63) / 64), (unsigned)batch), blk(64);
+#define SSCAN_STEP(NP)                                                                           \
+  if (gate) hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, true>), grid, blk, 0, s, k);   \
+  else hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, false>), grid, blk, 0, s, k);
+  switch (padded_n(k.N)) {
+    case 8: { SSCAN_STEP(8) break; }
+    case 16: { SSCAN_STEP(16) break; }
+    case 32: { SSCAN_STEP(32) break; }
+    case 64: { SSCAN_STEP(64) break; }
+    default: { SSCAN_STEP(128) break; }
+  }
+#undef SSCAN_STEP
+}
+
+}  // namespace sscan
