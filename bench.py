@@ -1,0 +1,276 @@
+"""Benchmark of the selective scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only-main]
+
+A step is one sscan_mamba1_fwd over the Mamba-130m layer workload (batch 8,
+seq 2048, d_inner 1536, state_dim 16, bf16 activations, fp32 state, fused
+silu(z) gate). Inputs are resident in HBM when timing starts; three copies of
+them rotate so no step finds its inputs in the 256 MiB Infinity Cache. K steps
+are timed between two device synchronizations; each call is also bracketed by
+HIP events on the stream the kernels are launched on. Beside the main line the
+run reports the Falcon-Mamba-7b-width Mamba-1 workload, the Mamba-2 2.7B SSD
+workload and the 512-call decode-step workload, and the fp64 CPU oracle timed
+on this host. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one fp32 op per lane per
+# slot; v_exp_f32 takes two slots). Peak in T lane-slots/s.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+METRIC = "scan tokens/s & % HBM roofline (Mamba-1); SSD tokens/s & % MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def upload(inp, torch):
+    def act(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+        return (t.to(torch.bfloat16) if inp.act == "bf16" else t).cuda()
+
+    def par(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+    return dict(x=act(inp.x), dt_raw=act(inp.dt_raw), B=act(inp.B), C=act(inp.C), z=act(inp.z),
+                dt_bias=par(inp.dt_bias), A_log=par(inp.A_log), D=par(inp.D), state_input=par(inp.h0))
+
+
+def clone_set(d):
+    return {k: (None if v is None else v.clone()) for k, v in d.items()}
+
+
+def mamba1_bytes(inp):
+    b, L, Dc, N, G = inp.batch, inp.seqlen, inp.channels, inp.state_dim, inp.ngroups
+    es = 2 if inp.act == "bf16" else 4
+    nact = 3 if inp.z is not None else 2
+    rd = nact * b * L * Dc * es + 2 * b * L * G * N * es + (2 * Dc + Dc * N) * 4
+    if inp.h0 is not None:
+        rd += b * Dc * N * 4
+    wr = b * L * Dc * es + b * Dc * N * 4
+    return rd + wr
+
+
+def ssd_bytes(inp):
+    b, L, H, P, N, G = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim, inp.ngroups
+    es = 2 if inp.act == "bf16" else 4
+    nact = 2 if inp.z is not None else 1
+    rd = nact * b * L * H * P * es + b * L * H * es + 2 * b * L * G * N * es + 3 * H * 4
+    if inp.h0 is not None:
+        rd += b * H * P * N * 4
+    wr = b * L * H * P * es + b * H * P * N * 4
+    return rd + wr
+
+
+def ssd_flops(inp, Q=256):
+    """Contraction FLOPs of the chunked SSD at chunk Q (dense Q x Q blocks): C.B^T per
+    (batch, chunk, group), and per (batch, chunk, head) the diagonal block M.X, the chunk
+    state X^T.(B*w) and the off-diagonal read C.H^T."""
+    b, L, H, P, N, G = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim, inp.ngroups
+    nch = -(-L // Q)
+    return b * nch * (G * 2 * Q * Q * N + H * (2 * Q * Q * P + 2 * Q * N * P + 2 * Q * N * P))
+
+
+def time_calls(fn, sets, steps, warmup, torch):
+    """Run fn(set) `warmup` times untimed, then `steps` times timed; returns
+    (wall ms per step, mean event ms per call)."""
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn(sets[i % len(sets)])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return wall, ev
+
+
+def bench_mamba1(wid, steps, warmup, torch, bd, gen):
+    inp = gen.make_workload(wid)
+    base = upload(inp, torch)
+    sets = [base] + [clone_set(base) for _ in range(2)]
+    b, L, Dc, N = inp.batch, inp.seqlen, inp.channels, inp.state_dim
+    y = torch.empty_like(base["x"])
+    h = torch.empty((b, Dc, N), dtype=torch.float32, device="cuda")
+    ws_n = bd.sscan_mamba1_workspace_size(bd.mamba1_desc(base["x"], base["B"], inp.bc_eps))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def fn(s):
+        bd.sscan_mamba1_fwd(s["x"], s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"], s["D"], s["z"],
+                            s["state_input"], y=y, state_output=h, workspace=ws, bc_rms_eps=inp.bc_eps)
+
+    wall, ev = time_calls(fn, sets, steps, warmup, torch)
+    upd = b * L * Dc * N
+    by = mamba1_bytes(inp)
+    return dict(workload=gen.WORKLOADS[wid]["name"], ms_per_step=wall, kernel_ms=ev, tokens=b * L,
+                tokens_per_s=b * L / (wall * 1e-3), updates_per_s=upd / (ev * 1e-3), bytes=by,
+                hbm_gbs=by / (ev * 1e-3) / 1e9, hbm_frac=by / (ev * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                valu_tslots=6 * upd / (ev * 1e-3) / 1e12, inp=inp)
+
+
+def bench_ssd(steps, warmup, torch, bd, gen):
+    inp = gen.make_workload(4)
+    base = upload(inp, torch)
+    sets = [base] + [clone_set(base) for _ in range(2)]
+    b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
+    y = torch.empty_like(base["x"])
+    h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def fn(s):
+        bd.sscan_ssd_fwd(s["x"], s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"], s["D"], s["z"],
+                         s["state_input"], y=y, state_output=h, workspace=ws, chunk=inp.chunk)
+
+    wall, ev = time_calls(fn, sets, steps, warmup, torch)
+    by = ssd_bytes(inp)
+    fl = ssd_flops(inp, 256)
+    return dict(workload=gen.WORKLOADS[4]["name"], ms_per_step=wall, kernel_ms=ev, tokens=b * L,
+                tokens_per_s=b * L / (wall * 1e-3), bytes=by, hbm_gbs=by / (ev * 1e-3) / 1e9,
+                hbm_frac=by / (ev * 1e-3) / 1e9 / HBM_PEAK_GBS, flops_q256=fl,
+                mfma_tflops=fl / (ev * 1e-3) / 1e12, mfma_frac=fl / (ev * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                inp=inp)
+
+
+def bench_step(torch, bd, gen, calls=512):
+    """Workload 2 as `calls` one-token sscan_step calls, state updated in place."""
+    inp = gen.make_workload(2)
+    base = upload(inp, torch)
+    b, Dc = inp.batch, inp.channels
+    xs = [base[k][:, t:t + 1].contiguous() for k in ("x",) for t in range(calls)]
+    dts = [base["dt_raw"][:, t:t + 1].contiguous() for t in range(calls)]
+    zs = [base["z"][:, t:t + 1].contiguous() for t in range(calls)]
+    Bs = [base["B"][:, t:t + 1].contiguous() for t in range(calls)]
+    Cs = [base["C"][:, t:t + 1].contiguous() for t in range(calls)]
+    state = base["state_input"].clone()
+    y = torch.empty_like(xs[0])
+
+    def run(n):
+        for t in range(n):
+            bd.sscan_step(state, xs[t], dts[t], base["dt_bias"], base["A_log"], Bs[t], Cs[t], base["D"], zs[t],
+                          y=y, state_output=state)
+
+    run(8)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    run(calls)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e6 / calls
+    per_call_bytes = 2 * b * Dc * 16 * 4 + 4 * b * Dc * 4 + 2 * b * 16 * 4 + (2 * Dc + Dc * 16) * 4
+    return dict(workload=gen.WORKLOADS[2]["name"] + " as %d sscan_step calls" % calls,
+                us_per_step_wall=wall, us_per_step_gpu=e0.elapsed_time(e1) * 1e3 / calls,
+                bytes_per_call=per_call_bytes)
+
+
+def cpu_baseline(inp, repeats=2):
+    import oracle
+
+    oracle.build(force=False)
+    best = None
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.run_inputs(inp, want_states=False)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    toks = inp.batch * inp.seqlen
+    return dict(value=toks / best, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample="the whole workload (%d x %d tokens x %d channels x %d states), fp64, best of %d runs, "
+                       "%.2f s each" % (inp.batch, inp.seqlen, inp.channels, inp.state_dim, repeats, best))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-main", action="store_true", help="time only the main workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one MI355X). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from state_space_model_sscan_amd import binding as bd
+    from state_space_model_sscan_amd import inputs as gen
+
+    bd.lib()  # fails loudly if libsscan.so is missing
+    torch.cuda.set_device(0)
+
+    log("bench: workload 1 (main)")
+    m = bench_mamba1(1, args.steps, args.warmup, torch, bd, gen)
+    extra = {}
+    if not args.only_main:
+        log("bench: workload 3")
+        m3 = bench_mamba1(3, max(10, args.steps // 4), 3, torch, bd, gen)
+        log("bench: workload 4 (SSD)")
+        s4 = bench_ssd(max(10, args.steps // 4), 3, torch, bd, gen)
+        log("bench: workload 2 (decode steps)")
+        st = bench_step(torch, bd, gen)
+        extra = dict(
+            mamba1_falcon_width={k: v for k, v in m3.items() if k != "inp"},
+            ssd_mamba2_2p7b={k: v for k, v in s4.items() if k != "inp"},
+            decode_step=st,
+        )
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(m["inp"])
+
+    inp = m["inp"]
+    valu_frac = m["valu_tslots"] / VALU_PEAK_TSLOTS
+    line = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": m["workload"], "batch": inp.batch, "seq_len": inp.seqlen,
+                   "channels": inp.channels, "state_dim": inp.state_dim, "ngroups": inp.ngroups,
+                   "gate": True, "state": "fp32"},
+        "roofline": {"bound": "alu", "achieved": m["valu_tslots"], "peak": VALU_PEAK_TSLOTS,
+                     "unit": "T VALU-slots/s", "frac": valu_frac, "traffic": None,
+                     "kernel": "sscan_mamba1_fwd (all its kernels)", "kernel_ms": m["kernel_ms"],
+                     "hbm_gbs": m["hbm_gbs"], "hbm_frac": m["hbm_frac"], "algorithmic_bytes": m["bytes"],
+                     "updates_per_s": m["updates_per_s"]},
+        "cpu_baseline": cpu,
+        "secondary": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

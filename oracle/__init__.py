@@ -46,8 +46,15 @@ def _load():
         lib.oracle_conv1d_silu.restype = ctypes.c_int
         lib.oracle_gated_rmsnorm.argtypes = [I64, I64, P, P, P, D, P]
         lib.oracle_gated_rmsnorm.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().oracle_threads())
 
 
 def _f64(a):

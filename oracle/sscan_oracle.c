@@ -37,6 +37,7 @@
  * and state invariants, the RMS-of-one property); see tests/test_oracle_pins.py.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,6 +52,9 @@ static double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 int oracle_abi_version(void) { return 1; }
+
+/* Threads an OpenMP loop of the oracle uses (for reporting the CPU baseline). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* Weightless RMS norm of every [state_dim] vector of a [rows, state_dim] array
  * ([FM] "Where the norms sit"): out = v / sqrt(mean(v^2) + eps). */

@@ -11,8 +11,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsscan.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "tokenloop.hip", "tl_m1_f32.hip", "tl_m1_bf16.hip", "tl_ssd_f32.hip", "tl_ssd_bf16.hip",
-           "ssd_chunk.hip"]
+SOURCES = ["api.cpp", "tokenloop.hip", "m1_fast.hip", "tl_m1_f32.hip", "tl_m1_bf16.hip", "tl_ssd_f32.hip",
+           "tl_ssd_bf16.hip", "m1f_f32_16.hip", "m1f_f32_32.hip", "m1f_f32_64.hip", "m1f_bf16_16.hip",
+           "m1f_bf16_32.hip", "m1f_bf16_64.hip", "ssd_chunk.hip"]
 ARCH = os.environ.get("SSCAN_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU instructions are switched off for every device pass.
@@ -36,7 +37,7 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, jobs: int = 7) -> str:
+def build(extra: list[str] | None = None, jobs: int = 8) -> str:
     """Compile every HIP source for gfx950 and link libsscan.so. Always recompiles."""
     os.makedirs(OBJDIR, exist_ok=True)
     extra = list(extra or [])

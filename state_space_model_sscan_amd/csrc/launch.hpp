@@ -24,13 +24,18 @@ struct Mamba1Args {
   float* states;
 };
 
-// Sequence slicing of the Mamba-1 prompt scan (a pure function of the shape).
+// Launch plan of a prompt scan (a pure function of the shape): lanes per channel
+// and the cut of the sequence into slices (workspace holds the slice carries).
 struct Mamba1Plan {
   int64_t nslices;
   int64_t slice_len;
   size_t ws_bytes;
+  int64_t lanes_per_channel;
 };
-Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N);
+Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t es);  // 0 lanes: token loop
+Mamba1Plan tokenloop_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N);  // token-loop kernel
+hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const float* ws_h, const float* ws_sdt,
+                          hipStream_t s);
 
 hipError_t launch_mamba1_fwd(const Mamba1Args& a, const Mamba1Plan& plan, void* ws, hipStream_t s);
 hipError_t launch_mamba1_step(const Mamba1Args& a, hipStream_t s);

@@ -4,4 +4,5 @@
 namespace sscan {
 template void dispatch_scan<float, false>(const TLK&, int64_t, bool, bool, hipStream_t);
 template void dispatch_step<float, false>(const TLK&, int64_t, bool, hipStream_t);
+template void dispatch_pass1<float, false>(const TLK&, int64_t, hipStream_t);
 }  // namespace sscan

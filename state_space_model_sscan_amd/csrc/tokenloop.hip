@@ -8,6 +8,8 @@ extern template void dispatch_scan<float, false>(const TLK&, int64_t, bool, bool
 extern template void dispatch_scan<float, true>(const TLK&, int64_t, bool, bool, hipStream_t);
 extern template void dispatch_scan<uint16_t, false>(const TLK&, int64_t, bool, bool, hipStream_t);
 extern template void dispatch_scan<uint16_t, true>(const TLK&, int64_t, bool, bool, hipStream_t);
+extern template void dispatch_pass1<float, false>(const TLK&, int64_t, hipStream_t);
+extern template void dispatch_pass1<uint16_t, false>(const TLK&, int64_t, hipStream_t);
 extern template void dispatch_step<float, false>(const TLK&, int64_t, bool, hipStream_t);
 extern template void dispatch_step<float, true>(const TLK&, int64_t, bool, hipStream_t);
 extern template void dispatch_step<uint16_t, false>(const TLK&, int64_t, bool, hipStream_t);
@@ -20,8 +22,8 @@ __global__ void copy_or_zero_kernel(const float* src, float* dst, int64_t n) {
 }
 
 // Slices for the token-loop prompt scan (a pure function of the shape).
-Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N) {
-  Mamba1Plan p{1, L > 0 ? L : 1, 0};
+Mamba1Plan tokenloop_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N) {
+  Mamba1Plan p{1, L > 0 ? L : 1, 0, 1};
   const int64_t waves = batch * ((Dc + 63) / 64);
   const int64_t target = 2048;  // two waves per SIMD on 256 CUs x 4 SIMDs
   int64_t ns = waves > 0 ? (target + waves - 1) / waves : 1;
@@ -72,13 +74,61 @@ static hipError_t zero_length(const float* h0, float* h_out, int64_t nst, hipStr
   return hipGetLastError();
 }
 
+// Mamba-1 prompt plan: K lanes per channel so that the grid covers the 1024
+// SIMDs of the chip, and slices (two-pass carry) only when even K = 4 leaves
+// fewer than 512 waves on a long sequence.
+Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t es) {
+  // a batch row the buffer offsets of the fast kernel cannot span: token-loop kernel
+  if (L * Dc * es >= (int64_t(1) << 31)) {
+    Mamba1Plan t = tokenloop_plan(batch, L, Dc, N);
+    t.lanes_per_channel = 0;
+    return t;
+  }
+  Mamba1Plan p{1, L > 0 ? L : 1, 0, 1};
+  auto waves = [&](int64_t K) { return batch * ((Dc * K + 63) / 64); };
+  int64_t K = N > 32 ? 2 : 1;  // 64 states in one lane would spill
+  while (K < 4 && waves(K) < 1024) K *= 2;
+  p.lanes_per_channel = K;
+  const int64_t w = waves(K);
+  if (w > 0 && w < 512 && L >= 1024) {
+    int64_t ns = (1024 + w - 1) / w;
+    if (ns > L / 512) ns = L / 512;
+    if (ns > 1) {
+      int64_t len = (L + ns - 1) / ns;
+      len = (len + 63) / 64 * 64;
+      ns = (L + len - 1) / len;
+      p.nslices = ns;
+      p.slice_len = len;
+    }
+  }
+  p.ws_bytes = p.nslices > 1 ? (size_t)(batch * p.nslices * Dc * (N + 1)) * sizeof(float) : 0;
+  return p;
+}
+
 hipError_t launch_mamba1_fwd(const Mamba1Args& a, const Mamba1Plan& plan, void* ws, hipStream_t s) {
   if (a.L == 0 || a.batch == 0) return zero_length(a.h0, a.h_out, a.batch * a.Dc * a.N, s);
-  TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, a.states);
-  k.L = a.L; k.Dc = a.Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = a.Dc / a.G;
-  k.bc_eps = a.bc_eps; k.H = a.Dc; k.P = 1;
-  run_tokenloop(k, a.batch, a.bf16, false, a.z != nullptr, a.states != nullptr, plan, ws, s);
-  return hipGetLastError();
+  if (plan.lanes_per_channel == 0) {  // the token-loop kernel, both passes
+    TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, a.states);
+    k.L = a.L; k.Dc = a.Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = a.Dc / a.G;
+    k.bc_eps = a.bc_eps; k.H = a.Dc; k.P = 1;
+    run_tokenloop(k, a.batch, a.bf16, false, a.z != nullptr, a.states != nullptr, plan, ws, s);
+    return hipGetLastError();
+  }
+  const float* ws_h = nullptr;
+  const float* ws_sdt = nullptr;
+  if (plan.nslices > 1) {
+    TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, a.states);
+    k.L = a.L; k.Dc = a.Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = a.Dc / a.G;
+    k.bc_eps = a.bc_eps; k.H = a.Dc; k.P = 1;
+    k.nslices = (int)plan.nslices; k.slice_len = (int)plan.slice_len;
+    k.ws_h = (float*)ws;
+    k.ws_sdt = (float*)ws + a.batch * plan.nslices * a.Dc * a.N;
+    if (a.bf16) dispatch_pass1<uint16_t, false>(k, a.batch, s);
+    else dispatch_pass1<float, false>(k, a.batch, s);
+    ws_h = k.ws_h;
+    ws_sdt = k.ws_sdt;
+  }
+  return launch_m1_fast(a, plan, ws_h, ws_sdt, s);
 }
 
 hipError_t launch_mamba1_step(const Mamba1Args& a, hipStream_t s) {
@@ -92,7 +142,7 @@ hipError_t launch_mamba1_step(const Mamba1Args& a, hipStream_t s) {
 }
 
 // SSD through the token loop (any dtype, state_dim up to 128, per-token states).
-size_t ssd_tokenloop_ws(const SSDArgs& a) { return mamba1_plan(a.batch, a.L, a.H * a.P, a.N).ws_bytes; }
+size_t ssd_tokenloop_ws(const SSDArgs& a) { return tokenloop_plan(a.batch, a.L, a.H * a.P, a.N).ws_bytes; }
 
 hipError_t launch_ssd_tokenloop(const SSDArgs& a, void* ws, hipStream_t s) {
   const int64_t Dc = a.H * a.P;
@@ -100,7 +150,7 @@ hipError_t launch_ssd_tokenloop(const SSDArgs& a, void* ws, hipStream_t s) {
   TLK k = make_k(a.x, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.z, a.h0, a.y, a.h_out, a.states);
   k.L = a.L; k.Dc = Dc; k.N = (int)a.N; k.G = (int)a.G; k.per_group = Dc / a.G;
   k.bc_eps = 0.0f; k.H = a.H; k.P = a.P;
-  run_tokenloop(k, a.batch, a.bf16, true, a.z != nullptr, a.states != nullptr, mamba1_plan(a.batch, a.L, Dc, a.N),
+  run_tokenloop(k, a.batch, a.bf16, true, a.z != nullptr, a.states != nullptr, tokenloop_plan(a.batch, a.L, Dc, a.N),
                 ws, s);
   return hipGetLastError();
 }

@@ -258,6 +258,21 @@ void dispatch_scan(const TLK& k, int64_t batch, bool gate, bool states, hipStrea
   }
 }
 
+// Pass 1 only: slice end states and step sums into the workspace.
+template <typename T, bool SSD>
+void dispatch_pass1(const TLK& k, int64_t batch, hipStream_t s) {
+  const dim3 grid1((unsigned)((k.Dc + 63) / 64), (unsigned)(k.nslices - 1), (unsigned)batch), blk(64);
+#define SSCAN_P1(NP) hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, true>), grid1, blk, 0, s, k);
+  switch (padded_n(k.N)) {
+    case 8: { SSCAN_P1(8) break; }
+    case 16: { SSCAN_P1(16) break; }
+    case 32: { SSCAN_P1(32) break; }
+    case 64: { SSCAN_P1(64) break; }
+    default: { SSCAN_P1(128) break; }
+  }
+#undef SSCAN_P1
+}
+
 template <typename T, bool SSD>
 void dispatch_step(const TLK& k, int64_t batch, bool gate, hipStream_t s) {
   const dim3 grid((unsigned)((k.Dc + 63) / 64), (unsigned)batch), blk(64);

@@ -126,11 +126,14 @@ def test_mamba1_pointer_errors():
 
 def test_mamba1_workspace():
     h = Host()
-    d = desc(batch=8, seqlen=2048, channels=1536)
+    # one batch row of 128 channels over a long sequence is cut into slices
+    d = desc(batch=1, seqlen=16384, channels=128)
     need = bd.lib().sscan_mamba1_workspace_size(ctypes.byref(d))
     assert need > 0 and need % 4 == 0
     # the query is a pure function of the shape
-    assert need == bd.lib().sscan_mamba1_workspace_size(ctypes.byref(desc(batch=8, seqlen=2048, channels=1536)))
+    assert need == bd.lib().sscan_mamba1_workspace_size(ctypes.byref(desc(batch=1, seqlen=16384, channels=128)))
+    # the Mamba-130m layer shape fills the chip without slices
+    assert bd.lib().sscan_mamba1_workspace_size(ctypes.byref(desc(batch=8, seqlen=2048, channels=1536))) == 0
     a = m1_args(h, d, ws=need - 4)
     assert status(call_m1(d, a)) == "SSCAN_ERR_WORKSPACE"
     a = m1_args(h, d, ws=0)

@@ -38,6 +38,10 @@ M1_CASES = [
     (2, 1000, 192, 16, "bf16", True, False, False, 0.0),
     (1, 777, 64, 64, "f32", True, True, False, 0.0),
     (2, 3000, 64, 16, "f32", True, True, True, 0.0),     # several slices
+    (16, 100, 4096, 16, "bf16", True, False, False, 0.0),  # one lane per channel
+    (8, 77, 4096, 16, "f32", False, True, True, 1e-6),     # two lanes per channel
+    (8, 45, 4096, 32, "f32", True, True, False, 0.0),      # 32 states, two lanes per channel
+    (3, 333, 256, 64, "bf16", True, True, True, 0.0),      # 64 states, four lanes per channel
 ]
 
 
