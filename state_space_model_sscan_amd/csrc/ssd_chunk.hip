@@ -27,8 +27,11 @@
 //      accumulators, converted to bf16;
 //   4. Y += M X;
 //   5. S = exp(cs_last) S + B^T (w X), w_j = exp(cs_last - cs_j) dt_j;
-//   6. y = Y + D x, times silu(z), stored as bf16.
-// The global loads of chunk c+1 are in flight while chunk c is computed.
+//   6. y = Y + D x, times silu(z), stored as bf16 through an LDS tile so that
+//      every store is a whole 16-byte piece of a row.
+// The global loads of chunk c+1 are in flight while chunk c is computed. All
+// global traffic goes through buffer resources over the batch row, so a token
+// past the end reads zeros and writes nothing without a branch.
 // MFMA: v_mfma_f32_16x16x32_bf16. Operand layouts (verified on gfx950):
 // A[16 x 32]: lane l holds row l%16, k = 8*(l/16) .. +8; B[32 x 16]: lane l
 // holds column l%16, the same k; D[16 x 16]: lane l holds rows 4*(l/16) + r,
@@ -47,10 +50,13 @@ constexpr int P = 64;      // head_dim
 constexpr int NS = 128;    // state_dim
 constexpr int LDB = NS + 8;   // row pitch (bf16) of sB, sC
 constexpr int LDBT = Q + 8;   // row pitch of sBT (one row per state entry)
-constexpr int LDX = P + 8;    // row pitch of sX
+constexpr int LDX = P + 8;    // row pitch of sX, sZ
 constexpr int LDM = Q + 8;    // row pitch of sM
+constexpr int LDY = P + 4;    // row pitch (fp32) of the output tile, which reuses sB
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past any resource built here
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -79,25 +85,35 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 lds128(const uint16_t* p) { return *(const u32x4*)p; }
 
+// two floats to two bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// chunk-ahead global loads of one thread (16-byte pieces; zeros past the sequence end)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+// One chunk's global loads of one thread, in flight during the previous chunk:
+// B, C: 4 pieces of 8 bf16 (rows tid & 63, pieces (tid >> 6) + 4*it); x, z: 2 pieces
+// (rows tid & 63, pieces (tid >> 6) + 4*it); dt: one value (threads 0..63).
 struct Prefetch {
-  u32x4 b[4], c[4], x[2];
+  u32x4 b[4], c[4], x[2], z[2];
   float dt;
 };
 
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
-  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * LDB];  // reused for the fp32 output tile
   __shared__ __attribute__((aligned(16))) uint16_t sC[Q * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t sBT[NS * LDBT];
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * LDX];
-  __shared__ __attribute__((aligned(16))) uint16_t sM[Q * LDM];
+  __shared__ __attribute__((aligned(16))) uint16_t sM[Q * LDM];  // reused for z in the epilogue
   __shared__ float sDT[Q], sCS[Q], sW[Q], sE[Q];
+  static_assert(Q * LDY * 4 <= Q * LDB * 2, "the output tile fits in sB");
+  static_assert(LDX <= LDM, "z fits in sM");
 
   // block -> (batch, head): consecutive heads of one batch row share an XCD (and its L2)
   int lin = blockIdx.x;
@@ -109,46 +125,58 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   const float A2 = -expf(k.A_log[h]) * kLog2e;  // decay per unit step, exp2 domain
   const float bias = k.dt_bias[h];
   const float Dh = k.D[h];
-  const int p_own = 16 * w + li;  // the head_dim column this lane holds in D layouts
+  const int p_own = 16 * w + li;  // the head_dim column this lane holds in MFMA D layouts
+  const bool gate = k.z != nullptr;
+
+  // buffer resources over this batch row (the host guarantees each is < 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t rB = rsrc(k.B + b * L * G * NS, (uint64_t)L * G * NS * 2);
+  const __amdgpu_buffer_rsrc_t rC = rsrc(k.C + b * L * G * NS, (uint64_t)L * G * NS * 2);
+  const __amdgpu_buffer_rsrc_t rX = rsrc(k.x + b * L * H * P, (uint64_t)L * H * P * 2);
+  const __amdgpu_buffer_rsrc_t rZ = rsrc(gate ? k.z + b * L * H * P : k.x, (uint64_t)L * H * P * 2);
+  const __amdgpu_buffer_rsrc_t rY = rsrc(k.y + b * L * H * P, (uint64_t)L * H * P * 2);
+  const __amdgpu_buffer_rsrc_t rD = rsrc(k.dt + b * L * H, (uint64_t)L * H * 2);
+  const int row = l;        // staging row of this thread
+  const int pc0 = w;        // its first 8-element piece; pieces pc0 + 4*it
+  const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2);
+  const uint32_t bc_lane = (uint32_t)(row * G * NS * 2 + g * NS * 2 + pc0 * 16);
+  const uint32_t xz_lane = (uint32_t)(row * H * P * 2 + h * P * 2 + pc0 * 16);
+  const uint32_t dt_lane = (uint32_t)((tid * H + h) * 2);
 
   // state slice: hacc[Nt][r] = S[p = 16w + li][n = 16Nt + 4lg + r]
   f32x4 hacc[8];
+  if (k.h0) {
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    if (k.h0) {
-      const float* hp = k.h0 + ((b * H + h) * P + p_own) * NS + 16 * nt + 4 * lg;
-      hacc[nt] = *(const f32x4*)hp;
-    } else {
-      hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int nt = 0; nt < 8; ++nt)
+      hacc[nt] = *(const f32x4*)(k.h0 + ((b * H + h) * P + p_own) * NS + 16 * nt + 4 * lg);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // the tiles of M above the diagonal block row stay zero
   for (int e = tid; e < Q * LDM; e += 256) sM[e] = 0;
 
   const int64_t nchunks = (L + Q - 1) / Q;
+  // Loads of chunk c (zeros past the sequence end, via out-of-range offsets).
   auto load_chunk = [&](Prefetch& pf, int64_t c) {
     const int64_t t0 = c * Q;
+    const bool ok = t0 + row < L;
+    const uint32_t bcv = ok ? bc_lane : kOOB, xzv = ok ? xz_lane : kOOB;
+    const uint32_t bcs = ok ? (uint32_t)(t0 * bc_row) : 0u, xzs = ok ? (uint32_t)(t0 * xz_row) : 0u;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {  // B, C: 64 rows x 16 pieces
-      const int idx = tid + 256 * it, row = idx >> 4, piece = idx & 15;
-      const int64_t t = t0 + row;
-      const bool ok = c < nchunks && t < L;
-      const int64_t off = ((b * L + (ok ? t : 0)) * G + g) * NS + piece * 8;
-      pf.b[it] = ok ? *(const u32x4*)(k.B + off) : u32x4{0, 0, 0, 0};
-      pf.c[it] = ok ? *(const u32x4*)(k.C + off) : u32x4{0, 0, 0, 0};
+    for (int it = 0; it < 4; ++it) {
+      pf.b[it] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(bcv + it * 64), (int)bcs, 0);
+      pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bcv + it * 64), (int)bcs, 0);
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {  // x: 64 rows x 8 pieces
-      const int idx = tid + 256 * it, row = idx >> 3, piece = idx & 7;
-      const int64_t t = t0 + row;
-      const bool ok = c < nchunks && t < L;
-      const int64_t off = ((b * L + (ok ? t : 0)) * H + h) * P + piece * 8;
-      pf.x[it] = ok ? *(const u32x4*)(k.x + off) : u32x4{0, 0, 0, 0};
+    for (int it = 0; it < 2; ++it) {
+      pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(xzv + it * 64), (int)xzs, 0);
+      if (gate) pf.z[it] = __builtin_amdgcn_raw_buffer_load_b128(rZ, (int)(xzv + it * 64), (int)xzs, 0);
     }
     if (tid < Q) {
-      const int64_t t = t0 + tid;
-      const bool ok = c < nchunks && t < L;
-      pf.dt = ok ? bf16_to_f32(k.dt[(b * L + t) * H + h]) : 0.0f;
+      const bool okd = t0 + tid < L;
+      const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b16(rD, (int)(okd ? dt_lane : kOOB),
+                                                                okd ? (int)(t0 * H * 2) : 0, 0);
+      pf.dt = bf16_to_f32((uint16_t)raw);
     }
   };
 
@@ -159,26 +187,26 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     const int64_t t0 = c * Q;
     const int nt_valid = (int)min((int64_t)Q, L - t0);
     __syncthreads();  // the previous chunk is done with every LDS buffer
-    // ---- 1. stage
+    // ---- 1. stage B, C, B^T, x, z; steps and their cumulative sum
+    u32x4 zkeep[2];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = tid + 256 * it, row = idx >> 4, piece = idx & 15;
-      *(u32x4*)(sB + row * LDB + piece * 8) = pf.b[it];
-      *(u32x4*)(sC + row * LDB + piece * 8) = pf.c[it];
+      const int pc = pc0 + 4 * it;
+      *(u32x4*)(sB + row * LDB + pc * 8) = pf.b[it];
+      *(u32x4*)(sC + row * LDB + pc * 8) = pf.c[it];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t wv = pf.b[it][e >> 1];
-        sBT[(piece * 8 + e) * LDBT + row] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+        sBT[(pc * 8 + e) * LDBT + row] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
       }
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      const int idx = tid + 256 * it, row = idx >> 3, piece = idx & 7;
-      *(u32x4*)(sX + row * LDX + piece * 8) = pf.x[it];
+      *(u32x4*)(sX + row * LDX + (pc0 + 4 * it) * 8) = pf.x[it];
+      zkeep[it] = pf.z[it];
     }
     if (tid < Q) {  // wave 0: steps and their inclusive cumulative sum (exp2 domain)
-      const bool ok = tid < nt_valid;
-      const float dtv = ok ? softplus(pf.dt + bias) : 0.0f;  // a token past the end is a zero step
+      const float dtv = tid < nt_valid ? softplus(pf.dt + bias) : 0.0f;  // past the end: a zero step
       float cs = dtv * A2;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -191,54 +219,63 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       sE[tid] = fast_exp2(cs);
       sW[tid] = fast_exp2(cs_last - cs) * dtv;
     }
-    // z of this chunk for the epilogue (rows i = 16It + 4lg + r, column p_own)
-    float zv[4][4];
-    if (k.z) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * it + 4 * lg + r;
-          const int64_t t = t0 + (i < nt_valid ? i : 0);
-          zv[it][r] = bf16_to_f32(k.z[((b * L + t) * H + h) * P + p_own]);
-        }
-    }
     // the next chunk's loads run during this chunk's compute
     load_chunk(pf, c + 1);
     __syncthreads();
 
-    // ---- 2. G^T tiles -> M (lower triangle), shared out over the waves
-    for (int ti = w; ti < 10; ti += 4) {
-      // ti -> (Jt, It), It >= Jt: (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
-      const int Jt = ti < 4 ? 0 : (ti < 7 ? 1 : (ti < 9 ? 2 : 3));
-      const int It = ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3));
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- 2. G^T tiles -> M (lower triangle): wave w takes tiles w, w+4, w+8
+    {
+      f32x4 acc[3];
+      int Jt[3], It[3];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt + li) * LDB + 32 * kb + 8 * lg));
-        const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It + li) * LDB + 32 * kb + 8 * lg));
-        acc = mfma(a, bb, acc);
+      for (int u = 0; u < 3; ++u) {
+        const int ti = w + 4 * u < 10 ? w + 4 * u : w;  // waves 2, 3 redo a tile, then skip its store
+        // ti -> (Jt, It), It >= Jt: (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
+        Jt[u] = ti < 4 ? 0 : (ti < 7 ? 1 : (ti < 9 ? 2 : 3));
+        It[u] = ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3));
+        acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // acc[r] = G[i][j], i = 16It + li, j = 16Jt + 4lg + r
-      const int i = 16 * It + li;
-      const float csi = sCS[i];
-      float m[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * Jt + 4 * lg + r;
-        m[r] = j <= i ? acc[r] * fast_exp2(csi - sCS[j]) * sDT[j] : 0.0f;
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt[u] + li) * LDB + 32 * kb + 8 * lg));
+          const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDB + 32 * kb + 8 * lg));
+          acc[u] = mfma(a, bb, acc[u]);
+        }
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        if (w + 4 * u >= 10) continue;
+        // acc[r] = G[i][j], i = 16It + li, j = 16Jt + 4lg + r
+        const int i = 16 * It[u] + li;
+        const float csi = sCS[i];
+        float m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * Jt[u] + 4 * lg + r;
+          m[r] = j <= i ? acc[u][r] * fast_exp2(csi - sCS[j]) * sDT[j] : 0.0f;
+        }
+        uint32_t* dst = (uint32_t*)(sM + i * LDM + 16 * Jt[u] + 4 * lg);
+        dst[0] = pack2(m[0], m[1]);
+        dst[1] = pack2(m[2], m[3]);
       }
-      uint32_t* dst = (uint32_t*)(sM + i * LDM + 16 * Jt + 4 * lg);
-      dst[0] = pack2(m[0], m[1]);
-      dst[1] = pack2(m[2], m[3]);
     }
 
     // ---- x of this wave's 16 columns as B operands: X[j][p_own], j = 32kb + 8lg + e
-    float xw[2][8];
+    bf16x8 xop[2], wxop[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 v, vw;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xw[kb][e] = bf16_to_f32(sX[(32 * kb + 8 * lg + e) * LDX + p_own]);
+      for (int e = 0; e < 4; ++e) {
+        const int j = 32 * kb + 8 * lg + 2 * e;
+        const float x0 = bf16_to_f32(sX[j * LDX + p_own]), x1 = bf16_to_f32(sX[(j + 1) * LDX + p_own]);
+        v[e] = pack2(x0, x1);
+        vw[e] = pack2(x0 * sW[j], x1 * sW[j + 1]);
+      }
+      xop[kb] = as_bf16x8(v);
+      wxop[kb] = as_bf16x8(vw);
+    }
 
     // ---- 3. Y = C S_in^T (before the state moves on), rows scaled by exp(cs_i)
     f32x4 yacc[4];
@@ -267,40 +304,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) yacc[it][r] *= sE[16 * it + 4 * lg + r];
 
-    __syncthreads();  // M complete
-
-    // ---- 4. Y += M X
-    bf16x8 xop[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = pack2(xw[kb][2 * e], xw[kb][2 * e + 1]);
-      xop[kb] = as_bf16x8(v);
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && it < 2) continue;  // M[i][j] = 0 for j >= 32 when i < 32
-        const bf16x8 a = as_bf16x8(lds128(sM + (16 * it + li) * LDM + 32 * kb + 8 * lg));
-        yacc[it] = mfma(a, xop[kb], yacc[it]);
-      }
-    }
-
-    // ---- 5. S = exp(cs_last) S + B^T (w X)
+    // ---- 5. S = exp(cs_last) S + B^T (w X)   (independent of M: before the M barrier)
     const float dec_last = sE[Q - 1];
-    bf16x8 wxop[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 32 * kb + 8 * lg + 2 * e;
-        v[e] = pack2(xw[kb][2 * e] * sW[j], xw[kb][2 * e + 1] * sW[j + 1]);
-      }
-      wxop[kb] = as_bf16x8(v);
-    }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
@@ -312,18 +317,47 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       }
     }
 
-    // ---- 6. epilogue
+    __syncthreads();  // M complete; sB free
+
+    // ---- 4. Y += M X
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && it < 2) continue;  // M[i][j] = 0 for j >= 32 when i < 32
+        const bf16x8 a = as_bf16x8(lds128(sM + (16 * it + li) * LDM + 32 * kb + 8 * lg));
+        yacc[it] = mfma(a, xop[kb], yacc[it]);
+      }
+    }
+    // the output tile (fp32) into sB's space: Yt[i][p]
+    float* sY = (float*)sB;
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * lg + r;
-        if (i < nt_valid) {
-          float yv = yacc[it][r] + Dh * bf16_to_f32(sX[i * LDX + p_own]);
-          if (k.z) yv *= silu(zv[it][r]);
-          k.y[((b * L + t0 + i) * H + h) * P + p_own] = f32_to_bf16(yv);
+      for (int r = 0; r < 4; ++r) sY[(16 * it + 4 * lg + r) * LDY + p_own] = yacc[it][r];
+    __syncthreads();  // output tile complete; sM free
+
+    // ---- 6. epilogue in row pieces: y = (Y + D x) * silu(z), 8 elements per piece
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pc = pc0 + 4 * it;
+      const float* yr = sY + row * LDY + pc * 8;
+      const u32x4 xv = *(const u32x4*)(sX + row * LDX + pc * 8);
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v0 = yr[2 * e] + Dh * __uint_as_float(xv[e] << 16);
+        float v1 = yr[2 * e + 1] + Dh * __uint_as_float(xv[e] & 0xffff0000u);
+        if (gate) {
+          v0 *= silu(__uint_as_float(zkeep[it][e] << 16));
+          v1 *= silu(__uint_as_float(zkeep[it][e] & 0xffff0000u));
         }
+        out[e] = pack2(v0, v1);
       }
+      const bool ok = row < nt_valid;
+      __builtin_amdgcn_raw_buffer_store_b128(out, rY, (int)(ok ? xz_lane + it * 64 : kOOB),
+                                             ok ? (int)(t0 * xz_row) : 0, 0);
+    }
   }
 
   // final state, [b, h, p, n]
@@ -335,7 +369,10 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 }
 
 bool ssd_chunk_supported(const SSDArgs& a) {
-  return a.bf16 && a.P == P && a.N == NS && a.states == nullptr && a.batch * a.H <= 0x7fffffff;
+  // buffer offsets are 32-bit: each batch row of x / z / y / B / C must stay below 2^31 bytes
+  const int64_t row_x = a.L * a.H * P * 2, row_bc = a.L * a.G * NS * 2;
+  return a.bf16 && a.P == P && a.N == NS && a.states == nullptr && a.batch * a.H <= 0x7fffffff &&
+         row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
 }
 
 size_t ssd_chunk_ws(const SSDArgs&) { return 0; }
