@@ -95,6 +95,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: Hillis-Steele
+// shifts within each row of 16 lanes, then the last lane of row 0 (row 2) is
+// added to row 1 (row 3), and lane 31 to rows 2 and 3.
+#define SSCAN_DPP(x, ctrl, rmask) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), (rmask), 0xF, false))
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  x += SSCAN_DPP(x, 0x111, 0xF);  // row_shr:1
+  x += SSCAN_DPP(x, 0x112, 0xF);  // row_shr:2
+  x += SSCAN_DPP(x, 0x114, 0xF);  // row_shr:4
+  x += SSCAN_DPP(x, 0x118, 0xF);  // row_shr:8
+  x += SSCAN_DPP(x, 0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+  x += SSCAN_DPP(x, 0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // One chunk's global loads of one thread, in flight during the previous chunk:
 // B, C: 4 pieces of 8 bf16 (rows tid & 63, pieces (tid >> 6) + 4*it); x, z: 2 pieces
 // (rows tid & 63, pieces (tid >> 6) + 4*it); dt: one value (threads 0..63).
@@ -207,13 +222,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     }
     if (tid < Q) {  // wave 0: steps and their inclusive cumulative sum (exp2 domain)
       const float dtv = tid < nt_valid ? softplus(pf.dt + bias) : 0.0f;  // past the end: a zero step
-      float cs = dtv * A2;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(cs, off, 64);
-        if (tid >= off) cs += o;
-      }
-      const float cs_last = __shfl(cs, 63, 64);
+      const float cs = wave_inclusive_sum(dtv * A2);
+      const float cs_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
       sDT[tid] = dtv;
       sCS[tid] = cs;
       sE[tid] = fast_exp2(cs);
@@ -227,9 +237,10 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     {
       f32x4 acc[3];
       int Jt[3], It[3];
+      const int ntiles = w < 2 ? 3 : 2;  // tiles w, w+4, w+8 (< 10)
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
-        const int ti = w + 4 * u < 10 ? w + 4 * u : w;  // waves 2, 3 redo a tile, then skip its store
+        const int ti = w + 4 * u < 10 ? w + 4 * u : w;
         // ti -> (Jt, It), It >= Jt: (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
         Jt[u] = ti < 4 ? 0 : (ti < 7 ? 1 : (ti < 9 ? 2 : 3));
         It[u] = ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3));
@@ -239,13 +250,14 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
+          if (u == 2 && ntiles < 3) continue;  // wave-uniform
           const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt[u] + li) * LDB + 32 * kb + 8 * lg));
           const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDB + 32 * kb + 8 * lg));
           acc[u] = mfma(a, bb, acc[u]);
         }
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
-        if (w + 4 * u >= 10) continue;
+        if (u == 2 && ntiles < 3) continue;
         // acc[r] = G[i][j], i = 16It + li, j = 16Jt + 4lg + r
         const int i = 16 * It[u] + li;
         const float csi = sCS[i];
