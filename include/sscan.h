@@ -152,6 +152,37 @@ sscan_status sscan_ssd_step(const sscan_ssd_desc* desc, const float* state_input
                             const void* B, const void* C, const float* D, const void* z, void* y,
                             void* stream);
 
+/* Causal depthwise conv1d + silu, the step in front of the scan ("Mamba-2",
+ * section "The block, in order": x, B, C = silu(conv1d(xBC)), causal, width 4;
+ * "Mamba", tokentrails lineage, section "Code": depthwise, width 4).
+ * Output token t of channel c is
+ *     out[b, t, c] = silu(bias[c] + sum_{k=0}^{W-1} weight[c, k] * xx[t - W + 1 + k])
+ * where xx is x preceded by the W-1 inputs of conv_state_in (oldest first), or
+ * by zeros when conv_state_in is NULL.
+ *   x, out          [batch, seqlen, channels]  act
+ *   weight          [channels, width]          f32
+ *   bias            [channels] f32 or NULL
+ *   conv_state_in   [batch, channels, width-1] f32 or NULL
+ *   conv_state_out  [batch, channels, width-1] f32 or NULL: the last width-1 inputs
+ *                   (for the next call); may not alias conv_state_in.
+ * width in 1..8. seqlen may be 0 (the state passes through). */
+typedef struct sscan_conv_desc {
+  int64_t batch, seqlen, channels, width;
+  int32_t act;
+  int32_t reserved;   /* must be 0 */
+} sscan_conv_desc;
+
+sscan_status sscan_conv1d_silu(const sscan_conv_desc* desc, const void* x, const float* weight, const float* bias,
+                               const float* conv_state_in, void* out, float* conv_state_out, void* stream);
+
+/* Gated RMS norm after the SSD ("Mamba-2", section "The block, in order" and
+ * the note under it): g = y * silu(z), then
+ *     out = g / sqrt(mean(g^2) + eps) * weight
+ * with the mean over the whole width of a row (all heads), in fp32.
+ *   y, z, out  [rows, width] act;  weight [width] f32;  eps > 0. */
+sscan_status sscan_gated_rmsnorm(int64_t rows, int64_t width, int32_t act, const void* y, const void* z,
+                                 const float* weight, float eps, void* out, void* stream);
+
 /* Text of a status code (static storage). */
 const char* sscan_status_string(int status);
 /* Detail of the last failing call on this thread (thread-local storage). */

@@ -20,8 +20,8 @@ F32, BF16 = 0, 1
 STATUS_NAMES = ["SSCAN_OK", "SSCAN_ERR_NULL", "SSCAN_ERR_SHAPE", "SSCAN_ERR_DTYPE", "SSCAN_ERR_UNSUPPORTED",
                 "SSCAN_ERR_NOT_DEVICE", "SSCAN_ERR_ALIGN", "SSCAN_ERR_ALIAS", "SSCAN_ERR_WORKSPACE", "SSCAN_ERR_HIP"]
 EXPORTS = ["sscan_mamba1_workspace_size", "sscan_mamba1_fwd", "sscan_step", "sscan_ssd_workspace_size",
-           "sscan_ssd_fwd", "sscan_ssd_step", "sscan_status_string", "sscan_last_error", "sscan_abi_version",
-           "sscan_set_pointer_checks"]
+           "sscan_ssd_fwd", "sscan_ssd_step", "sscan_conv1d_silu", "sscan_gated_rmsnorm", "sscan_status_string",
+           "sscan_last_error", "sscan_abi_version", "sscan_set_pointer_checks"]
 
 
 class Mamba1Desc(ctypes.Structure):
@@ -34,6 +34,11 @@ class SSDDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("head_dim", ctypes.c_int64), ("state_dim", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("act", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("act", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SscanError(RuntimeError):
@@ -71,6 +76,10 @@ def lib():
     L.sscan_ssd_fwd.restype = I
     L.sscan_ssd_step.argtypes = [SD] + [P] * 12
     L.sscan_ssd_step.restype = I
+    L.sscan_conv1d_silu.argtypes = [ctypes.POINTER(ConvDesc)] + [P] * 7
+    L.sscan_conv1d_silu.restype = I
+    L.sscan_gated_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, P, P, P, ctypes.c_float, P, P]
+    L.sscan_gated_rmsnorm.restype = I
     L.sscan_status_string.argtypes = [I]
     L.sscan_status_string.restype = ctypes.c_char_p
     L.sscan_last_error.argtypes = []
@@ -236,6 +245,37 @@ def sscan_ssd_step(state_input, x, dt_raw, dt_bias, A_log, B, C, D, z=None, y=No
                                _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
                                _stream(stream)))
     return y, state_output
+
+
+def sscan_conv1d_silu(x, weight, bias=None, conv_state_in=None, out=None, conv_state_out=None,
+                      want_state=True, stream=None):
+    """Causal depthwise conv1d + silu. x: [b, L, Dc] (f32/bf16); weight: [Dc, W] f32;
+    conv state [b, Dc, W-1] f32. Returns (out, conv_state_out or None)."""
+    b, L, Dc = x.shape
+    W = weight.shape[1]
+    for n, t in (("weight", weight), ("bias", bias), ("conv_state_in", conv_state_in)):
+        _f32(n, t)
+    desc = ConvDesc(b, L, Dc, W, _act_code(x), 0)
+    if out is None:
+        out = torch.empty_like(x)
+    if conv_state_out is None and want_state and W > 1:
+        conv_state_out = torch.empty((b, Dc, W - 1), dtype=torch.float32, device=x.device)
+    check(lib().sscan_conv1d_silu(ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state_in),
+                                  _ptr(out), _ptr(conv_state_out), _stream(stream)))
+    return out, conv_state_out
+
+
+def sscan_gated_rmsnorm(y, z, weight, eps, out=None, stream=None):
+    """out = (y * silu(z)) / sqrt(mean over the last axis + eps) * weight. y, z: [..., width]."""
+    _same("z", z, y.dtype)
+    _f32("weight", weight)
+    width = y.shape[-1]
+    rows = y.numel() // width if width else 0
+    if out is None:
+        out = torch.empty_like(y)
+    check(lib().sscan_gated_rmsnorm(rows, width, _act_code(y), _ptr(y), _ptr(z), _ptr(weight), float(eps), _ptr(out),
+                                    _stream(stream)))
+    return out
 
 
 def ssd_state_key_first(state: torch.Tensor) -> torch.Tensor:

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "launch.hpp"
+#include "mixer_ops.hpp"
 
 namespace {
 
@@ -324,6 +325,60 @@ sscan_status sscan_ssd_step(const sscan_ssd_desc* d, const float* state_input, f
   a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
   a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = nullptr;
   return hip_status(sscan::launch_ssd_step(a, (hipStream_t)stream), "sscan_ssd_step launch");
+}
+
+sscan_status sscan_conv1d_silu(const sscan_conv_desc* d, const void* x, const float* weight, const float* bias,
+                               const float* conv_state_in, void* out, float* conv_state_out, void* stream) {
+  if (!d) return fail(SSCAN_ERR_NULL, "descriptor is NULL");
+  if (d->batch < 0 || d->seqlen < 0 || d->channels <= 0 || d->width <= 0)
+    return fail(SSCAN_ERR_SHAPE, "need batch >= 0, seqlen >= 0, channels > 0, width > 0");
+  if (d->batch >= kMaxDim || d->seqlen >= kMaxDim || d->channels >= kMaxDim)
+    return fail(SSCAN_ERR_SHAPE, "a size exceeds 2^31");
+  if (d->reserved != 0) return fail(SSCAN_ERR_SHAPE, "reserved must be 0");
+  if (d->act != SSCAN_F32 && d->act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
+  if (d->width > 8) return fail(SSCAN_ERR_UNSUPPORTED, "width must be <= 8");
+  if (d->batch > 65535) return fail(SSCAN_ERR_UNSUPPORTED, "batch must be <= 65535");
+  const int64_t b = d->batch, L = d->seqlen, Dc = d->channels, W = d->width;
+  const size_t es = d->act == SSCAN_BF16 ? 2 : 4;
+  const size_t act_bytes = (size_t)(b * L * Dc) * es, st_bytes = (size_t)(b * Dc * (W - 1)) * 4;
+  const Buf bufs[] = {
+      {"x", x, act_bytes, false},
+      {"weight", weight, (size_t)(Dc * W) * 4, false},
+      {"bias", bias, (size_t)Dc * 4, false},
+      {"conv_state_in", conv_state_in, st_bytes, false},
+      {"out", out, act_bytes, true},
+      {"conv_state_out", conv_state_out, st_bytes, true},
+  };
+  const bool req[] = {true, true, false, false, true, false};
+  sscan_status st = check_buffers(bufs, 6, req, nullptr, nullptr);
+  if (st != SSCAN_OK) return st;
+  sscan::ConvArgs a{};
+  a.batch = b; a.L = L; a.Dc = Dc; a.W = W; a.bf16 = d->act == SSCAN_BF16;
+  a.x = x; a.weight = weight; a.bias = bias; a.state_in = conv_state_in; a.out = out; a.state_out = conv_state_out;
+  return hip_status(sscan::launch_conv1d_silu(a, (hipStream_t)stream), "sscan_conv1d_silu launch");
+}
+
+sscan_status sscan_gated_rmsnorm(int64_t rows, int64_t width, int32_t act, const void* y, const void* z,
+                                 const float* weight, float eps, void* out, void* stream) {
+  if (rows < 0 || width <= 0) return fail(SSCAN_ERR_SHAPE, "need rows >= 0 and width > 0");
+  if (rows >= kMaxDim || width >= kMaxDim) return fail(SSCAN_ERR_SHAPE, "a size exceeds 2^31");
+  if (!(eps > 0.0f)) return fail(SSCAN_ERR_SHAPE, "eps must be > 0");
+  if (act != SSCAN_F32 && act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
+  const size_t es = act == SSCAN_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)(rows * width) * es;
+  const Buf bufs[] = {
+      {"y", y, bytes, false},
+      {"z", z, bytes, false},
+      {"weight", weight, (size_t)width * 4, false},
+      {"out", out, bytes, true},
+  };
+  const bool req[] = {true, true, true, true};
+  sscan_status st = check_buffers(bufs, 4, req, nullptr, nullptr);
+  if (st != SSCAN_OK) return st;
+  sscan::NormArgs a{};
+  a.rows = rows; a.width = width; a.bf16 = act == SSCAN_BF16; a.eps = eps;
+  a.y = y; a.z = z; a.weight = weight; a.out = out;
+  return hip_status(sscan::launch_gated_rmsnorm(a, (hipStream_t)stream), "sscan_gated_rmsnorm launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,31 @@
+// mixer_ops.hpp -- internal interface of the conv1d + silu and gated RMS norm kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sscan {
+
+struct ConvArgs {
+  int64_t batch, L, Dc, W;
+  bool bf16;
+  const void* x;
+  const float* weight;
+  const float* bias;
+  const float* state_in;
+  void* out;
+  float* state_out;
+};
+hipError_t launch_conv1d_silu(const ConvArgs& a, hipStream_t s);
+
+struct NormArgs {
+  int64_t rows, width;
+  bool bf16;
+  float eps;
+  const void* y;
+  const void* z;
+  const float* weight;
+  void* out;
+};
+hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
+
+}  // namespace sscan

@@ -202,3 +202,24 @@ def test_ssd_host_pointers_refused():
     assert status(L.sscan_ssd_fwd(ctypes.byref(d), *ptrs, ws, None)) == "SSCAN_ERR_NOT_DEVICE"
     # the pointer check can be switched off; the previous setting is returned
     assert bd.set_pointer_checks(True) is True
+
+
+def test_conv_and_norm_errors():
+    L = bd.lib()
+    h = Host()
+    d = bd.ConvDesc(2, 8, 64, 4, 0, 0)
+    p = [h.buf(2 * 8 * 64 * 4), h.buf(64 * 4 * 4), None, None, h.buf(2 * 8 * 64 * 4), None]
+    assert status(L.sscan_conv1d_silu(ctypes.byref(d), *p, None)) == "SSCAN_ERR_NOT_DEVICE"
+    assert status(L.sscan_conv1d_silu(ctypes.byref(bd.ConvDesc(2, 8, 64, 9, 0, 0)), *p, None)) == "SSCAN_ERR_UNSUPPORTED"
+    assert status(L.sscan_conv1d_silu(ctypes.byref(bd.ConvDesc(2, 8, 64, 0, 0, 0)), *p, None)) == "SSCAN_ERR_SHAPE"
+    assert status(L.sscan_conv1d_silu(ctypes.byref(bd.ConvDesc(2, 8, 64, 4, 3, 0)), *p, None)) == "SSCAN_ERR_DTYPE"
+    assert status(L.sscan_conv1d_silu(None, *p, None)) == "SSCAN_ERR_NULL"
+    q = list(p)
+    q[4] = q[0]
+    assert status(L.sscan_conv1d_silu(ctypes.byref(d), *q, None)) == "SSCAN_ERR_ALIAS"
+    y, z, w, o = h.buf(4 * 64 * 4), h.buf(4 * 64 * 4), h.buf(64 * 4), h.buf(4 * 64 * 4)
+    assert status(L.sscan_gated_rmsnorm(4, 64, 0, y, z, w, 1e-5, o, None)) == "SSCAN_ERR_NOT_DEVICE"
+    assert status(L.sscan_gated_rmsnorm(4, 64, 0, y, z, w, 0.0, o, None)) == "SSCAN_ERR_SHAPE"
+    assert status(L.sscan_gated_rmsnorm(4, 0, 0, y, z, w, 1e-5, o, None)) == "SSCAN_ERR_SHAPE"
+    assert status(L.sscan_gated_rmsnorm(4, 64, 5, y, z, w, 1e-5, o, None)) == "SSCAN_ERR_DTYPE"
+    assert status(L.sscan_gated_rmsnorm(4, 64, 0, y, z, w, 1e-5, y, None)) == "SSCAN_ERR_ALIAS"

@@ -1,0 +1,123 @@
+"""GPU parity of the steps next to the scan: causal depthwise conv1d + silu (with
+its carried state) and the gated RMS norm, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_model_sscan_amd import binding as bd
+from state_space_model_sscan_amd import inputs as gen
+
+from _gpu import check, dev, host, par, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def conv_inputs(b, L, Dc, W, act, seed, state):
+    rng = np.random.default_rng(seed)
+    x = gen.bf16_round(rng.standard_normal((b, L, Dc)).astype(np.float32)) if act == "bf16" else \
+        rng.standard_normal((b, L, Dc)).astype(np.float32)
+    w = (rng.standard_normal((Dc, W)) * 0.5).astype(np.float32)
+    bias = (rng.standard_normal(Dc) * 0.1).astype(np.float32)
+    st = rng.standard_normal((b, Dc, W - 1)).astype(np.float32) if state else None
+    return x, w, bias, st
+
+
+CONV_CASES = [
+    # batch, seqlen, channels, width, act, state_in, bias
+    (1, 1, 64, 4, "f32", False, True),
+    (2, 2, 100, 4, "f32", True, True),      # shorter than the history
+    (2, 3, 96, 4, "bf16", True, False),
+    (3, 64, 1536, 4, "bf16", False, True),
+    (2, 65, 257, 4, "f32", True, True),
+    (1, 1000, 1792, 4, "bf16", True, True),  # mamba2-130m's xBC width
+    (2, 130, 64, 1, "f32", False, True),
+    (2, 70, 64, 7, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "b%d_L%d_D%d_W%d_%s_s%d_b%d" % c)
+def test_conv1d_silu(case):
+    b, L, Dc, W, act, state, use_bias = case
+    say("conv case", case)
+    x, w, bias, st = conv_inputs(b, L, Dc, W, act, L + Dc, state)
+    bias = bias if use_bias else None
+    ref, ref_st = oracle.conv1d_silu(x, w, bias, st)
+    out, st_out = bd.sscan_conv1d_silu(dev(x, act), par(w), par(bias), par(st))
+    torch.cuda.synchronize()
+    check(host(out), ref, act, "conv out")
+    if W > 1:
+        # the carried state is a copy of inputs: exact
+        assert np.array_equal(host(st_out), ref_st.astype(np.float32).astype(np.float64))
+
+
+def test_conv1d_state_chain_equals_whole():
+    b, L, Dc, W = 2, 300, 128, 4
+    x, w, bias, _ = conv_inputs(b, L, Dc, W, "f32", 5, False)
+    whole, st = bd.sscan_conv1d_silu(dev(x, "f32"), par(w), par(bias))
+    a, sa = bd.sscan_conv1d_silu(dev(x[:, :100], "f32"), par(w), par(bias))
+    c, sc = bd.sscan_conv1d_silu(dev(x[:, 100:101], "f32"), par(w), par(bias), sa)   # one decode token
+    d, sd = bd.sscan_conv1d_silu(dev(x[:, 101:], "f32"), par(w), par(bias), sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.concatenate([host(a), host(c), host(d)], 1), host(whole))
+    assert np.array_equal(host(sd), host(st))
+
+
+NORM_CASES = [(1, 1536, "f32"), (37, 1536, "bf16"), (5, 5120, "bf16"), (3, 333, "f32"), (700, 1536, "bf16")]
+
+
+@pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "r%d_w%d_%s" % c)
+def test_gated_rmsnorm(case):
+    rows, width, act = case
+    rng = np.random.default_rng(rows + width)
+    y = rng.standard_normal((rows, width)).astype(np.float32)
+    z = rng.standard_normal((rows, width)).astype(np.float32)
+    if act == "bf16":
+        y, z = gen.bf16_round(y), gen.bf16_round(z)
+    wt = rng.uniform(0.5, 2.0, width).astype(np.float32)
+    ref = oracle.gated_rmsnorm(y, z, wt, 1e-5)
+    out = bd.sscan_gated_rmsnorm(dev(y, act), dev(z, act), par(wt), 1e-5)
+    torch.cuda.synchronize()
+    check(host(out), ref, act, "norm out")
+
+
+def test_mamba2_mixer_core_chain():
+    """conv1d+silu over xBC, then the SSD, then the gated norm, on the Mamba2-130m mixer
+    widths (24 heads x 64, state 128, one group): each step's GPU output feeds the next GPU
+    step; the oracle runs the same chain on the same inputs."""
+    b, L, H, P, N = 2, 200, 24, 64, 128
+    Dx = H * P
+    width = Dx + 2 * N
+    rng = np.random.default_rng(9)
+    xbc = gen.bf16_round(rng.standard_normal((b, L, width)).astype(np.float32))
+    w = (rng.standard_normal((width, 4)) * 0.5).astype(np.float32)
+    cb = (rng.standard_normal(width) * 0.1).astype(np.float32)
+    s = gen.make_ssd(b, L, H, P, N, act="bf16", seed=10, gate=False, h0=False)
+    z = gen.bf16_round(rng.standard_normal((b, L, H, P)).astype(np.float32))
+    nw = rng.uniform(0.5, 1.5, Dx).astype(np.float32)
+    # GPU chain
+    conv, _ = bd.sscan_conv1d_silu(dev(xbc, "bf16"), par(w), par(cb), want_state=False)
+    xg = conv[..., :Dx].contiguous().view(b, L, H, P)
+    Bg = conv[..., Dx:Dx + N].contiguous().view(b, L, 1, N)
+    Cg = conv[..., Dx + N:].contiguous().view(b, L, 1, N)
+    yg, hg, _ = bd.sscan_ssd_fwd(xg, dev(s.dt_raw, "bf16"), par(s.dt_bias), par(s.A_log), Bg, Cg, par(s.D))
+    og = bd.sscan_gated_rmsnorm(yg.view(b, L, Dx), dev(z, "bf16").view(b, L, Dx), par(nw), 1e-5)
+    torch.cuda.synchronize()
+    # oracle chain on the GPU's bf16 intermediates (each step compared on its own inputs)
+    conv_ref, _ = oracle.conv1d_silu(xbc, w, cb)
+    check(host(conv), conv_ref, "bf16", "conv")
+    ch = host(conv)
+    xs, Bs, Cs = ch[..., :Dx].reshape(b, L, H, P), ch[..., Dx:Dx + N].reshape(b, L, 1, N), \
+        ch[..., Dx + N:].reshape(b, L, 1, N)
+    y_ref, h_ref, _ = oracle.ssd(xs, s.dt_raw, s.dt_bias, s.A_log, Bs, Cs, s.D)
+    check(host(yg), y_ref, "bf16", "ssd y")
+    check(host(hg), h_ref, "bf16", "ssd state")
+    o_ref = oracle.gated_rmsnorm(host(yg).reshape(b, L, Dx), z.reshape(b, L, Dx), nw, 1e-5)
+    check(host(og), o_ref, "bf16", "gated norm")
