@@ -15,8 +15,10 @@ on this host. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +33,37 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
 # slot; v_exp_f32 takes two slots). Peak in T lane-slots/s.
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "scan tokens/s & % HBM roofline (Mamba-1); SSD tokens/s & % MFMA peak"
+MAIN_KERNEL = "m1_fast_kernel<bf16, 16 states, 4 lanes per channel, gate>"
+# sources of the main kernel: HBM traffic from hardware counters is reported only
+# while these hash to the value recorded with the counters
+MAIN_KERNEL_SOURCES = ["state_space_model_sscan_amd/csrc/m1_fast_impl.hpp",
+                       "state_space_model_sscan_amd/csrc/m1_fast.hip",
+                       "state_space_model_sscan_amd/csrc/device_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+
+
+def sources_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_key):
+    """HBM bytes per launch measured by FETCH_SIZE/WRITE_SIZE (scaled by a plain copy's
+    reading), from the counter summary in profiles/, if it is for the current source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(kernel_key)
+    if not rec or rec.get("sources_sha256_16") != sources_hash(rec.get("sources", [])):
+        return None
+    return rec
 
 
 def log(*a):
@@ -202,6 +235,17 @@ def cpu_baseline(inp, repeats=2):
                        "%.2f s each" % (inp.batch, inp.seqlen, inp.channels, inp.state_dim, repeats, best))
 
 
+def copy_calibration(torch, gib=1, reps=3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = gib * (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: %d x copy of %d bytes" % (reps, n * 4))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +253,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the main workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one MI355X). "
@@ -222,6 +268,8 @@ def main():
 
     bd.lib()  # fails loudly if libsscan.so is missing
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     log("bench: workload 1 (main)")
     m = bench_mamba1(1, args.steps, args.warmup, torch, bd, gen)
@@ -245,6 +293,8 @@ def main():
 
     inp = m["inp"]
     valu_frac = m["valu_tslots"] / VALU_PEAK_TSLOTS
+    tr = recorded_traffic("mamba1_workload1")
+    traffic = None if tr is None else tr["hbm_bytes_per_launch"]
     line = {
         "metric": METRIC,
         "value": m["tokens_per_s"],
@@ -262,8 +312,8 @@ def main():
                    "channels": inp.channels, "state_dim": inp.state_dim, "ngroups": inp.ngroups,
                    "gate": True, "state": "fp32"},
         "roofline": {"bound": "alu", "achieved": m["valu_tslots"], "peak": VALU_PEAK_TSLOTS,
-                     "unit": "T VALU-slots/s", "frac": valu_frac, "traffic": None,
-                     "kernel": "sscan_mamba1_fwd (all its kernels)", "kernel_ms": m["kernel_ms"],
+                     "unit": "T VALU-slots/s", "frac": valu_frac, "traffic": traffic,
+                     "kernel": MAIN_KERNEL, "kernel_ms": m["kernel_ms"],
                      "hbm_gbs": m["hbm_gbs"], "hbm_frac": m["hbm_frac"], "algorithmic_bytes": m["bytes"],
                      "updates_per_s": m["updates_per_s"]},
         "cpu_baseline": cpu,

@@ -43,6 +43,23 @@ __device__ __forceinline__ float softplus(float v) {
   return fmaxf(v, 0.0f) + l;
 }
 
+// softplus without the rounding correction of 1 + e. Its absolute error in dt is
+// below 2^-24 (the rounding of 1 + e), which enters the scan only through
+// dt * x * B and dt * A: negligible next to fp32 rounding of the state. Used in the
+// hot loops; softplus() above where a step is computed once per call.
+__device__ __forceinline__ float softplus_fast(float v) {
+  const float e = fast_exp2(-fabsf(v) * kLog2e);
+  return fmaf(fast_log2(1.0f + e), kLn2, fmaxf(v, 0.0f));
+}
+
+// Bijective map of a linear block index onto an order in which consecutive
+// logical blocks are dispatched to the same XCD (the dispatcher places block i
+// on XCD i % 8), so neighbours that share cache lines share an L2.
+__device__ __forceinline__ int64_t xcd_local_order(int64_t lin, int64_t n) {
+  const int64_t xcd = lin % 8, k = lin / 8, q = n / 8, r = n % 8;
+  return xcd * q + (xcd < r ? xcd : r) + k;
+}
+
 // silu(z) = z / (1 + e^-z); z -> -inf gives -0, z -> +inf gives z.
 __device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 

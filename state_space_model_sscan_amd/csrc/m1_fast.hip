@@ -21,7 +21,7 @@ hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const flo
   k.bc_eps = a.bc_eps;
   const int K = (int)plan.lanes_per_channel;
   const int64_t cpw = 64 / K;
-  const dim3 grid((unsigned)((a.Dc + cpw - 1) / cpw), (unsigned)plan.nslices, (unsigned)a.batch);
+  const dim3 grid((unsigned)(((a.Dc + cpw - 1) / cpw) * plan.nslices * a.batch));
   const bool gate = a.z != nullptr, st = a.states != nullptr;
   const int np = a.N <= 16 ? 16 : a.N <= 32 ? 32 : 64;
   if (a.bf16) {

@@ -216,12 +216,17 @@ __global__ __launch_bounds__(64) void m1_fast_kernel(M1F k) {
 
   const int lane = threadIdx.x;
   const int q = lane % K;
-  const int64_t c0 = (int64_t)blockIdx.x * CPW;
+  // 1-D grid of (channel block, slice, batch); neighbouring channel blocks share
+  // 128-byte lines of x/dt/z/y, so they go to one XCD
+  const int64_t ncb = (k.Dc + CPW - 1) / CPW;
+  const int64_t lb = xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t cb = lb % ncb;
+  const int s = (int)((lb / ncb) % k.nslices);
+  const int64_t b = lb / (ncb * k.nslices);
+  const int64_t c0 = cb * CPW;
   const int64_t c = c0 + lane / K;
   const bool active = c < k.Dc;
   const int64_t cc = active ? c : k.Dc - 1;
-  const int s = blockIdx.y;
-  const int64_t b = blockIdx.z;
   const int64_t t_begin = (int64_t)s * k.slice_len;
   const int64_t t_end = min(k.L, t_begin + (int64_t)k.slice_len);
   const int g = (int)(c0 / k.per_group);  // the host guarantees one group per wave
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(64) void m1_fast_kernel(M1F k) {
       const int64_t tq = tb + gi * K + q;  // this lane's token in group gi
       const bool vq = tq < t_end;
       const float xv = BufAct<T>::f(cur.x[gi]);
-      const float sp = softplus(BufAct<T>::f(cur.d[gi]) + bias);
+      const float sp = softplus_fast(BufAct<T>::f(cur.d[gi]) + bias);
       const float dtv = vq ? sp : 0.0f;  // a token past the end is a zero step
       const float dtx = dtv * xv;
       float yp_[K];

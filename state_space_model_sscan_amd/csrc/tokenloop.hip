@@ -1,5 +1,7 @@
 // tokenloop.hip -- host side of the token-loop scan: slicing plan and launches.
 // The kernels are in tokenloop_impl.hpp, instantiated in tl_*.hip.
+#include <cstdlib>
+
 #include "tokenloop_impl.hpp"
 
 namespace sscan {
@@ -74,9 +76,11 @@ static hipError_t zero_length(const float* h0, float* h_out, int64_t nst, hipStr
   return hipGetLastError();
 }
 
-// Mamba-1 prompt plan: K lanes per channel so that the grid covers the 1024
-// SIMDs of the chip, and slices (two-pass carry) only when even K = 4 leaves
-// fewer than 512 waves on a long sequence.
+// Mamba-1 prompt plan: K lanes per channel so that the grid puts two waves on
+// each of the 1024 SIMDs of the chip (measured on MI355X: at the Mamba-130m and
+// Falcon-Mamba-7b widths K = 4 beats K = 2 and K = 1, since a second wave per
+// SIMD hides latency that a lone wave exposes), and slices (two-pass carry) only
+// when even K = 4 leaves fewer than 512 waves on a long sequence.
 Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t es) {
   // a batch row the buffer offsets of the fast kernel cannot span: token-loop kernel
   if (L * Dc * es >= (int64_t(1) << 31)) {
@@ -87,7 +91,11 @@ Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t 
   Mamba1Plan p{1, L > 0 ? L : 1, 0, 1};
   auto waves = [&](int64_t K) { return batch * ((Dc * K + 63) / 64); };
   int64_t K = N > 32 ? 2 : 1;  // 64 states in one lane would spill
-  while (K < 4 && waves(K) < 1024) K *= 2;
+  while (K < 4 && waves(K) < 2048) K *= 2;
+  if (const char* e = getenv("SSCAN_M1_LANES")) {  // tuning override: 1, 2 or 4
+    const int64_t v = atoi(e);
+    if ((v == 1 && N <= 32) || v == 2 || v == 4) K = v;
+  }
   p.lanes_per_channel = K;
   const int64_t w = waves(K);
   if (w > 0 && w < 512 && L >= 1024) {
