@@ -186,22 +186,24 @@ def bench_ssd(steps, warmup, torch, bd, gen):
 
 
 def bench_step(torch, bd, gen, calls=512):
-    """Workload 2 as `calls` one-token sscan_step calls, state updated in place."""
+    """Workload 2 as `calls` one-token sscan_step calls, state updated in place: timed
+    eagerly (includes the Python/ctypes cost of each call) and as a HIP graph that
+    replays the same `calls` launches (the GPU-side cost per step)."""
     inp = gen.make_workload(2)
     base = upload(inp, torch)
     b, Dc = inp.batch, inp.channels
-    xs = [base[k][:, t:t + 1].contiguous() for k in ("x",) for t in range(calls)]
+    xs = [base["x"][:, t:t + 1].contiguous() for t in range(calls)]
     dts = [base["dt_raw"][:, t:t + 1].contiguous() for t in range(calls)]
     zs = [base["z"][:, t:t + 1].contiguous() for t in range(calls)]
     Bs = [base["B"][:, t:t + 1].contiguous() for t in range(calls)]
     Cs = [base["C"][:, t:t + 1].contiguous() for t in range(calls)]
     state = base["state_input"].clone()
-    y = torch.empty_like(xs[0])
+    ys = [torch.empty_like(xs[0]) for _ in range(calls)]
 
     def run(n):
         for t in range(n):
             bd.sscan_step(state, xs[t], dts[t], base["dt_bias"], base["A_log"], Bs[t], Cs[t], base["D"], zs[t],
-                          y=y, state_output=state)
+                          y=ys[t], state_output=state)
 
     run(8)
     torch.cuda.synchronize()
@@ -213,10 +215,32 @@ def bench_step(torch, bd, gen, calls=512):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e6 / calls
+    eager_gpu = e0.elapsed_time(e1) * 1e3 / calls
+    # the same calls captured once into a HIP graph (pointer checks are host-side queries:
+    # off while capturing), then replayed
+    graph_us = None
+    try:
+        prev = bd.set_pointer_checks(False)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(calls)
+        bd.set_pointer_checks(prev)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    except Exception as ex:  # report, do not fail the bench
+        log("graph capture of the decode steps failed: %s" % ex)
     per_call_bytes = 2 * b * Dc * 16 * 4 + 4 * b * Dc * 4 + 2 * b * 16 * 4 + (2 * Dc + Dc * 16) * 4
     return dict(workload=gen.WORKLOADS[2]["name"] + " as %d sscan_step calls" % calls,
-                us_per_step_wall=wall, us_per_step_gpu=e0.elapsed_time(e1) * 1e3 / calls,
-                bytes_per_call=per_call_bytes)
+                us_per_step_wall=wall, us_per_step_gpu_eager=eager_gpu, us_per_step_graph=graph_us,
+                bytes_per_call=per_call_bytes,
+                graph_gbs=None if not graph_us else per_call_bytes / (graph_us * 1e-6) / 1e9)
 
 
 def cpu_baseline(inp, repeats=2):

@@ -180,51 +180,69 @@ __global__ __launch_bounds__(64) void tokenloop_scan_kernel(TLK k) {
   }
 }
 
-// One token per call: lane = channel; the state is read, updated, then y is read
-// from the updated state ("Mamba", section "The state").
+// One token per call: four lanes per channel, each holding a quarter of its
+// state_dim entries; the state is read, updated, then y is read from the
+// updated state ("Mamba", section "The state"). The four partial read-outs are
+// summed with a DPP butterfly inside the quad, and lane 0 of the quad stores y.
 template <typename T, int NP, bool SSD, bool GATE>
-__global__ __launch_bounds__(64) void tokenloop_step_kernel(TLK k) {
-  const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
+__global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
+  constexpr int NQ = (NP + 3) / 4;  // entries per lane
+  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = (int)(gl & 3);
+  const int64_t c = gl >> 2;
   const int64_t b = blockIdx.y;
-  if (c >= k.Dc) return;
-  const int g = (int)(c / k.per_group);
-  const int64_t hd = SSD ? c / k.P : c;
-  const int64_t sidx = (b * k.Dc + c) * k.N;
+  const bool active = c < k.Dc;
+  const int64_t cc = active ? c : k.Dc - 1;  // inactive lanes compute on a valid channel, store nothing
+  const int g = (int)(cc / k.per_group);
+  const int64_t hd = SSD ? cc / k.P : cc;
+  const int64_t sidx = (b * k.Dc + cc) * k.N;
   const T* Bp = (const T*)k.B + (b * k.G + g) * k.N;
   const T* Cp = (const T*)k.C + (b * k.G + g) * k.N;
   float ib = 1.0f, ic = 1.0f;
   if (k.bc_eps > 0.0f) {
     float sb = 0.0f, sc = 0.0f;
-    for (int n = 0; n < k.N; ++n) {
+    for (int n = q; n < k.N; n += 4) {
       const float bv = Act<T>::ld(Bp + n), cv = Act<T>::ld(Cp + n);
       sb = fmaf(bv, bv, sb);
       sc = fmaf(cv, cv, sc);
     }
+    // sum over the quad (lanes q = 0..3 of this channel)
+    sb += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sb), 0xB1, 0xF, 0xF, false));
+    sc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sc), 0xB1, 0xF, 0xF, false));
+    sb += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sb), 0x4E, 0xF, 0xF, false));
+    sc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sc), 0x4E, 0xF, 0xF, false));
     ib = 1.0f / sqrtf(sb / (float)k.N + k.bc_eps);
     ic = 1.0f / sqrtf(sc / (float)k.N + k.bc_eps);
   }
-  const int64_t idx = b * k.Dc + c;  // seqlen 1
+  const int64_t idx = b * k.Dc + cc;  // seqlen 1
   const float xv = Act<T>::ld((const T*)k.x + idx);
   const float dtv = softplus(Act<T>::ld((const T*)k.dt + b * (SSD ? k.H : k.Dc) + hd) + k.dt_bias[hd]);
   const float dtx = dtv * xv;
-  const float dec0 = SSD ? fast_exp2(dtv * (-expf(k.A_log[hd]) * kLog2e)) : 0.0f;
-  float yv = k.D[hd] * xv;
-  float h[NP];
+  const float dec0 = SSD ? fast_exp2(dtv * (-fast_exp2(k.A_log[hd] * kLog2e) * kLog2e)) : 0.0f;
+  float acc = 0.0f;
+  float h[NQ];
 #pragma unroll
-  for (int n = 0; n < NP; ++n) {
+  for (int i = 0; i < NQ; ++i) {
+    const int n = q + 4 * i;  // entries q, q+4, ...: a quad reads 16 contiguous bytes per step
     if (n < k.N) {
-      const float dec = SSD ? dec0 : fast_exp2(dtv * (-expf(k.A_log[c * k.N + n]) * kLog2e));
-      h[n] = fmaf(dec, k.h0[sidx + n], dtx * (Act<T>::ld(Bp + n) * ib));
-      yv = fmaf(Act<T>::ld(Cp + n) * ic, h[n], yv);
+      const float dec = SSD ? dec0 : fast_exp2(dtv * (-fast_exp2(k.A_log[cc * k.N + n] * kLog2e) * kLog2e));
+      h[i] = fmaf(dec, k.h0[sidx + n], dtx * (Act<T>::ld(Bp + n) * ib));
+      acc = fmaf(Act<T>::ld(Cp + n) * ic, h[i], acc);
+    } else {
+      h[i] = 0.0f;
     }
   }
+  acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
+  acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+  float yv = acc + k.D[hd] * xv;
   if (GATE) yv *= silu(Act<T>::ld((const T*)k.z + idx));
-  Act<T>::st((T*)k.y + idx, yv);
+  if (active) {
+    if (q == 0) Act<T>::st((T*)k.y + idx, yv);
 #pragma unroll
-  for (int n = 0; n < NP; ++n)
-    if (n < k.N) k.h_out[sidx + n] = h[n];
+    for (int i = 0; i < NQ; ++i)
+      if (q + 4 * i < k.N) k.h_out[sidx + q + 4 * i] = h[i];
+  }
 }
-
 
 static int padded_n(int64_t N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : N <= 64 ? 64 : 128; }
 
@@ -275,7 +293,7 @@ void dispatch_pass1(const TLK& k, int64_t batch, hipStream_t s) {
 
 template <typename T, bool SSD>
 void dispatch_step(const TLK& k, int64_t batch, bool gate, hipStream_t s) {
-  const dim3 grid((unsigned)((k.Dc + 63) / 64), (unsigned)batch), blk(64);
+  const dim3 grid((unsigned)((k.Dc * 4 + 255) / 256), (unsigned)batch), blk(256);
 #define SSCAN_STEP(NP)                                                                           \
   if (gate) hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, true>), grid, blk, 0, s, k);   \
   else hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, false>), grid, blk, 0, s, k);

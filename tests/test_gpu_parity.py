@@ -248,3 +248,45 @@ def test_host_tensors_are_refused():
         bd.sscan_mamba1_fwd(t(inp.x), t(inp.dt_raw), t(inp.dt_bias), t(inp.A_log), t(inp.B), t(inp.C), t(inp.D),
                             y=torch.empty(1, 4, 64), state_output=torch.empty(1, 64, 16))
     assert e.value.name == "SSCAN_ERR_NOT_DEVICE"
+
+
+def test_decode_steps_replayed_from_a_hip_graph():
+    """512-style decode loop captured once and replayed: every replay matches the eager run
+    (the kernels launch no memset and allocate nothing)."""
+    inp = gen.make_mamba1(4, 24, 256, 16, act="f32", seed=31, gate=True, h0=True)
+    x, dt, z = dev(inp.x, "f32"), dev(inp.dt_raw, "f32"), dev(inp.z, "f32")
+    B, C = dev(inp.B, "f32"), dev(inp.C, "f32")
+    bias, alog, D = par(inp.dt_bias), par(inp.A_log), par(inp.D)
+    xs = [x[:, t:t + 1].contiguous() for t in range(inp.seqlen)]
+    ds = [dt[:, t:t + 1].contiguous() for t in range(inp.seqlen)]
+    zs = [z[:, t:t + 1].contiguous() for t in range(inp.seqlen)]
+    Bs = [B[:, t:t + 1].contiguous() for t in range(inp.seqlen)]
+    Cs = [C[:, t:t + 1].contiguous() for t in range(inp.seqlen)]
+    h0 = par(inp.h0)
+    state = h0.clone()
+    ys = [torch.empty_like(xs[0]) for _ in range(inp.seqlen)]
+
+    def run():
+        for t in range(inp.seqlen):
+            bd.sscan_step(state, xs[t], ds[t], bias, alog, Bs[t], Cs[t], D, zs[t], y=ys[t], state_output=state)
+
+    run()
+    torch.cuda.synchronize()
+    eager_y = torch.cat(ys, 1).clone()
+    eager_h = state.clone()
+    prev = bd.set_pointer_checks(False)
+    g = torch.cuda.CUDAGraph()
+    state.copy_(h0)
+    with torch.cuda.graph(g):
+        run()
+    bd.set_pointer_checks(prev)
+    for rep in range(3):
+        state.copy_(h0)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(ys, 1), eager_y), rep
+        assert torch.equal(state, eager_h), rep
+    yr, hr, _ = oracle.run_inputs(inp)
+    check(host(eager_y), yr, "f32", "y (steps)")
+    check(host(eager_h), hr, "f32", "state (steps)")
