@@ -260,14 +260,15 @@ def cpu_baseline(inp, repeats=2):
 
 
 def copy_calibration(torch, gib=1, reps=3):
-    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    """A plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
     n = gib * (1 << 30) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     for _ in range(reps):
-        b.copy_(a)
+        torch.add(a, 1.0, out=b)
     torch.cuda.synchronize()
-    log("copy calibration: %d x copy of %d bytes" % (reps, n * 4))
+    log("copy calibration: %d x elementwise copy of %d bytes" % (reps, n * 4))
 
 
 def main():
