@@ -33,11 +33,13 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
 # slot; v_exp_f32 takes two slots). Peak in T lane-slots/s.
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "scan tokens/s & % HBM roofline (Mamba-1); SSD tokens/s & % MFMA peak"
-MAIN_KERNEL = "m1_fast_kernel<bf16, 16 states, 4 lanes per channel, gate>"
+MAIN_KERNEL = "m1_row_kernel<bf16, 16 states, gate> (a 16-lane row per channel)"
 # sources of the main kernel: HBM traffic from hardware counters is reported only
 # while these hash to the value recorded with the counters
-MAIN_KERNEL_SOURCES = ["state_space_model_sscan_amd/csrc/m1_fast_impl.hpp",
+MAIN_KERNEL_SOURCES = ["state_space_model_sscan_amd/csrc/m1_row_impl.hpp",
+                       "state_space_model_sscan_amd/csrc/m1_fast_impl.hpp",
                        "state_space_model_sscan_amd/csrc/m1_fast.hip",
+                       "state_space_model_sscan_amd/csrc/m1r_bf16_16.hip",
                        "state_space_model_sscan_amd/csrc/device_common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 

@@ -169,7 +169,9 @@ const char* sscan_status_string(int st) {
 
 size_t sscan_mamba1_workspace_size(const sscan_mamba1_desc* d) {
   if (check_mamba1_desc(d, false) != SSCAN_OK) return 0;
-  return sscan::mamba1_plan(d->batch, d->seqlen, d->channels, d->state_dim, d->act == SSCAN_BF16 ? 2 : 4).ws_bytes;
+  return sscan::mamba1_plan(d->batch, d->seqlen, d->channels, d->state_dim, d->ngroups,
+                            d->act == SSCAN_BF16 ? 2 : 4)
+      .ws_bytes;
 }
 
 sscan_status sscan_mamba1_fwd(const sscan_mamba1_desc* d, const void* x, const void* dt_raw,
@@ -181,7 +183,7 @@ sscan_status sscan_mamba1_fwd(const sscan_mamba1_desc* d, const void* x, const v
   if (st != SSCAN_OK) return st;
   const int64_t b = d->batch, L = d->seqlen, Dc = d->channels, N = d->state_dim, G = d->ngroups;
   const size_t es = d->act == SSCAN_BF16 ? 2 : 4;
-  const sscan::Mamba1Plan plan = sscan::mamba1_plan(b, L, Dc, N, (int64_t)es);
+  const sscan::Mamba1Plan plan = sscan::mamba1_plan(b, L, Dc, N, G, (int64_t)es);
   const size_t act_bytes = (size_t)(b * L * Dc) * es, bc_bytes = (size_t)(b * L * G * N) * es;
   const size_t st_bytes = (size_t)(b * Dc * N) * 4;
   const Buf bufs[] = {

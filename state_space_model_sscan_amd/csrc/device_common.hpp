@@ -8,14 +8,10 @@ namespace sscan {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// bf16 <-> f32. Loads are exact; stores round to nearest even (NaN stays NaN).
+// bf16 <-> f32. Loads are exact; stores round to nearest even (NaN stays NaN):
+// gfx950 converts in one instruction (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename T> struct Act;
 template <> struct Act<float> {

@@ -32,7 +32,7 @@ struct Mamba1Plan {
   size_t ws_bytes;
   int64_t lanes_per_channel;
 };
-Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t es);  // 0 lanes: token loop
+Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t G, int64_t es);  // 0 lanes: token loop
 Mamba1Plan tokenloop_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N);  // token-loop kernel
 hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const float* ws_h, const float* ws_sdt,
                           hipStream_t s);

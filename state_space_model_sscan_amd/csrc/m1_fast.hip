@@ -1,5 +1,7 @@
 // m1_fast.hip -- host launch of the Mamba-1 prompt kernel (m1_fast_impl.hpp).
-#include "m1_fast_impl.hpp"
+#include <cstdlib>
+
+#include "m1_row_impl.hpp"
 
 namespace sscan {
 
@@ -9,6 +11,12 @@ extern template void launch_m1_np<float, 64>(const M1F&, int, bool, bool, dim3, 
 extern template void launch_m1_np<uint16_t, 16>(const M1F&, int, bool, bool, dim3, hipStream_t);
 extern template void launch_m1_np<uint16_t, 32>(const M1F&, int, bool, bool, dim3, hipStream_t);
 extern template void launch_m1_np<uint16_t, 64>(const M1F&, int, bool, bool, dim3, hipStream_t);
+extern template void launch_m1_row_np<float, 16>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
+extern template void launch_m1_row_np<float, 32>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
+extern template void launch_m1_row_np<float, 64>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
+extern template void launch_m1_row_np<uint16_t, 16>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
+extern template void launch_m1_row_np<uint16_t, 32>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
+extern template void launch_m1_row_np<uint16_t, 64>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
 
 hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const float* ws_h, const float* ws_sdt,
                           hipStream_t s) {
@@ -20,10 +28,33 @@ hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const flo
   k.nslices = (int)plan.nslices; k.slice_len = (int)plan.slice_len;
   k.bc_eps = a.bc_eps;
   const int K = (int)plan.lanes_per_channel;
-  const int64_t cpw = 64 / K;
-  const dim3 grid((unsigned)(((a.Dc + cpw - 1) / cpw) * plan.nslices * a.batch));
   const bool gate = a.z != nullptr, st = a.states != nullptr;
   const int np = a.N <= 16 ? 16 : a.N <= 32 ? 32 : 64;
+  if (K == 16) {  // a 16-lane row per channel, 16 channels per 256-thread block
+    const int64_t nb = ((a.Dc + 15) / 16) * plan.nslices * a.batch;
+    const dim3 grid((unsigned)nb);
+    // Blocks per CU: unused dynamic LDS caps how many the dispatcher may stack
+    // on one CU, so that the grid spreads evenly over the 256 CUs.
+    size_t dyn = 0;
+    if (const char* e = getenv("SSCAN_M1_BPC")) {
+      const int bpc = atoi(e);
+      const size_t stat = (size_t)2 * 2 * np * 68 * 4;
+      const size_t want = (160 * 1024) / (bpc + 1) + 1024;
+      if (bpc > 0 && want > stat) dyn = want - stat;
+    }
+    if (a.bf16) {
+      if (np == 16) launch_m1_row_np<uint16_t, 16>(k, gate, st, grid, dyn, s);
+      else if (np == 32) launch_m1_row_np<uint16_t, 32>(k, gate, st, grid, dyn, s);
+      else launch_m1_row_np<uint16_t, 64>(k, gate, st, grid, dyn, s);
+    } else {
+      if (np == 16) launch_m1_row_np<float, 16>(k, gate, st, grid, dyn, s);
+      else if (np == 32) launch_m1_row_np<float, 32>(k, gate, st, grid, dyn, s);
+      else launch_m1_row_np<float, 64>(k, gate, st, grid, dyn, s);
+    }
+    return hipGetLastError();
+  }
+  const int64_t cpw = 64 / K;
+  const dim3 grid((unsigned)(((a.Dc + cpw - 1) / cpw) * plan.nslices * a.batch));
   if (a.bf16) {
     if (np == 16) launch_m1_np<uint16_t, 16>(k, K, gate, st, grid, s);
     else if (np == 32) launch_m1_np<uint16_t, 32>(k, K, gate, st, grid, s);

@@ -106,6 +106,17 @@ __device__ __forceinline__ float kreduce(const float (&yp)[K], int q) {
 // Raw buffer access to one activation element (bf16 or f32).
 template <typename T> struct BufAct;
 template <> struct BufAct<uint16_t> {
+  // A loaded element in the low half of a register whose high half is left
+  // undefined (the conversion shifts it out), so no zero-extension is needed
+  // between the load and the conversion.
+  using Raw = uint32_t;
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ Raw ldr(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    s16x2 v;
+    v[0] = (short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float fr(Raw raw) { return __uint_as_float(raw << 16); }
   static __device__ __forceinline__ uint32_t ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
   }
@@ -115,6 +126,11 @@ template <> struct BufAct<uint16_t> {
   }
 };
 template <> struct BufAct<float> {
+  using Raw = uint32_t;
+  static __device__ __forceinline__ Raw ldr(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+  }
+  static __device__ __forceinline__ float fr(Raw raw) { return __uint_as_float(raw); }
   static __device__ __forceinline__ uint32_t ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
   }

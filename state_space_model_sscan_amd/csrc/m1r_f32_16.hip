@@ -1,0 +1,6 @@
+// m1r_f32_16.hip -- instantiates the row-per-channel Mamba-1 prompt kernel for f32, up to 16 states.
+#include "m1_row_impl.hpp"
+
+namespace sscan {
+template void launch_m1_row_np<float, 16>(const M1F&, bool, bool, dim3, size_t, hipStream_t);
+}  // namespace sscan

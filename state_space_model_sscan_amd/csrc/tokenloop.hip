@@ -76,25 +76,32 @@ static hipError_t zero_length(const float* h0, float* h_out, int64_t nst, hipStr
   return hipGetLastError();
 }
 
-// Mamba-1 prompt plan: K lanes per channel so that the grid puts two waves on
-// each of the 1024 SIMDs of the chip (measured on MI355X: at the Mamba-130m and
-// Falcon-Mamba-7b widths K = 4 beats K = 2 and K = 1, since a second wave per
-// SIMD hides latency that a lone wave exposes), and slices (two-pass carry) only
-// when even K = 4 leaves fewer than 512 waves on a long sequence.
-Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t es) {
-  // a batch row the buffer offsets of the fast kernel cannot span: token-loop kernel
-  if (L * Dc * es >= (int64_t(1) << 31)) {
+// Mamba-1 prompt plan. With state_dim 16, 32 or 64 and channels in groups of 4
+// the row-per-channel kernel (16 lanes per channel) runs: measured on MI355X it
+// beats four lanes per channel at the Mamba-130m width (1.5x, where four lanes
+// leave a quarter of the SIMDs empty) and at the Falcon-Mamba-7b width. Other
+// shapes take K = 1, 2 or 4 lanes per channel, the smallest K that puts two
+// waves on each of the 1024 SIMDs. Slices (two-pass carry) only when the grid
+// still has fewer than 512 waves on a long sequence.
+Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t G, int64_t es) {
+  // a batch row (of x/dt/z/y, or of B/C) that the 32-bit buffer offsets of the
+  // fast kernels cannot span: token-loop kernel
+  if (L * Dc * es >= (int64_t(1) << 31) || L * G * N * es >= (int64_t(1) << 31)) {
     Mamba1Plan t = tokenloop_plan(batch, L, Dc, N);
     t.lanes_per_channel = 0;
     return t;
   }
   Mamba1Plan p{1, L > 0 ? L : 1, 0, 1};
   auto waves = [&](int64_t K) { return batch * ((Dc * K + 63) / 64); };
+  // the row-per-channel kernel (16 lanes) takes state_dim 16, 32 or 64 and
+  // channels in whole groups of 4
+  const bool row_ok = (N == 16 || N == 32 || N == 64) && Dc % 4 == 0;
   int64_t K = N > 32 ? 2 : 1;  // 64 states in one lane would spill
   while (K < 4 && waves(K) < 2048) K *= 2;
-  if (const char* e = getenv("SSCAN_M1_LANES")) {  // tuning override: 1, 2 or 4
+  if (row_ok) K = 16;
+  if (const char* e = getenv("SSCAN_M1_LANES")) {  // tuning override: 1, 2, 4 or 16
     const int64_t v = atoi(e);
-    if ((v == 1 && N <= 32) || v == 2 || v == 4) K = v;
+    if ((v == 1 && N <= 32) || v == 2 || v == 4 || (v == 16 && row_ok)) K = v;
   }
   p.lanes_per_channel = K;
   const int64_t w = waves(K);

@@ -60,6 +60,34 @@ def test_mamba1_small(case):
         assert np.array_equal(sg[:, -1], hg), "states[:, -1] must equal state_output bit for bit"
 
 
+# The plan gives state_dim 16/32/64 (with channels in groups of 4) to the
+# row-per-channel kernel; these cases force the 1/2/4-lanes-per-channel kernel,
+# which the other shapes take, through its tuning override.
+LANE_CASES = [
+    # lanes, batch, seqlen, channels, N, act, gate, h0, states, bc_eps
+    (1, 2, 300, 256, 16, "bf16", True, True, False, 1e-6),
+    (2, 3, 129, 192, 32, "f32", True, False, True, 0.0),
+    (4, 2, 1000, 128, 16, "f32", False, True, False, 0.0),
+    (4, 1, 77, 64, 64, "bf16", True, True, True, 1e-5),
+]
+
+
+@pytest.mark.parametrize("case", LANE_CASES, ids=lambda c: "K%d_b%d_L%d_D%d_N%d_%s_g%d_h%d_s%d_e%g" % c)
+def test_mamba1_forced_lanes(case, monkeypatch):
+    K, b, L, Dc, N, act, gate, h0, states, eps = case
+    say("mamba1 forced lanes", case)
+    monkeypatch.setenv("SSCAN_M1_LANES", str(K))
+    inp = gen.make_mamba1(b, L, Dc, N, act=act, seed=L * 5 + Dc + K, gate=gate, h0=h0, bc_eps=eps,
+                          want_states=states)
+    yr, hr, sr = oracle.run_inputs(inp)
+    yg, hg, sg = run_mamba1(inp)
+    check(yg, yr, act, "y")
+    check(hg, hr, act, "state_output")
+    if states:
+        check(sg, sr, act, "states")
+        assert np.array_equal(sg[:, -1], hg)
+
+
 def test_mamba1_grouped_B_C():
     inp = gen.make_mamba1(2, 300, 256, 16, ngroups=2, act="f32", seed=11, gate=True, h0=True)
     yr, hr, _ = oracle.run_inputs(inp)
