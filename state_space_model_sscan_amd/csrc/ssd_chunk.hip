@@ -48,6 +48,11 @@
 // Transposing LDS load (verified on gfx950): within each 16-lane group, if
 // lane a supplies the address of 4 consecutive bf16 at row k0 + a/4, column
 // c0 + 4(a%4) of a row-major tile, lane i receives rows k0..k0+3 of column c0 + i.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -83,10 +88,25 @@ struct SsdK {
   const float* h0;
   uint16_t* y;
   float* h_out;
+  unsigned* queue;  // [0]: next work item; [1]: a wait gave up; [2 + ch]: segments of chain ch finished
+  float* carry;     // [chains, P, NS]: the state a segment hands to the next one
   int64_t L, H, G;
   int heads_per_group;
-  int nblocks;  // batch * H
+  int nchains;      // batch * H
+  int seg_chunks;   // chunks per segment
+  int nseg;         // segments per chain
+  int nitems;       // nseg * nchains work items, item i = segment i / nchains of chain i % nchains
 };
+
+typedef __attribute__((address_space(4))) const SsdK KArgs;
+// The kernel's arguments, read again from the argument segment: used where a
+// value is needed rarely, so that it does not hold a scalar register.
+__device__ __forceinline__ KArgs* kargs() {
+  uint64_t v = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(v));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (KArgs*)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -147,75 +167,101 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t sM[Q * LDM];
   __shared__ __attribute__((aligned(16))) float sCS[Q], sDT[Q], sW[Q], sE[Q];
+  __shared__ int sTicket[2];  // [0]: the first item; [1]: the item after the current one
 
-  // block -> (batch, head): consecutive heads of one batch row share an XCD (and its L2)
-  int lin = blockIdx.x;
-  if (k.nblocks % 8 == 0) lin = (blockIdx.x % 8) * (k.nblocks / 8) + blockIdx.x / 8;
-  const int64_t b = lin / k.H, h = lin % k.H;
-  const int64_t g = h / k.heads_per_group;
   // the wave index through readfirstlane: a scalar, so branches on it stay uniform
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, li = l & 15,
             lg = l >> 4;
-  const int64_t L = k.L, H = k.H, G = k.G;
-  const float A2 = -expf(k.A_log[h]) * kLog2e;  // decay per unit step, exp2 domain
-  const float bias = k.dt_bias[h];
-  const float Dh = k.D[h];
+  // 32-bit sizes: the host guarantees each batch row of every tensor is < 2^31 bytes
+  const int L = (int)k.L, H = (int)k.H, G = (int)k.G;
   const bool gate = k.z != nullptr;
 
-  // Global access: buffer resources based at the chunk's first token row and
-  // ending at the sequence end (the host guarantees each batch row is < 2^31 bytes).
-  const uint16_t* Bb = k.B + b * L * G * NS;
-  const uint16_t* Cb = k.C + b * L * G * NS;
-  const uint16_t* Xb = k.x + b * L * H * P;
-  const uint16_t* Zb = gate ? k.z + b * L * H * P : Xb;  // no gate: loads of x, unused
-  uint16_t* Yb = k.y + b * L * H * P;
-  const uint16_t* Db = k.dt + b * L * H;
+  // Work items come from a counter. Each workgroup takes its first item at
+  // once and the second after its first chunk is staged (by then every
+  // workgroup of the grid has taken its first, so the first round is items
+  // 0 .. grid-1); after that it takes an item when it starts the last chunk of
+  // the current one, so that it knows the next item one item ahead and can
+  // load the next item's first chunk during the current item's last chunk.
+  if (tid == 0) sTicket[0] = (int)atomicAdd(kargs()->queue, 1u);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(sTicket[0]);
+  if (cur >= kargs()->nitems) return;  // the whole workgroup
+  int nxt = -1;
+
   const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2), dt_row = (uint32_t)(H * 2);
-  auto chunk_rsrc = [&](const void* base, int64_t t0, uint32_t rowb) {
-    const int64_t left = L - t0;
-    return rsrc((const char*)base + t0 * rowb, left > 0 ? (uint64_t)left * rowb : 0);
-  };
+  // elements per batch row
+  const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * H;
   const int row = l;   // staging row of this thread
   const int pc0 = w;   // its first 8-element piece; pieces pc0 + 4*it
-  const uint32_t bc_lane = (uint32_t)(row * bc_row + (g * NS + pc0 * 8) * 2);
-  const uint32_t x_lane = (uint32_t)(row * xz_row + (h * P + pc0 * 8) * 2);
+  const uint32_t bc_lane = (uint32_t)(row * bc_row + pc0 * 16);
+  const uint32_t x_lane = (uint32_t)(row * xz_row + pc0 * 16);
   // epilogue layout: row 16*it + li, columns 16w + 4lg .. +3
-  const uint32_t e_lane = (uint32_t)(li * xz_row + (h * P + 16 * w + 4 * lg) * 2);
-  const uint32_t dt_lane = (uint32_t)(l * dt_row + h * 2);
+  const uint32_t e_lane = (uint32_t)(li * xz_row + (16 * w + 4 * lg) * 2);
+  const uint32_t dt_lane = (uint32_t)(l * dt_row);
 
-  // The loads of chunk c, in four parts that the loop spreads over the phases of
-  // the chunk before it, so that the address units never take them in one burst.
-  auto load_b = [&](Prefetch& pf, int64_t c) {
-    const __amdgpu_buffer_rsrc_t rB = chunk_rsrc(Bb, c * Q, bc_row);
+  // Global access goes through buffer resources based at a chunk's first token
+  // row and this chain's first column, ending at the sequence end (the host
+  // guarantees each batch row is < 2^31 bytes): rows past the end read zeros
+  // and drop their stores in hardware, and the lane offsets stay uniform.
+  // Target of the loads in flight: chain (tb, th, tg), first token tt (tt >= L:
+  // none; every load reads zeros).
+  int tb = 0, th = 0, tg = 0, tt = 0;
+  auto tgt_rsrc = [&](const uint16_t* base, uint32_t bat, uint32_t col, uint32_t rowb) {
+    const int left = L - tt;
+    return rsrc((const char*)(base + (uint64_t)tb * bat + col) + (uint32_t)tt * rowb,
+                left > 0 ? (uint32_t)left * rowb - col * 2 : 0u);
+  };
+  auto load_b = [&](Prefetch& pf) {
+    const __amdgpu_buffer_rsrc_t rB = tgt_rsrc(k.B, bc_bat, (uint32_t)tg * NS, bc_row);
 #pragma unroll
     for (int it = 0; it < 4; ++it)
       pf.b[it] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(bc_lane + it * 64), 0, 0);
   };
-  auto load_c = [&](Prefetch& pf, int64_t c) {
-    const __amdgpu_buffer_rsrc_t rC = chunk_rsrc(Cb, c * Q, bc_row);
+  auto load_c = [&](Prefetch& pf) {
+    const __amdgpu_buffer_rsrc_t rC = tgt_rsrc(k.C, bc_bat, (uint32_t)tg * NS, bc_row);
 #pragma unroll
     for (int it = 0; it < 4; ++it)
       pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bc_lane + it * 64), 0, 0);
   };
-  auto load_x = [&](Prefetch& pf, int64_t c) {
-    const __amdgpu_buffer_rsrc_t rX = chunk_rsrc(Xb, c * Q, xz_row), rD = chunk_rsrc(Db, c * Q, dt_row);
+  auto load_x = [&](Prefetch& pf) {
+    const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
+    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
       pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(x_lane + it * 64), 0, 0);
     pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rD, (int)dt_lane, 0, 0);
   };
-  // z of chunk c in the epilogue's layout (4 bf16 of row 16*it + li)
+  // z of the target chunk in the epilogue's layout (4 bf16 of row 16*it + li);
+  // without a gate these are loads of x, unused
   u32x2 zkeep[4];
-  auto load_z = [&](u32x2 (&zz)[4], int64_t c) {
-    const __amdgpu_buffer_rsrc_t rZ = chunk_rsrc(Zb, c * Q, xz_row);
+  auto load_z = [&](u32x2 (&zz)[4]) {
+    const __amdgpu_buffer_rsrc_t rZ = tgt_rsrc(gate ? k.z : k.x, xz_bat, (uint32_t)th * P, xz_row);
 #pragma unroll
     for (int it = 0; it < 4; ++it)
       zz[it] = __builtin_amdgcn_raw_buffer_load_b64(rZ, (int)(e_lane + it * 16 * xz_row), 0, 0);
   };
 
-  // Chunk c from the prefetch registers into LDS; wave 0 adds the steps, their
-  // inclusive cumulative sum (exp2 domain) and the derived decays.
-  auto stage = [&](Prefetch& pf, int64_t c) {
+  // The current item: chain (b, h) of group g, chunks [c, c_end); per-head constants.
+  int b = 0, h = 0, g = 0, c = 0, c_end = 0;
+  int seg = 0;
+  float A2 = 0.f, bias = 0.f, Dh = 0.f;
+  auto set_item = [&](int it) {
+    const KArgs* kk = kargs();
+    seg = it / kk->nchains;
+    const int ch = it % kk->nchains;
+    b = ch / H;
+    h = ch % H;
+    g = h / kk->heads_per_group;
+    c = seg * kk->seg_chunks;
+    c_end = min(c + kk->seg_chunks, max((L + Q - 1) / Q, 1));  // seqlen 0: one empty chunk
+    A2 = -expf(kk->A_log[h]) * kLog2e;  // decay per unit step, exp2 domain
+    bias = kk->dt_bias[h];
+    Dh = kk->D[h];
+  };
+
+  // Chunk at token tt from the prefetch registers into LDS; wave 0 adds the
+  // steps, their inclusive cumulative sum (exp2 domain) and the derived decays.
+  auto stage = [&](Prefetch& pf) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int pc = pc0 + 4 * it;
@@ -225,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) *(u32x4*)(sX + row * LDX + (pc0 + 4 * it) * 8) = pf.x[it];
     if (w == 0) {
-      const int nt_valid = (int)min((int64_t)Q, L - c * Q);
+      const int nt_valid = max(0, min(Q, L - tt));
       const float dtv = l < nt_valid ? softplus(lo_f(pf.dt) + bias) : 0.0f;  // past the end: a zero step
       const float cs = wave_inclusive_sum(dtv * A2);
       const float cs_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
@@ -236,32 +282,111 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     }
   };
 
-  // state slice: hacc[nt][r] = S[p = 16w + li][n = 16nt + 4lg + r]
+  // state slice: hacc[nt][r] = S[p = 16w + li][n = 16nt + 4lg + r]; stored as [chain, p, n]
   f32x4 hacc[8];
-  if (k.h0) {
+  const int64_t s_lane = (int64_t)(16 * w + li) * NS + 4 * lg;
+  // The entering state of the current item: the caller's (or zeros) for a first
+  // segment, else the one the previous segment left in carry, once its flag says
+  // so. The producer of that segment holds an item dequeued earlier than this
+  // one, so it is running and never waits on this workgroup: the wait ends. Its
+  // bound (2^20 polls, about a second) only guarantees that the kernel
+  // terminates; a wait that gives up raises queue[1], which ends every other.
+  // carry and the flags move through device-scope atomic loads and stores,
+  // which are coherent across the compute dies without a cache write-back or
+  // invalidation (either would flush the L2 that the other workgroups share).
+  auto state_in = [&]() {
+    const int64_t ch = (int64_t)b * H + h;
+    if (seg > 0) {
+      if (tid == 0) {
+        unsigned* flag = kargs()->queue + 2 + ch;
+        bool done = false;
+        for (int n = 0; n < (1 << 20) && !done; ++n) {
+          done = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg ||
+                 __hip_atomic_load(kargs()->queue + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+          if (!done) __builtin_amdgcn_s_sleep(2);
+        }
+        if (!done) __hip_atomic_store(kargs()->queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      float* src = kargs()->carry + ch * (P * NS) + s_lane;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      hacc[nt] = *(const f32x4*)(k.h0 + ((b * H + h) * P + 16 * w + li) * NS + 16 * nt + 4 * lg);
-  } else {
+      for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+        for (int r = 0; r < 4; ++r)
+          hacc[nt][r] = __hip_atomic_load(src + 16 * nt + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (kargs()->h0) {
+      const float* src = kargs()->h0 + ch * (P * NS) + s_lane;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // The loads complete here: otherwise every chunk would wait for them (and
+    // for the chunk loads queued behind them) before it first reads the state.
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
+  };
+  // The leaving state: to the caller after the last segment, else to carry and
+  // then the flag. Every thread waits until its stores are complete (visible to
+  // the device) before the barrier; thread 0 raises the flag after it.
+  auto state_out = [&]() {
+    const int64_t ch = (int64_t)b * H + h;
+    if (seg + 1 < kargs()->nseg) {
+      float* dst = kargs()->carry + ch * (P * NS) + s_lane;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(dst + 16 * nt + r, hacc[nt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(kargs()->queue + 2 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      float* dst = kargs()->h_out + ch * (P * NS) + s_lane;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
+    }
+  };
+
   // the tiles of M above the diagonal block row stay zero
   for (int e = tid; e < Q * LDM; e += 256) sM[e] = 0;
 
-  const int64_t nchunks = (L + Q - 1) / Q;
+  set_item(cur);
+  tb = b; th = h; tg = g; tt = c * Q;
   Prefetch pf;
-  load_b(pf, 0);
-  load_c(pf, 0);
-  load_x(pf, 0);
-  load_z(zkeep, 0);
-  stage(pf, 0);
+  load_b(pf);
+  load_c(pf);
+  load_x(pf);
+  load_z(zkeep);
+  stage(pf);
+  state_in();
+  if (tid == 0) sTicket[1] = (int)atomicAdd(kargs()->queue, 1u);
   __syncthreads();
+  {
+    const int t = __builtin_amdgcn_readfirstlane(sTicket[1]);
+    nxt = t < kargs()->nitems ? t : -1;
+  }
 
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int64_t t0 = c * Q;
-    // ---- after barrier A: chunk c is in LDS; the next chunk's B is requested
-    load_b(pf, c + 1);
+  for (;;) {
+    const int t0 = c * Q;
+    const bool last = c + 1 == c_end;
+    // ---- after barrier A: chunk c is in LDS. Loads now go to the next chunk of
+    // this item, or to the first chunk of the next item.
+    int ticket = 0;
+    if (!last) {
+      tt = t0 + Q;
+    } else if (nxt >= 0) {
+      const int ns = nxt / kargs()->nchains, nch = nxt % kargs()->nchains;
+      tb = nch / H;
+      th = nch % H;
+      tg = th / kargs()->heads_per_group;
+      tt = ns * kargs()->seg_chunks * Q;
+      if (tid == 0) ticket = (int)atomicAdd(kargs()->queue, 1u);  // the item after that
+    } else {
+      tt = L;
+    }
+    load_b(pf);
 
     // x^T fragments (A operand of Y^T += X^T M^T; k = j = 32kb + 8lg + e) by two
     // transposing loads each, and the epilogue's x values (8 bytes of row 16it + li)
@@ -319,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       }
     }
 
-    load_c(pf, c + 1);
+    load_c(pf);
     // ---- Y^T = S_in C^T, columns scaled by exp(cs_i). A operand: the state,
     // k = n in {32kb + 4lg + r} U {32kb + 16 + 4lg + r} (the accumulator layout);
     // B operand: C[i][n] for the same n, two 8-byte pieces of row i.
@@ -348,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       for (int r = 0; r < 4; ++r) yacc[it][r] *= ei;
     }
 
-    load_x(pf, c + 1);
+    load_x(pf);
     // ---- S = exp(cs_last) S + B^T (w x). A operand: B^T rows n = 16nt + li, k = j
     // (transposing loads of B); B operand: w_j x[j][16w + li] from the x^T fragments.
     bf16x8 wxb[2];
@@ -390,7 +515,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     }
     // ---- epilogue: lane holds y[i = 16it + li][16w + 4lg + r]; y = (Y + D x) silu(z)
     {
-      const __amdgpu_buffer_rsrc_t rY = chunk_rsrc(Yb, t0, xz_row);
+      const __amdgpu_buffer_rsrc_t rY = rsrc((const char*)(k.y + (uint64_t)b * xz_bat + h * P) + (uint32_t)t0 * xz_row,
+                                             (uint32_t)(L - t0) * xz_row - h * P * 2);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const float xs[4] = {lo_f(xe[it][0]), hi_f(xe[it][0]), lo_f(xe[it][1]), hi_f(xe[it][1])};
@@ -402,39 +528,124 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
         __builtin_amdgcn_raw_buffer_store_b64(out, rY, (int)(e_lane + it * 16 * xz_row), 0, 0);
       }
     }
+    const bool finished = last && nxt < 0;
+    if (last) {
+      // ---- the item is done: hand its state on and switch to the next item
+      state_out();
+      if (!finished) {
+        if (tid == 0) sTicket[1] = ticket;
+        set_item(nxt);
+        state_in();
+        __syncthreads();  // sTicket[1]
+        const int t = __builtin_amdgcn_readfirstlane(sTicket[1]);
+        nxt = t < kargs()->nitems ? t : -1;
+      }
+    } else {
+      ++c;
+    }
     // ---- the next chunk's z into the registers the epilogue freed; the next chunk
-    // into LDS (past the end: zeros, harmless)
-    load_z(zkeep, c + 1);
-    stage(pf, c + 1);
-    __syncthreads();  // ---- barrier A of chunk c + 1
-  }
-
-  // final state, [b, h, p, n]
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    float* hp = k.h_out + ((b * H + h) * P + 16 * w + li) * NS + 16 * nt + 4 * lg;
-    *(f32x4*)hp = hacc[nt];
+    // into LDS (past the end, or after the last item: zeros, harmless). The loop
+    // leaves only here, so every path back to its head passes the waits of the
+    // staging: otherwise the next chunk would wait for this chunk's stores.
+    load_z(zkeep);
+    stage(pf);
+    __syncthreads();  // ---- barrier A of the next chunk
+    if (finished) break;
   }
 }
+
+// Zeroes the work counter, the give-up word and the per-chain flags (a kernel, not a memset, so
+// that the call can be captured in a graph).
+__global__ void ssd_queue_reset(unsigned* q, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) q[i] = 0;
+}
+
+namespace {
+
+// How the chains are cut into segments and how many workgroups take them. A
+// chain (one head of one batch row) is sequential; with fewer chains than
+// compute units some units idle whatever is done, and with a few more (say 1.25
+// per unit) whole chains leave some units with two and the rest idle half the
+// time. Cutting every chain into segments that any workgroup may take evens
+// the load: the cost model counts rounds of items over one workgroup per unit,
+// plus one chunk of overhead per item.
+struct SsdPlan {
+  int nchains, seg_chunks, nseg, nitems, grid;
+  size_t queue_bytes, ws_bytes;
+};
+
+SsdPlan ssd_plan(const SSDArgs& a) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    ncu = 256;
+  SsdPlan p{};
+  const int64_t nchains = a.batch * a.H, nchunks = std::max<int64_t>((a.L + Q - 1) / Q, 1);
+  p.nchains = (int)nchains;
+  int64_t best_seg = nchunks, best_ns = 1;
+  if (nchains < 2 * (int64_t)ncu) {
+    auto cost = [&](int64_t sc, int64_t ns) {
+      const int64_t rounds = (ns * nchains + ncu - 1) / ncu;
+      return std::max(rounds * (sc + 1), nchunks + ns);
+    };
+    int64_t best = cost(nchunks, 1);
+    for (int64_t s = 2; s <= std::min<int64_t>(nchunks, 64) && s * nchains < (int64_t(1) << 30); ++s) {
+      const int64_t sc = (nchunks + s - 1) / s, ns = (nchunks + sc - 1) / sc;
+      const int64_t cst = cost(sc, ns);
+      if (cst * 100 < best * 97) {  // a cut must win by 3% to be taken
+        best = cst;
+        best_seg = sc;
+        best_ns = ns;
+      }
+    }
+  }
+  int64_t grid = nchains < 2 * (int64_t)ncu ? ncu : 2 * ncu;  // two per unit (the occupancy the
+                                                               // kernel is built for) with many chains
+  // tuning override "chunks per segment[,workgroups]"
+  if (const char* e = getenv("SSCAN_SSD_SEGMENT")) {
+    const int64_t sc = atoll(e);
+    const char* comma = strchr(e, ',');
+    if (sc > 0) {
+      best_seg = std::min(sc, nchunks);
+      best_ns = (nchunks + best_seg - 1) / best_seg;
+      if (best_ns * nchains >= (int64_t(1) << 30)) best_seg = nchunks, best_ns = 1;
+    }
+    if (comma && atoll(comma + 1) > 0) grid = std::min<int64_t>(atoll(comma + 1), 1 << 20);
+  }
+  p.seg_chunks = (int)best_seg;
+  p.nseg = (int)best_ns;
+  p.nitems = p.nseg * p.nchains;
+  p.grid = (int)std::min<int64_t>(p.nitems, grid);
+  p.queue_bytes = ((size_t)(2 + p.nchains) * 4 + 255) / 256 * 256;
+  p.ws_bytes = p.queue_bytes + (p.nseg > 1 ? (size_t)p.nchains * P * NS * 4 : 0);
+  return p;
+}
+
+}  // namespace
 
 bool ssd_chunk_supported(const SSDArgs& a) {
   // buffer offsets are 32-bit: each batch row of x / z / y / B / C must stay below 2^31 bytes
   const int64_t row_x = a.L * a.H * P * 2, row_bc = a.L * a.G * NS * 2;
-  return a.bf16 && a.P == P && a.N == NS && a.states == nullptr && a.batch * a.H <= 0x7fffffff &&
+  return a.bf16 && a.P == P && a.N == NS && a.states == nullptr && a.batch * a.H <= (1 << 24) &&
          row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
 }
 
-size_t ssd_chunk_ws(const SSDArgs&) { return 0; }
+size_t ssd_chunk_ws(const SSDArgs& a) { return a.batch == 0 ? 0 : ssd_plan(a).ws_bytes; }
 
-hipError_t launch_ssd_chunk(const SSDArgs& a, void*, hipStream_t s) {
+hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
+  const SsdPlan p = ssd_plan(a);
   SsdK k{};
   k.x = (const uint16_t*)a.x; k.dt = (const uint16_t*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const uint16_t*)a.B; k.C = (const uint16_t*)a.C; k.D = a.D; k.z = (const uint16_t*)a.z;
   k.h0 = a.h0; k.y = (uint16_t*)a.y; k.h_out = a.h_out;
+  k.queue = (unsigned*)ws;
+  k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
   k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
-  k.nblocks = (int)(a.batch * a.H);
-  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)k.nblocks), dim3(256), 0, s, k);
+  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nitems = p.nitems;
+  const int nq = 2 + p.nchains;
+  hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nq + 255) / 256)), dim3(256), 0, s, k.queue, nq);
+  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)p.grid), dim3(256), 0, s, k);
   return hipGetLastError();
 }
 

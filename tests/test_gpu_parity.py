@@ -190,6 +190,35 @@ def test_ssd_small(case):
         assert np.array_equal(sg[:, -1], hg)
 
 
+# The chunk kernel cuts each chain (one head of one batch row) into segments of
+# whole chunks that any workgroup may take, handing the state over between
+# them. Forced cuts: one-chunk segments on a grid far smaller than the items,
+# so that items wait on their predecessors and workgroups run several chains.
+SEGMENT_CASES = [
+    # chunks per segment, workgroups, batch, seqlen, H, G, gate, h0
+    (1, 3, 2, 300, 3, 1, True, True),
+    (2, 5, 1, 1000, 4, 2, True, False),
+    (1, 1, 1, 200, 2, 1, False, True),
+    (3, 64, 3, 700, 4, 1, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SEGMENT_CASES, ids=lambda c: "seg%d_wg%d_b%d_L%d_H%d_G%d_g%d_h%d" % c)
+def test_ssd_forced_segments(case, monkeypatch):
+    sc, wg, b, L, H, G, gate, h0 = case
+    say("ssd forced segments", case)
+    monkeypatch.setenv("SSCAN_SSD_SEGMENT", "%d,%d" % (sc, wg))
+    inp = gen.make_ssd(b, L, H, 64, 128, G, act="bf16", seed=L + 7 * sc + wg, gate=gate, h0=h0)
+    yr, hr, _ = oracle.run_inputs(inp)
+    yg, hg, _ = run_ssd(inp)
+    check(yg, yr, "bf16", "y")
+    check(hg, hr, "bf16", "state_output")
+    # the cut changes who computes a chunk, not what: the result is bit-identical
+    monkeypatch.delenv("SSCAN_SSD_SEGMENT")
+    yw, hw, _ = run_ssd(inp)
+    assert np.array_equal(yg, yw) and np.array_equal(hg, hw)
+
+
 def test_ssd_step_chain_equals_oracle():
     inp = gen.make_ssd(2, 12, 3, 64, 128, act="f32", seed=5, gate=True, h0=True)
     yr, hr, _ = oracle.run_inputs(inp)
