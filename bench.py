@@ -245,20 +245,23 @@ def bench_step(torch, bd, gen, calls=512):
                 graph_gbs=None if not graph_us else per_call_bytes / (graph_us * 1e-6) / 1e9)
 
 
-def cpu_baseline(inp, repeats=2):
+def cpu_baseline(inp, min_seconds=10.0, max_runs=200):
+    """The fp64 oracle on the same workload, run whole and repeated until at least
+    `min_seconds` of CPU work have been timed; reports the mean rate over the runs."""
     import oracle
 
     oracle.build(force=False)
-    best = None
-    for _ in range(repeats):
+    runs, total = 0, 0.0
+    while runs < 2 or (total < min_seconds and runs < max_runs):
         t0 = time.perf_counter()
         oracle.run_inputs(inp, want_states=False)
-        dt = time.perf_counter() - t0
-        best = dt if best is None else min(best, dt)
-    toks = inp.batch * inp.seqlen
-    return dict(value=toks / best, unit="tokens/s", cores=oracle.threads(), kind="oracle",
-                sample="the whole workload (%d x %d tokens x %d channels x %d states), fp64, best of %d runs, "
-                       "%.2f s each" % (inp.batch, inp.seqlen, inp.channels, inp.state_dim, repeats, best))
+        total += time.perf_counter() - t0
+        runs += 1
+    toks = inp.batch * inp.seqlen * runs
+    return dict(value=toks / total, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample="the whole workload (%d x %d tokens x %d channels x %d states), fp64, run %d times "
+                       "back to back, %.1f s in all" % (inp.batch, inp.seqlen, inp.channels, inp.state_dim, runs,
+                                                        total))
 
 
 def copy_calibration(torch, gib=1, reps=3):

@@ -88,14 +88,16 @@ struct SsdK {
   const float* h0;
   uint16_t* y;
   float* h_out;
-  unsigned* queue;  // [0]: next work item; [1]: a wait gave up; [2 + ch]: segments of chain ch finished
+  unsigned* queue;  // [16 q]: next item of queue q; [128]: a wait gave up; [256 + ch]: segments of chain ch done
   float* carry;     // [chains, P, NS]: the state a segment hands to the next one
   int64_t L, H, G;
   int heads_per_group;
   int nchains;      // batch * H
   int seg_chunks;   // chunks per segment
   int nseg;         // segments per chain
-  int nitems;       // nseg * nchains work items, item i = segment i / nchains of chain i % nchains
+  int nq;           // work queues; workgroup i serves queue i % nq, which holds chains
+                    // [q nchains / nq, (q + 1) nchains / nq): item i of a queue with n chains is
+                    // segment i / n of its chain i % n
 };
 
 typedef __attribute__((address_space(4))) const SsdK KArgs;
@@ -131,6 +133,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Cache policy of a buffer access that is coherent across the compute dies
+// (sc1 on gfx950: written through to memory, read from the coherent level).
+constexpr int kDeviceCoherent = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
@@ -176,16 +182,34 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   const int L = (int)k.L, H = (int)k.H, G = (int)k.G;
   const bool gate = k.z != nullptr;
 
+  // This workgroup's queue (the dispatcher deals workgroups to the eight compute
+  // dies in turn, so the queues match the dies and a die's L2 serves neighbouring
+  // heads, which share B and C): its counter, first chain, chains and items.
+  // Computed where needed from the argument segment, so that none holds a
+  // scalar register through the chunk loop.
+  // (32-bit: chains < 2^24 and queues <= 8; readfirstlane marks the quotients
+  // uniform, so buffer resources built from them stay scalar)
+  auto qindex = [&]() { return __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)kargs()->nq)); };
+  auto qcounter = [&]() { return kargs()->queue + 16 * qindex(); };
+  auto qfirst = [&]() {
+    return __builtin_amdgcn_readfirstlane((int)((unsigned)(qindex() * kargs()->nchains) / (unsigned)kargs()->nq));
+  };
+  auto qchains = [&]() {
+    const unsigned q = (unsigned)qindex(), n = (unsigned)kargs()->nchains, nq = (unsigned)kargs()->nq;
+    return __builtin_amdgcn_readfirstlane((int)((q + 1) * n / nq - q * n / nq));
+  };
+  auto qitems = [&]() { return kargs()->nseg * qchains(); };
+
   // Work items come from a counter. Each workgroup takes its first item at
   // once and the second after its first chunk is staged (by then every
   // workgroup of the grid has taken its first, so the first round is items
   // 0 .. grid-1); after that it takes an item when it starts the last chunk of
   // the current one, so that it knows the next item one item ahead and can
   // load the next item's first chunk during the current item's last chunk.
-  if (tid == 0) sTicket[0] = (int)atomicAdd(kargs()->queue, 1u);
+  if (tid == 0) sTicket[0] = (int)atomicAdd(qcounter(), 1u);
   __syncthreads();
   int cur = __builtin_amdgcn_readfirstlane(sTicket[0]);
-  if (cur >= kargs()->nitems) return;  // the whole workgroup
+  if (cur >= qitems()) return;  // the whole workgroup
   int nxt = -1;
 
   const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2), dt_row = (uint32_t)(H * 2);
@@ -247,8 +271,9 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   float A2 = 0.f, bias = 0.f, Dh = 0.f;
   auto set_item = [&](int it) {
     const KArgs* kk = kargs();
-    seg = it / kk->nchains;
-    const int ch = it % kk->nchains;
+    const int nch = qchains();
+    seg = it / nch;
+    const int ch = qfirst() + it % nch;
     b = ch / H;
     h = ch % H;
     g = h / kk->heads_per_group;
@@ -290,30 +315,31 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   // so. The producer of that segment holds an item dequeued earlier than this
   // one, so it is running and never waits on this workgroup: the wait ends. Its
   // bound (2^20 polls, about a second) only guarantees that the kernel
-  // terminates; a wait that gives up raises queue[1], which ends every other.
-  // carry and the flags move through device-scope atomic loads and stores,
-  // which are coherent across the compute dies without a cache write-back or
-  // invalidation (either would flush the L2 that the other workgroups share).
+  // terminates; a wait that gives up raises queue[128], which ends every other.
+  // carry and the flags move through device-coherent loads and stores (the sc1
+  // cache policy, as device-scope atomics use), which need no cache write-back
+  // or invalidation (either would flush the L2 that the other workgroups share);
+  // carry moves in 16-byte pieces, so the write-through goes out in whole
+  // 64-byte segments.
   auto state_in = [&]() {
     const int64_t ch = (int64_t)b * H + h;
     if (seg > 0) {
       if (tid == 0) {
-        unsigned* flag = kargs()->queue + 2 + ch;
+        unsigned* flag = kargs()->queue + 256 + ch;
         bool done = false;
         for (int n = 0; n < (1 << 20) && !done; ++n) {
           done = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg ||
-                 __hip_atomic_load(kargs()->queue + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+                 __hip_atomic_load(kargs()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
           if (!done) __builtin_amdgcn_s_sleep(2);
         }
-        if (!done) __hip_atomic_store(kargs()->queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!done) __hip_atomic_store(kargs()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
-      float* src = kargs()->carry + ch * (P * NS) + s_lane;
+      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + ch * (P * NS), P * NS * 4);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          hacc[nt][r] = __hip_atomic_load(src + 16 * nt + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hacc[nt] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
     } else if (kargs()->h0) {
       const float* src = kargs()->h0 + ch * (P * NS) + s_lane;
 #pragma unroll
@@ -333,15 +359,14 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   auto state_out = [&]() {
     const int64_t ch = (int64_t)b * H + h;
     if (seg + 1 < kargs()->nseg) {
-      float* dst = kargs()->carry + ch * (P * NS) + s_lane;
+      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + ch * (P * NS), P * NS * 4);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __hip_atomic_store(dst + 16 * nt + r, hacc[nt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hacc[nt]), rS, (int)((s_lane + 16 * nt) * 4), 0,
+                                               kDeviceCoherent);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(kargs()->queue + 2 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(kargs()->queue + 256 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       float* dst = kargs()->h_out + ch * (P * NS) + s_lane;
 #pragma unroll
@@ -361,11 +386,11 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   load_z(zkeep);
   stage(pf);
   state_in();
-  if (tid == 0) sTicket[1] = (int)atomicAdd(kargs()->queue, 1u);
+  if (tid == 0) sTicket[1] = (int)atomicAdd(qcounter(), 1u);
   __syncthreads();
   {
     const int t = __builtin_amdgcn_readfirstlane(sTicket[1]);
-    nxt = t < kargs()->nitems ? t : -1;
+    nxt = t < qitems() ? t : -1;
   }
 
   for (;;) {
@@ -377,12 +402,12 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     if (!last) {
       tt = t0 + Q;
     } else if (nxt >= 0) {
-      const int ns = nxt / kargs()->nchains, nch = nxt % kargs()->nchains;
+      const int qn = qchains(), ns = nxt / qn, nch = qfirst() + nxt % qn;
       tb = nch / H;
       th = nch % H;
       tg = th / kargs()->heads_per_group;
       tt = ns * kargs()->seg_chunks * Q;
-      if (tid == 0) ticket = (int)atomicAdd(kargs()->queue, 1u);  // the item after that
+      if (tid == 0) ticket = (int)atomicAdd(qcounter(), 1u);  // the item after that
     } else {
       tt = L;
     }
@@ -538,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
         state_in();
         __syncthreads();  // sTicket[1]
         const int t = __builtin_amdgcn_readfirstlane(sTicket[1]);
-        nxt = t < kargs()->nitems ? t : -1;
+        nxt = t < qitems() ? t : -1;
       }
     } else {
       ++c;
@@ -554,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   }
 }
 
-// Zeroes the work counter, the give-up word and the per-chain flags (a kernel, not a memset, so
+// Zeroes the queue counters, the give-up word and the per-chain flags (a kernel, not a memset, so
 // that the call can be captured in a graph).
 __global__ void ssd_queue_reset(unsigned* q, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) q[i] = 0;
@@ -570,7 +595,7 @@ namespace {
 // the load: the cost model counts rounds of items over one workgroup per unit,
 // plus one chunk of overhead per item.
 struct SsdPlan {
-  int nchains, seg_chunks, nseg, nitems, grid;
+  int nchains, seg_chunks, nseg, nq, grid;
   size_t queue_bytes, ws_bytes;
 };
 
@@ -582,10 +607,15 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   SsdPlan p{};
   const int64_t nchains = a.batch * a.H, nchunks = std::max<int64_t>((a.L + Q - 1) / Q, 1);
   p.nchains = (int)nchains;
+  int64_t grid = nchains < 2 * (int64_t)ncu ? ncu : 2 * ncu;  // two per unit (the occupancy the
+                                                               // kernel is built for) with many chains
   int64_t best_seg = nchunks, best_ns = 1;
+  auto queues = [&](int64_t g) { return std::max<int64_t>(1, std::min<int64_t>({8, nchains, g})); };
   if (nchains < 2 * (int64_t)ncu) {
+    // rounds of items in the fullest queue over its workgroups
+    const int64_t nq = queues(grid), qch = (nchains + nq - 1) / nq, qwg = std::max<int64_t>(grid / nq, 1);
     auto cost = [&](int64_t sc, int64_t ns) {
-      const int64_t rounds = (ns * nchains + ncu - 1) / ncu;
+      const int64_t rounds = (ns * qch + qwg - 1) / qwg;
       return std::max(rounds * (sc + 1), nchunks + ns);
     };
     int64_t best = cost(nchunks, 1);
@@ -599,8 +629,6 @@ SsdPlan ssd_plan(const SSDArgs& a) {
       }
     }
   }
-  int64_t grid = nchains < 2 * (int64_t)ncu ? ncu : 2 * ncu;  // two per unit (the occupancy the
-                                                               // kernel is built for) with many chains
   // tuning override "chunks per segment[,workgroups]"
   if (const char* e = getenv("SSCAN_SSD_SEGMENT")) {
     const int64_t sc = atoll(e);
@@ -614,9 +642,11 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   }
   p.seg_chunks = (int)best_seg;
   p.nseg = (int)best_ns;
-  p.nitems = p.nseg * p.nchains;
-  p.grid = (int)std::min<int64_t>(p.nitems, grid);
-  p.queue_bytes = ((size_t)(2 + p.nchains) * 4 + 255) / 256 * 256;
+  p.nq = (int)queues(grid);
+  // no more workgroups than the fullest queue has items, per queue
+  const int64_t qitems = best_ns * ((nchains + p.nq - 1) / p.nq);
+  p.grid = (int)std::min<int64_t>(grid, (int64_t)p.nq * qitems);
+  p.queue_bytes = ((size_t)(256 + p.nchains) * 4 + 255) / 256 * 256;
   p.ws_bytes = p.queue_bytes + (p.nseg > 1 ? (size_t)p.nchains * P * NS * 4 : 0);
   return p;
 }
@@ -642,9 +672,10 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   k.queue = (unsigned*)ws;
   k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
   k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
-  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nitems = p.nitems;
-  const int nq = 2 + p.nchains;
-  hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nq + 255) / 256)), dim3(256), 0, s, k.queue, nq);
+  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
+  const int nwords = 256 + p.nchains;
+  hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nwords + 255) / 256)), dim3(256), 0, s, k.queue,
+                     nwords);
   hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)p.grid), dim3(256), 0, s, k);
   return hipGetLastError();
 }
