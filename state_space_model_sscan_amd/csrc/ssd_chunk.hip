@@ -45,9 +45,15 @@
 // B[32 x 16]: lane l holds column l%16, the same k; D[16 x 16]: lane l holds rows
 // 4g + r (r = 0..3), column l%16. Any assignment of k to (lane group, element)
 // works as long as A and B use the same one.
-// Transposing LDS load (verified on gfx950): within each 16-lane group, if
-// lane a supplies the address of 4 consecutive bf16 at row k0 + a/4, column
-// c0 + 4(a%4) of a row-major tile, lane i receives rows k0..k0+3 of column c0 + i.
+// Transposing LDS load (verified on gfx950): within each 16-lane group, lanes
+// 4q..4q+3 supply the addresses of 4 consecutive bf16 each (columns c0 + 4(a%4))
+// of tile row q, and lane i receives tile rows 0..3 of column c0 + i. The LDS
+// serves these loads 32 lanes at a time, so the two 16-lane groups of a half
+// wave must hit disjoint banks: with the row pitches here that holds when tile
+// row q is LDS row k0 + 2q (k0 + 2q + 1 for the second load), and not for
+// consecutive rows. So within each 8 tokens k0..k0+7 the MFMA k order is
+// 0, 2, 4, 6, 1, 3, 5, 7 (kperm); the other operands follow it: w is stored in
+// that order and the masked M with its columns permuted the same way.
 #include <stdlib.h>
 #include <string.h>
 
@@ -99,6 +105,10 @@ struct SsdK {
                     // [q nchains / nq, (q + 1) nchains / nq): item i of a queue with n chains is
                     // segment i / n of its chain i % n
 };
+
+// Position of token t of a chunk in k order (see the note on the transposing load):
+// within each group of 8, token 8g + t sits at 8g + (t even ? t/2 : 4 + t/2).
+__device__ __forceinline__ int kslot(int t) { return (t & ~7) | ((t & 1) << 2) | ((t & 7) >> 1); }
 
 typedef __attribute__((address_space(4))) const SsdK KArgs;
 // The kernel's arguments, read again from the argument segment: used where a
@@ -158,10 +168,12 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 }
 
 // One chunk's staged global loads of one thread, in flight during the previous
-// chunk. B, C: 4 pieces of 8 bf16 (row tid & 63, pieces (tid >> 6) + 4*it); x: 2
-// pieces; dt: token tid & 63.
+// chunk. Coalesced: 16 lanes cover a 256-byte row of B or C (an instruction, 4
+// rows), 8 lanes a 128-byte row of x (8 rows), so each load touches a few cache
+// lines rather than one per lane. B, C: rows 16w + 4it + l/16, piece l%16; x and
+// z: rows 16w + 8it + l/8, piece l%8; dt (wave 0 only): token l.
 struct Prefetch {
-  u32x4 b[4], c[4], x[2];
+  u32x4 b[4], c[4], x[2], z[2];
   uint32_t dt;  // raw bf16 bits
 };
 
@@ -172,6 +184,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   __shared__ __attribute__((aligned(16))) uint16_t sC[Q * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t sM[Q * LDM];
+  __shared__ __attribute__((aligned(16))) uint16_t sZ[Q * LDX];  // z of the chunk
+  __shared__ __attribute__((aligned(16))) uint16_t sY[Q * LDX];  // y of the chunk, stored after the next barrier
   __shared__ __attribute__((aligned(16))) float sCS[Q], sDT[Q], sW[Q], sE[Q];
   __shared__ int sTicket[2];  // [0]: the first item; [1]: the item after the current one
 
@@ -215,12 +229,10 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2), dt_row = (uint32_t)(H * 2);
   // elements per batch row
   const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * H;
-  const int row = l;   // staging row of this thread
-  const int pc0 = w;   // its first 8-element piece; pieces pc0 + 4*it
-  const uint32_t bc_lane = (uint32_t)(row * bc_row + pc0 * 16);
-  const uint32_t x_lane = (uint32_t)(row * xz_row + pc0 * 16);
-  // epilogue layout: row 16*it + li, columns 16w + 4lg .. +3
-  const uint32_t e_lane = (uint32_t)(li * xz_row + (16 * w + 4 * lg) * 2);
+  const int bc_r = 16 * w + (l >> 4), bc_p = l & 15;  // staging row (+ 4 it) and piece of B, C
+  const int x_r = 16 * w + (l >> 3), x_p = l & 7;     // staging row (+ 8 it) and piece of x
+  const uint32_t bc_lane = (uint32_t)(bc_r * bc_row + bc_p * 16);
+  const uint32_t x_lane = (uint32_t)(x_r * xz_row + x_p * 16);
   const uint32_t dt_lane = (uint32_t)(l * dt_row);
 
   // Global access goes through buffer resources based at a chunk's first token
@@ -230,8 +242,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   // Target of the loads in flight: chain (tb, th, tg), first token tt (tt >= L:
   // none; every load reads zeros).
   int tb = 0, th = 0, tg = 0, tt = 0;
-  auto tgt_rsrc = [&](const uint16_t* base, uint32_t bat, uint32_t col, uint32_t rowb) {
-    const int left = L - tt;
+  auto tgt_rsrc = [&](const uint16_t* base, uint32_t bat, uint32_t col, uint32_t rowb, bool on = true) {
+    const int left = on ? L - tt : 0;
     return rsrc((const char*)(base + (uint64_t)tb * bat + col) + (uint32_t)tt * rowb,
                 left > 0 ? (uint32_t)left * rowb - col * 2 : 0u);
   };
@@ -239,30 +251,38 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     const __amdgpu_buffer_rsrc_t rB = tgt_rsrc(k.B, bc_bat, (uint32_t)tg * NS, bc_row);
 #pragma unroll
     for (int it = 0; it < 4; ++it)
-      pf.b[it] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(bc_lane + it * 64), 0, 0);
+      pf.b[it] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(bc_lane + it * 4 * bc_row), 0, 0);
   };
   auto load_c = [&](Prefetch& pf) {
     const __amdgpu_buffer_rsrc_t rC = tgt_rsrc(k.C, bc_bat, (uint32_t)tg * NS, bc_row);
 #pragma unroll
     for (int it = 0; it < 4; ++it)
-      pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bc_lane + it * 64), 0, 0);
+      pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bc_lane + it * 4 * bc_row), 0, 0);
   };
   auto load_x = [&](Prefetch& pf) {
     const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
-    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row);
+    // only wave 0 uses dt: the other waves' resource is empty (no memory access)
+    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, w == 0);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
-      pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(x_lane + it * 64), 0, 0);
+      pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(x_lane + it * 8 * xz_row), 0, 0);
     pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rD, (int)dt_lane, 0, 0);
   };
-  // z of the target chunk in the epilogue's layout (4 bf16 of row 16*it + li);
-  // without a gate these are loads of x, unused
-  u32x2 zkeep[4];
-  auto load_z = [&](u32x2 (&zz)[4]) {
+  // z of the target chunk, staged like x (without a gate: loads of x, unused)
+  auto load_z = [&](Prefetch& pf) {
     const __amdgpu_buffer_rsrc_t rZ = tgt_rsrc(gate ? k.z : k.x, xz_bat, (uint32_t)th * P, xz_row);
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-      zz[it] = __builtin_amdgcn_raw_buffer_load_b64(rZ, (int)(e_lane + it * 16 * xz_row), 0, 0);
+    for (int it = 0; it < 2; ++it)
+      pf.z[it] = __builtin_amdgcn_raw_buffer_load_b128(rZ, (int)(x_lane + it * 8 * xz_row), 0, 0);
+  };
+  // y of the previous chunk: sY (written by the epilogue in its layout) to memory
+  // as whole rows, through ry_prev (empty before the first chunk: no stores)
+  __amdgpu_buffer_rsrc_t ry_prev = rsrc(k.y, 0);
+  auto store_y = [&]() {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      __builtin_amdgcn_raw_buffer_store_b128(lds128(sY + (x_r + 8 * it) * LDX + x_p * 8), ry_prev,
+                                             (int)(x_lane + it * 8 * xz_row), 0, 0);
   };
 
   // The current item: chain (b, h) of group g, chunks [c, c_end); per-head constants.
@@ -289,12 +309,14 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   auto stage = [&](Prefetch& pf) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int pc = pc0 + 4 * it;
-      *(u32x4*)(sB + row * LDB + pc * 8) = pf.b[it];
-      *(u32x4*)(sC + row * LDB + pc * 8) = pf.c[it];
+      *(u32x4*)(sB + (bc_r + 4 * it) * LDB + bc_p * 8) = pf.b[it];
+      *(u32x4*)(sC + (bc_r + 4 * it) * LDB + bc_p * 8) = pf.c[it];
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) *(u32x4*)(sX + row * LDX + (pc0 + 4 * it) * 8) = pf.x[it];
+    for (int it = 0; it < 2; ++it) {
+      *(u32x4*)(sX + (x_r + 8 * it) * LDX + x_p * 8) = pf.x[it];
+      *(u32x4*)(sZ + (x_r + 8 * it) * LDX + x_p * 8) = pf.z[it];
+    }
     if (w == 0) {
       const int nt_valid = max(0, min(Q, L - tt));
       const float dtv = l < nt_valid ? softplus(lo_f(pf.dt) + bias) : 0.0f;  // past the end: a zero step
@@ -303,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       sDT[l] = dtv;
       sCS[l] = cs;
       sE[l] = fast_exp2(cs);
-      sW[l] = fast_exp2(cs_last - cs) * dtv;
+      sW[kslot(l)] = fast_exp2(cs_last - cs) * dtv;  // in k order
     }
   };
 
@@ -383,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   load_b(pf);
   load_c(pf);
   load_x(pf);
-  load_z(zkeep);
+  load_z(pf);
   stage(pf);
   state_in();
   if (tid == 0) sTicket[1] = (int)atomicAdd(qcounter(), 1u);
@@ -411,21 +433,26 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     } else {
       tt = L;
     }
+    store_y();  // the previous chunk's y (sY complete since barrier A)
     load_b(pf);
+    load_z(pf);
 
-    // x^T fragments (A operand of Y^T += X^T M^T; k = j = 32kb + 8lg + e) by two
-    // transposing loads each, and the epilogue's x values (8 bytes of row 16it + li)
+    // x^T fragments (A operand of Y^T += X^T M^T; k = j = 32kb + 8lg + kperm(e)) by
+    // two transposing loads each, and the epilogue's x values (8 bytes of row 16it + li)
     u32x4 xa[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = 32 * kb + 8 * lg;
-      const u32x2 lo = lds_tr(sX + (k0 + (li >> 2)) * LDX + 16 * w + 4 * (li & 3));
-      const u32x2 hi = lds_tr(sX + (k0 + 4 + (li >> 2)) * LDX + 16 * w + 4 * (li & 3));
+      const u32x2 lo = lds_tr(sX + (k0 + 2 * (li >> 2)) * LDX + 16 * w + 4 * (li & 3));
+      const u32x2 hi = lds_tr(sX + (k0 + 1 + 2 * (li >> 2)) * LDX + 16 * w + 4 * (li & 3));
       xa[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
-    u32x2 xe[4];
+    u32x2 xe[4], zkeep[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) xe[it] = lds64(sX + (16 * it + li) * LDX + 16 * w + 4 * lg);
+    for (int it = 0; it < 4; ++it) {
+      xe[it] = lds64(sX + (16 * it + li) * LDX + 16 * w + 4 * lg);
+      zkeep[it] = lds64(sZ + (16 * it + li) * LDX + 16 * w + 4 * lg);
+    }
 
     // ---- G^T tiles -> M (lower triangle): wave w takes tiles w, w+4, w+8
     {
@@ -463,9 +490,10 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
           const float v = acc[u][r] * fast_exp2(fminf(csi - sCS[j], 0.0f)) * sDT[j];
           m[r] = j <= i ? v : 0.0f;
         }
-        uint32_t* dst = (uint32_t*)(sM + i * LDM + 16 * Jt[u] + 4 * lg);
-        dst[0] = pack2(m[0], m[1]);
-        dst[1] = pack2(m[2], m[3]);
+        // columns in k order: j = 16Jt + 4lg + r sits at 16Jt + 8(lg/2) + kslot(4(lg%2) + r)
+        uint16_t* row = sM + i * LDM + 16 * Jt[u] + 8 * (lg >> 1) + 2 * (lg & 1);
+        *(uint32_t*)row = pack2(m[0], m[2]);
+        *(uint32_t*)(row + 4) = pack2(m[1], m[3]);
       }
     }
 
@@ -500,7 +528,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 
     load_x(pf);
     // ---- S = exp(cs_last) S + B^T (w x). A operand: B^T rows n = 16nt + li, k = j
-    // (transposing loads of B); B operand: w_j x[j][16w + li] from the x^T fragments.
+    // (transposing loads of B); B operand: w_j x[j][16w + li] from the x^T fragments
+    // (both in k order; sW holds w in k order).
     bf16x8 wxb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -520,8 +549,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int k0 = 32 * kb + 8 * lg;
-        const u32x2 lo = lds_tr(sB + (k0 + (li >> 2)) * LDB + 16 * nt + 4 * (li & 3));
-        const u32x2 hi = lds_tr(sB + (k0 + 4 + (li >> 2)) * LDB + 16 * nt + 4 * (li & 3));
+        const u32x2 lo = lds_tr(sB + (k0 + 2 * (li >> 2)) * LDB + 16 * nt + 4 * (li & 3));
+        const u32x2 hi = lds_tr(sB + (k0 + 1 + 2 * (li >> 2)) * LDB + 16 * nt + 4 * (li & 3));
         hacc[nt] = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), wxb[kb], hacc[nt]);
       }
     }
@@ -549,9 +578,9 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = fmaf(Dh, xs[r], yacc[it][r]) * (gate ? silu(zs[r]) : 1.0f);
-        const u32x2 out = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(out, rY, (int)(e_lane + it * 16 * xz_row), 0, 0);
+        *(u32x2*)(sY + (16 * it + li) * LDX + 16 * w + 4 * lg) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
       }
+      ry_prev = rY;
     }
     const bool finished = last && nxt < 0;
     if (last) {
@@ -568,15 +597,15 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     } else {
       ++c;
     }
-    // ---- the next chunk's z into the registers the epilogue freed; the next chunk
-    // into LDS (past the end, or after the last item: zeros, harmless). The loop
-    // leaves only here, so every path back to its head passes the waits of the
-    // staging: otherwise the next chunk would wait for this chunk's stores.
-    load_z(zkeep);
+    // ---- the next chunk into LDS (past the end, or after the last item: zeros,
+    // harmless). The loop leaves only here, so every path back to its head passes
+    // the waits of the staging: otherwise the next chunk would wait for this
+    // chunk's stores.
     stage(pf);
     __syncthreads();  // ---- barrier A of the next chunk
     if (finished) break;
   }
+  store_y();  // the last chunk's y
 }
 
 // Zeroes the queue counters, the give-up word and the per-chain flags (a kernel, not a memset, so
