@@ -74,6 +74,9 @@ constexpr int LDB = NS + 24;  // row pitch (bf16) of sB, sC: 76 dwords = 12 mod 
                               // windows of the transposing loads both hit distinct banks
 constexpr int LDX = P + 8;   // row pitch of sX
 constexpr int LDM = Q + 8;   // row pitch of sM
+// The wave that computes the chunk's steps and decays while staging: one of the
+// two waves with two G tiles (waves 0 and 1 take three).
+constexpr int kDecayWave = 3;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -171,7 +174,7 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 // chunk. Coalesced: 16 lanes cover a 256-byte row of B or C (an instruction, 4
 // rows), 8 lanes a 128-byte row of x (8 rows), so each load touches a few cache
 // lines rather than one per lane. B, C: rows 16w + 4it + l/16, piece l%16; x and
-// z: rows 16w + 8it + l/8, piece l%8; dt (wave 0 only): token l.
+// z: rows 16w + 8it + l/8, piece l%8; dt (wave kDecayWave only): token l.
 struct Prefetch {
   u32x4 b[4], c[4], x[2], z[2];
   uint32_t dt;  // raw bf16 bits
@@ -261,8 +264,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   };
   auto load_x = [&](Prefetch& pf) {
     const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
-    // only wave 0 uses dt: the other waves' resource is empty (no memory access)
-    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, w == 0);
+    // only the decay wave uses dt: the other waves' resource is empty (no memory access)
+    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, w == kDecayWave);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
       pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(x_lane + it * 8 * xz_row), 0, 0);
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     Dh = kk->D[h];
   };
 
-  // Chunk at token tt from the prefetch registers into LDS; wave 0 adds the
+  // Chunk at token tt from the prefetch registers into LDS; wave kDecayWave adds the
   // steps, their inclusive cumulative sum (exp2 domain) and the derived decays.
   auto stage = [&](Prefetch& pf) {
 #pragma unroll
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       *(u32x4*)(sX + (x_r + 8 * it) * LDX + x_p * 8) = pf.x[it];
       *(u32x4*)(sZ + (x_r + 8 * it) * LDX + x_p * 8) = pf.z[it];
     }
-    if (w == 0) {
+    if (w == kDecayWave) {
       const int nt_valid = max(0, min(Q, L - tt));
       const float dtv = l < nt_valid ? softplus(lo_f(pf.dt) + bias) : 0.0f;  // past the end: a zero step
       const float cs = wave_inclusive_sum(dtv * A2);
