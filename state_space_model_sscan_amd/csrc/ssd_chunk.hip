@@ -457,11 +457,13 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       zkeep[it] = lds64(sZ + (16 * it + li) * LDX + 16 * w + 4 * lg);
     }
 
-    // ---- G^T tiles -> M (lower triangle): wave w takes tiles w, w+4, w+8
+    // ---- G^T tiles -> M (lower triangle): wave w takes tiles w, w+4, w+8. Waves 2
+    // and 3 have no tile w+8 and compute tile w twice, writing the same values
+    // again: a branch around the third tile would split the phase into pieces
+    // that each wait for all of their LDS reads.
     {
       f32x4 acc[3];
       int Jt[3], It[3];
-      const int ntiles = w < 2 ? 3 : 2;  // tiles w, w+4, w+8 (< 10); wave-uniform
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
         const int ti = w + 4 * u < 10 ? w + 4 * u : w;
@@ -470,27 +472,36 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
         It[u] = ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3));
         acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      // the mask's cumulative sums and steps, read before the MFMAs so that their
+      // latency hides behind them (the scheduler would otherwise sink the reads to
+      // their use)
+      float csi[3];
+      f32x4 csj[3], dtj[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        csi[u] = sCS[16 * It[u] + li];
+        csj[u] = *(const f32x4*)(sCS + 16 * Jt[u] + 4 * lg);
+        dtj[u] = *(const f32x4*)(sDT + 16 * Jt[u] + 4 * lg);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-          if (u == 2 && ntiles < 3) continue;
           const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt[u] + li) * LDB + 32 * kb + 8 * lg));
           const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDB + 32 * kb + 8 * lg));
           acc[u] = mfma(a, bb, acc[u]);
         }
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
-        if (u == 2 && ntiles < 3) continue;
         // acc[r] = G[i][j], i = 16It + li, j = 16Jt + 4lg + r
         const int i = 16 * It[u] + li;
-        const float csi = sCS[i];
         float m[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * Jt[u] + 4 * lg + r;
           // computed for every lane and selected (the clamp keeps masked entries finite)
-          const float v = acc[u][r] * fast_exp2(fminf(csi - sCS[j], 0.0f)) * sDT[j];
+          const float v = acc[u][r] * fast_exp2(fminf(csi[u] - csj[u][r], 0.0f)) * dtj[u][r];
           m[r] = j <= i ? v : 0.0f;
         }
         // columns in k order: j = 16Jt + 4lg + r sits at 16Jt + 8(lg/2) + kslot(4(lg%2) + r)
@@ -504,6 +515,18 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     // ---- Y^T = S_in C^T, columns scaled by exp(cs_i). A operand: the state,
     // k = n in {32kb + 4lg + r} U {32kb + 16 + 4lg + r} (the accumulator layout);
     // B operand: C[i][n] for the same n, two 8-byte pieces of row i.
+    // the row scales and the state update's weights, read before the MFMAs
+    float ei[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) ei[it] = sE[16 * it + li];
+    f32x4 wj[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      wj[kb][0] = *(const f32x4*)(sW + 32 * kb + 8 * lg);
+      wj[kb][1] = *(const f32x4*)(sW + 32 * kb + 8 * lg + 4);
+    }
+    const float dec_last = sE[Q - 1];
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 yacc[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) yacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -524,9 +547,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const float ei = sE[16 * it + li];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yacc[it][r] *= ei;
+      for (int r = 0; r < 4; ++r) yacc[it][r] *= ei[it];
     }
 
     load_x(pf);
@@ -536,15 +558,13 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     bf16x8 wxb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int j0 = 32 * kb + 8 * lg;
-      const f32x4 w0 = *(const f32x4*)(sW + j0), w1 = *(const f32x4*)(sW + j0 + 4);
+      const f32x4 w0 = wj[kb][0], w1 = wj[kb][1];
       const u32x4 v = xa[kb];
       wxb[kb] = as_bf16x8(u32x4{pack2(lo_f(v[0]) * w0[0], hi_f(v[0]) * w0[1]),
                                 pack2(lo_f(v[1]) * w0[2], hi_f(v[1]) * w0[3]),
                                 pack2(lo_f(v[2]) * w1[0], hi_f(v[2]) * w1[1]),
                                 pack2(lo_f(v[3]) * w1[2], hi_f(v[3]) * w1[3])});
     }
-    const float dec_last = sE[Q - 1];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
