@@ -19,6 +19,10 @@ ARCH = os.environ.get("SSCAN_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU instructions are switched off for every device pass.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source flags. The SSD chunk kernel runs one workgroup per compute unit, so
+# the compiler may also use the accumulation registers; kept in the vector form,
+# its MFMA results need no copies between the two register files.
+SOURCE_FLAGS = {"ssd_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():
@@ -31,7 +35,8 @@ def _hipcc():
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
     cmd = [_hipcc(), "-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-           "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+           "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

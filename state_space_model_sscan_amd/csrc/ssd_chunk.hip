@@ -69,11 +69,13 @@ namespace {
 constexpr int Q = 64;        // tokens per chunk
 constexpr int P = 64;        // head_dim
 constexpr int NS = 128;      // state_dim
-constexpr int LDB = NS + 24;  // row pitch (bf16) of sB, sC: 76 dwords = 12 mod 64, so
-                              // 16 consecutive rows (MFMA operand reads) and the 4-row
-                              // windows of the transposing loads both hit distinct banks
+constexpr int LDB = NS + 24;  // row pitch (bf16) of sB: 76 dwords = 12 mod 64, so the 4-row
+                              // windows of the transposing loads hit distinct banks
+constexpr int LDC = NS + 16;  // row pitch of sC and sCk: 72 dwords, where 16-byte reads of
+                              // 16 rows (the MFMA operands) are conflict-free
 constexpr int LDX = P + 8;   // row pitch of sX
 constexpr int LDM = Q + 8;   // row pitch of sM
+constexpr size_t kCkBytes = (size_t)Q * LDC * 2;
 // The wave that computes the chunk's steps and decays while staging: one of the
 // two waves with two G tiles (waves 0 and 1 take three).
 constexpr int kDecayWave = 3;
@@ -184,7 +186,14 @@ struct Prefetch {
 
 __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * LDC];
+  // C again, each row in the k order of the Y^T = S C^T operand: positions
+  // 32kb + 8lg + e hold states 32kb + 4lg + e (e < 4) and 32kb + 16 + 4lg + e - 4
+  // (e >= 4), so that operand is one 16-byte read (the state accumulators fix
+  // that order)
+  // (dynamic LDS of kCkBytes: its size then does not lower the occupancy the code
+  // is compiled for, which schedules this kernel better)
+  extern __shared__ __attribute__((aligned(16))) uint16_t sCk[];
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t sM[Q * LDM];
   __shared__ __attribute__((aligned(16))) uint16_t sZ[Q * LDX];  // z of the chunk
@@ -313,7 +322,12 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       *(u32x4*)(sB + (bc_r + 4 * it) * LDB + bc_p * 8) = pf.b[it];
-      *(u32x4*)(sC + (bc_r + 4 * it) * LDB + bc_p * 8) = pf.c[it];
+      *(u32x4*)(sC + (bc_r + 4 * it) * LDC + bc_p * 8) = pf.c[it];
+      // states 8 bc_p + e: piece q = bc_p % 4 of the 32 states 32kb.. (kb = bc_p / 4)
+      // goes to positions 32kb + 16 (q % 2) + 4 (q / 2) and 8 further on
+      const int pk = 32 * (bc_p >> 2) + 16 * (bc_p & 1) + 4 * ((bc_p >> 1) & 1);
+      *(u32x2*)(sCk + (bc_r + 4 * it) * LDC + pk) = u32x2{pf.c[it][0], pf.c[it][1]};
+      *(u32x2*)(sCk + (bc_r + 4 * it) * LDC + pk + 8) = u32x2{pf.c[it][2], pf.c[it][3]};
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -489,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
           const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt[u] + li) * LDB + 32 * kb + 8 * lg));
-          const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDB + 32 * kb + 8 * lg));
+          const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDC + 32 * kb + 8 * lg));
           acc[u] = mfma(a, bb, acc[u]);
         }
 #pragma unroll
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     load_c(pf);
     // ---- Y^T = S_in C^T, columns scaled by exp(cs_i). A operand: the state,
     // k = n in {32kb + 4lg + r} U {32kb + 16 + 4lg + r} (the accumulator layout);
-    // B operand: C[i][n] for the same n, two 8-byte pieces of row i.
+    // B operand: C[i][n] for the same n, 16 bytes of row i of sCk.
     // the row scales and the state update's weights, read before the MFMAs
     float ei[4];
 #pragma unroll
@@ -540,9 +554,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       const bf16x8 aop = as_bf16x8(sv);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const uint16_t* cp = sC + (16 * it + li) * LDB + 32 * kb + 4 * lg;
-        const u32x2 lo = lds64(cp), hi = lds64(cp + 16);
-        yacc[it] = mfma(aop, as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), yacc[it]);
+        yacc[it] = mfma(aop, as_bf16x8(lds128(sCk + (16 * it + li) * LDC + 32 * kb + 8 * lg)), yacc[it]);
       }
     }
 #pragma unroll
@@ -728,7 +740,7 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   const int nwords = 256 + p.nchains;
   hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nwords + 255) / 256)), dim3(256), 0, s, k.queue,
                      nwords);
-  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
   return hipGetLastError();
 }
 
