@@ -180,13 +180,70 @@ __global__ __launch_bounds__(64) void tokenloop_scan_kernel(TLK k) {
   }
 }
 
-// One token per call: four lanes per channel, each holding a quarter of its
-// state_dim entries; the state is read, updated, then y is read from the
-// updated state ("Mamba", section "The state"). The four partial read-outs are
-// summed with a DPP butterfly inside the quad, and lane 0 of the quad stores y.
+// Contiguous loads of NQ elements into fp32 registers in 16-byte pieces (or the
+// whole run when it is shorter); the caller guarantees the alignment.
+template <int NQ>
+__device__ __forceinline__ void ld_run(const float* p, float (&o)[NQ]) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (NQ % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NQ; i += 4) {
+      const f32x4_t v = *(const f32x4_t*)(p + i);
+      o[i] = v[0]; o[i + 1] = v[1]; o[i + 2] = v[2]; o[i + 3] = v[3];
+    }
+  } else {
+    static_assert(NQ == 2, "runs of 2 or a multiple of 4");
+    const f32x2_t v = *(const f32x2_t*)p;
+    o[0] = v[0]; o[1] = v[1];
+  }
+}
+template <int NQ>
+__device__ __forceinline__ void ld_run(const uint16_t* p, float (&o)[NQ]) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t w[NQ / 2];
+  if constexpr (NQ % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < NQ / 2; i += 4) {
+      const u32x4_t v = *(const u32x4_t*)(p + 2 * i);
+      w[i] = v[0]; w[i + 1] = v[1]; w[i + 2] = v[2]; w[i + 3] = v[3];
+    }
+  } else if constexpr (NQ == 4) {
+    const u32x2_t v = *(const u32x2_t*)p;
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    static_assert(NQ == 2, "runs of 2, 4 or a multiple of 8");
+    w[0] = *(const uint32_t*)p;
+  }
+#pragma unroll
+  for (int i = 0; i < NQ / 2; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <int NQ>
+__device__ __forceinline__ void st_run(float* p, const float (&v)[NQ]) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (NQ % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NQ; i += 4) *(f32x4_t*)(p + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+  } else {
+    *(f32x2_t*)p = f32x2_t{v[0], v[1]};
+  }
+}
+
+// One token per call: four lanes per channel, lane q holding the contiguous
+// quarter [q NQ, q NQ + NQ) of its state_dim entries, so that a quad reads and
+// writes the channel's state as whole 16-byte pieces. The state is read,
+// updated, then y is read from the updated state ("Mamba", section "The
+// state"). The four partial read-outs are summed with a DPP butterfly inside the
+// quad, and lane 0 of the quad stores y. When state_dim is below the padded NP,
+// the entries are read one by one with a bound check.
 template <typename T, int NP, bool SSD, bool GATE>
 __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
-  constexpr int NQ = (NP + 3) / 4;  // entries per lane
+  constexpr int NQ = NP / 4;  // entries per lane
   const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int q = (int)(gl & 3);
   const int64_t c = gl >> 2;
@@ -198,13 +255,29 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
   const int64_t sidx = (b * k.Dc + cc) * k.N;
   const T* Bp = (const T*)k.B + (b * k.G + g) * k.N;
   const T* Cp = (const T*)k.C + (b * k.G + g) * k.N;
+  const int n0 = q * NQ;
+  const bool full = k.N == NP;  // every entry present: rows are NP-aligned runs
+  float bv[NQ], cv[NQ], hv[NQ];
+  if (full) {
+    ld_run<NQ>(Bp + n0, bv);
+    ld_run<NQ>(Cp + n0, cv);
+    ld_run<NQ>(k.h0 + sidx + n0, hv);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int n = n0 + i;
+      bv[i] = n < k.N ? Act<T>::ld(Bp + n) : 0.0f;
+      cv[i] = n < k.N ? Act<T>::ld(Cp + n) : 0.0f;
+      hv[i] = n < k.N ? k.h0[sidx + n] : 0.0f;
+    }
+  }
   float ib = 1.0f, ic = 1.0f;
   if (k.bc_eps > 0.0f) {
     float sb = 0.0f, sc = 0.0f;
-    for (int n = q; n < k.N; n += 4) {
-      const float bv = Act<T>::ld(Bp + n), cv = Act<T>::ld(Cp + n);
-      sb = fmaf(bv, bv, sb);
-      sc = fmaf(cv, cv, sc);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      sb = fmaf(bv[i], bv[i], sb);
+      sc = fmaf(cv[i], cv[i], sc);
     }
     // sum over the quad (lanes q = 0..3 of this channel)
     sb += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sb), 0xB1, 0xF, 0xF, false));
@@ -213,6 +286,15 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
     sc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sc), 0x4E, 0xF, 0xF, false));
     ib = 1.0f / sqrtf(sb / (float)k.N + k.bc_eps);
     ic = 1.0f / sqrtf(sc / (float)k.N + k.bc_eps);
+  }
+  float av[NQ];  // A_log of the entries (Mamba-1)
+  if constexpr (!SSD) {
+    if (full) {
+      ld_run<NQ>(k.A_log + cc * k.N + n0, av);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) av[i] = n0 + i < k.N ? k.A_log[cc * k.N + n0 + i] : 0.0f;
+    }
   }
   const int64_t idx = b * k.Dc + cc;  // seqlen 1
   const float xv = Act<T>::ld((const T*)k.x + idx);
@@ -223,14 +305,10 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
   float h[NQ];
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int n = q + 4 * i;  // entries q, q+4, ...: a quad reads 16 contiguous bytes per step
-    if (n < k.N) {
-      const float dec = SSD ? dec0 : fast_exp2(dtv * (-fast_exp2(k.A_log[cc * k.N + n] * kLog2e) * kLog2e));
-      h[i] = fmaf(dec, k.h0[sidx + n], dtx * (Act<T>::ld(Bp + n) * ib));
-      acc = fmaf(Act<T>::ld(Cp + n) * ic, h[i], acc);
-    } else {
-      h[i] = 0.0f;
-    }
+    // padded entries (n >= N) hold zeros in B, C and the state, and stay zero
+    const float dec = SSD ? dec0 : fast_exp2(dtv * (-fast_exp2(av[i] * kLog2e) * kLog2e));
+    h[i] = fmaf(dec, hv[i], dtx * (bv[i] * ib));
+    acc = fmaf(cv[i] * ic, h[i], acc);
   }
   acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
   acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
@@ -238,9 +316,13 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
   if (GATE) yv *= silu(Act<T>::ld((const T*)k.z + idx));
   if (active) {
     if (q == 0) Act<T>::st((T*)k.y + idx, yv);
+    if (full) {
+      st_run<NQ>(k.h_out + sidx + n0, h);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NQ; ++i)
-      if (q + 4 * i < k.N) k.h_out[sidx + q + 4 * i] = h[i];
+      for (int i = 0; i < NQ; ++i)
+        if (n0 + i < k.N) k.h_out[sidx + n0 + i] = h[i];
+    }
   }
 }
 

@@ -235,6 +235,48 @@ def test_ssd_step_chain_equals_oracle():
     check(host(state), hr, "f32", "state (ssd steps)")
 
 
+STEP_CASES = [
+    # ssd, batch, seqlen, channels or heads, N, act, gate, bc_eps
+    (False, 2, 6, 96, 5, "f32", True, 0.0),     # state_dim below the padded width: entry-wise path
+    (False, 3, 5, 64, 8, "bf16", False, 0.0),
+    (False, 2, 7, 130, 16, "bf16", True, 1e-6),
+    (False, 1, 4, 64, 24, "f32", True, 0.0),
+    (False, 2, 5, 64, 64, "bf16", True, 1e-6),
+    (False, 1, 3, 32, 40, "f32", False, 0.0),   # 40 of a padded 64
+    (True, 2, 6, 3, 16, "bf16", True, 0.0),
+    (True, 1, 5, 2, 64, "f32", False, 0.0),
+    (True, 2, 4, 2, 128, "bf16", True, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "ssd%d_b%d_L%d_D%d_N%d_%s_g%d_e%g" % c)
+def test_step_chain_shapes(case):
+    """One-token calls over a short sequence, the state updated in place, against
+    the oracle's scan of the whole sequence."""
+    ssd, b, L, D, N, act, gate, eps = case
+    say("step case", case)
+    if ssd:
+        inp = gen.make_ssd(b, L, D, 64, N, act=act, seed=N + L, gate=gate, h0=True)
+    else:
+        inp = gen.make_mamba1(b, L, D, N, act=act, seed=N + L, gate=gate, h0=True, bc_eps=eps)
+    yr, hr, _ = oracle.run_inputs(inp)
+    x, dt, B, C = dev(inp.x, act), dev(inp.dt_raw, act), dev(inp.B, act), dev(inp.C, act)
+    z = dev(inp.z, act) if gate else None
+    state = par(inp.h0).clone()
+    ys = []
+    for t in range(L):
+        one = lambda a: a[:, t:t + 1].clone()  # a fresh (16-byte aligned) allocation
+        args = (state, one(x), one(dt), par(inp.dt_bias), par(inp.A_log), one(B), one(C), par(inp.D),
+                one(z) if gate else None)
+        if ssd:
+            y1, _ = bd.sscan_ssd_step(*args, state_output=state)
+        else:
+            y1, _ = bd.sscan_step(*args, state_output=state, bc_rms_eps=eps)
+        ys.append(host(y1))
+    check(np.concatenate(ys, 1), yr, act, "y (steps)")
+    check(host(state), hr, act, "state (steps)")
+
+
 # ------------------------------------------------------------ invariants and edges
 def test_zero_step_on_gpu():
     inp = gen.make_mamba1(2, 40, 128, 16, act="f32", seed=21, gate=True, h0=True, want_states=True)
