@@ -15,15 +15,20 @@
 // tokens, carrying the state from chunk to chunk. Both are exact restatements
 // of the recurrence; only rounding differs.
 //
-// Mapping: one workgroup of 4 waves per (batch, head), walking the chunks in
-// order. Wave w owns head_dim columns [16w, 16w+16): its slice of the state
-// lives in fp32 MFMA accumulators (8 tiles of 16x16, state_dim 128) for the
-// whole sequence. The output is computed transposed, Y^T = X^T M^T + S C^T, so
-// that each lane ends up holding 4 neighbouring head_dim columns of one token
-// row and stores them straight from registers.
+// Mapping: persistent workgroups of 4 waves, one per compute unit, take work
+// items from per-die queues; an item is a segment of consecutive chunks of one
+// chain (a head of a batch row), and segments of a chain hand the state on
+// through the workspace (see the notes at state_in / state_out and ssd_plan).
+// Within an item the chunks are walked in order. Wave w owns head_dim columns
+// [16w, 16w+16): its slice of the state lives in fp32 MFMA accumulators (8 tiles
+// of 16x16, state_dim 128) for the whole item. The output is computed
+// transposed, Y^T = X^T M^T + S C^T, so that each lane ends up holding 4
+// neighbouring head_dim columns of one token row; y then leaves through LDS as
+// whole rows.
 //
 // Per chunk, between two barriers:
-//   after barrier A (chunk staged in LDS: B, C and x row-major, cumulative decay):
+//   after barrier A (chunk staged in LDS: B, C and x row-major, C once more in the
+//   k order of the S C^T operand, cumulative decay):
 //     - x^T fragments and the epilogue's x values move from LDS to registers;
 //     - G^T = B C^T on MFMA (10 lower-triangular 16x16 tiles over the 4 waves),
 //       masked and scaled into M[i, j] = G[i, j] exp(cs_i - cs_j) dt_j (bf16, LDS);
@@ -77,7 +82,7 @@ constexpr int LDX = P + 8;   // row pitch of sX
 constexpr int LDM = Q + 8;   // row pitch of sM
 constexpr size_t kCkBytes = (size_t)Q * LDC * 2;
 // The wave that computes the chunk's steps and decays while staging: one of the
-// two waves with two G tiles (waves 0 and 1 take three).
+// two waves whose third G tile is a repeat (waves 0 and 1 have three tiles).
 constexpr int kDecayWave = 3;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
