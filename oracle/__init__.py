@@ -42,6 +42,8 @@ def _load():
         lib.oracle_mamba1.restype = ctypes.c_int
         lib.oracle_ssd.argtypes = [I64] * 6 + [P] * 12
         lib.oracle_ssd.restype = ctypes.c_int
+        lib.oracle_ssd_attention.argtypes = [I64] * 5 + [P] * 6
+        lib.oracle_ssd_attention.restype = ctypes.c_int
         lib.oracle_conv1d_silu.argtypes = [I64] * 4 + [P] * 6
         lib.oracle_conv1d_silu.restype = ctypes.c_int
         lib.oracle_gated_rmsnorm.argtypes = [I64, I64, P, P, P, D, P]
@@ -97,6 +99,21 @@ def ssd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, h0=None, want_states=False):
     if rc != 0:
         raise ValueError("oracle_ssd rejected the shapes (rc=%d)" % rc)
     return y, h_out, states
+
+
+def ssd_attention(dt_raw, dt_bias, A_log, B, C):
+    """The SSD scan's hidden attention map. dt_raw: [b, L, H]; B, C: [b, L, G, N].
+    Returns alpha [b, L (query), L (key), H]: y_t = sum_s alpha[t, s] x_s + D x_t before the gate."""
+    lib = _load()
+    dt_raw, dt_bias, A_log, B, C = map(_f64, (dt_raw, dt_bias, A_log, B, C))
+    b, L, H = dt_raw.shape
+    G, N = B.shape[2], B.shape[3]
+    alpha = np.empty((b, L, L, H))
+    rc = lib.oracle_ssd_attention(b, L, H, N, G, _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                  _ptr(alpha))
+    if rc != 0:
+        raise ValueError("oracle_ssd_attention rejected the shapes (rc=%d)" % rc)
+    return alpha
 
 
 def conv1d_silu(x, weight, bias=None, conv_state=None):

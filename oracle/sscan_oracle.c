@@ -193,6 +193,50 @@ int oracle_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head_dim, 
 }
 
 /*
+ * The hidden attention of the SSD scan ([M2] "The hidden attention"): per head
+ * the scan is a causal linear map over tokens, y_t = sum_s alpha[t, s] x_s + D x_t
+ * (before the gate), with
+ *     alpha[t, s] = (C_t . B_s) * exp(decays_{s+1} + ... + decays_t) * betas_s,  s <= t,
+ * and 0 for s > t; betas = softplus(dt_raw + dt_bias), decays = betas * A,
+ * A = -exp(A_log) ([M2] "The mixer's values"). The decay sum is formed directly
+ * for each pair (no difference of running sums).
+ *   dt_raw  : [batch, seqlen, nheads];  dt_bias, A_log : [nheads]
+ *   B, C    : [batch, seqlen, ngroups, state_dim]; head h reads group h / (nheads / ngroups)
+ *   alpha   : [batch, seqlen (query t), seqlen (key s), nheads]
+ */
+int oracle_ssd_attention(int64_t batch, int64_t seqlen, int64_t nheads, int64_t state_dim, int64_t ngroups,
+                         const double* dt_raw, const double* dt_bias, const double* A_log, const double* B,
+                         const double* C, double* alpha) {
+  if (batch < 0 || seqlen < 0 || nheads <= 0 || state_dim <= 0 || ngroups <= 0 || nheads % ngroups != 0)
+    return -1;
+  const int64_t L = seqlen, H = nheads, N = state_dim, G = ngroups;
+  const int64_t heads_per_group = H / G;
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < batch * L; ++row) {
+    const int64_t b = row / L, t = row % L;
+    for (int64_t s = 0; s < L; ++s) {
+      for (int64_t h = 0; h < H; ++h) {
+        double v = 0.0;
+        if (s <= t) {
+          const int64_t g = h / heads_per_group;
+          const double A = -exp(A_log[h]);
+          const double* Ct = C + ((b * L + t) * G + g) * N;
+          const double* Bs = B + ((b * L + s) * G + g) * N;
+          double cb = 0.0;
+          for (int64_t n = 0; n < N; ++n) cb += Ct[n] * Bs[n];
+          double dsum = 0.0;  /* decays_{s+1} + ... + decays_t */
+          for (int64_t k = s + 1; k <= t; ++k) dsum += softplus(dt_raw[(b * L + k) * H + h] + dt_bias[h]) * A;
+          const double beta_s = softplus(dt_raw[(b * L + s) * H + h] + dt_bias[h]);
+          v = cb * exp(dsum) * beta_s;
+        }
+        alpha[((b * L + t) * L + s) * H + h] = v;
+      }
+    }
+  }
+  return 0;
+}
+
+/*
  * Causal depthwise conv1d of width W followed by silu, the step in front of the
  * scan ("Mamba-2", section "The block, in order": x, B, C = silu(conv1d(xBC)),
  * causal, width 4; "Mamba" tokentrails section "Code": depthwise, width 4).

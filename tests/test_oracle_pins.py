@@ -220,6 +220,44 @@ def test_ssd_hidden_attention_form(G):
     np.testing.assert_allclose(y, _ssd_hidden_attention(s), rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_attention_rebuilds_the_scan(G):
+    """The oracle's hidden attention map, applied to x, gives the token loop's y
+    before the gate ('Mamba-2', section 'The hidden attention'): two code paths."""
+    rng = np.random.default_rng(7 + G)
+    s = _rand_ssd(rng, 2, 23, 4, 3, 8, G=G, h0=False)
+    s["dt_raw"][0, 5, :] = -np.inf  # a zero step: its column of the map is zero
+    alpha = oracle.ssd_attention(s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"])
+    y, _, _ = oracle.ssd(**s)
+    y2 = np.einsum("btsh,bshp->bthp", alpha, s["x"]) + s["D"][None, None, :, None] * s["x"]
+    np.testing.assert_allclose(y2, y, rtol=1e-10, atol=1e-12)
+    assert np.all(alpha[0, :, 5, :] == 0.0)
+    # causal: nothing above the diagonal
+    L = alpha.shape[1]
+    assert np.all(alpha[:, np.triu_indices(L, 1)[0], np.triu_indices(L, 1)[1], :] == 0.0)
+
+
+def test_ssd_attention_hand_case():
+    """One head, state_dim 1, three tokens, written out: alpha[t, s] = C_t B_s exp(sum of the
+    decays after s up to t) beta_s, with beta = softplus(dt), decay = beta * A."""
+    sp = lambda v: math.log1p(math.exp(v))
+    dt_raw = np.array([[[0.0], [0.5], [-1.0]]])
+    dt_bias = np.array([0.25])
+    A_log = np.array([math.log(2.0)])  # A = -2
+    B = np.array([[[[1.5]], [[-2.0]], [[0.5]]]])
+    C = np.array([[[[0.5]], [[3.0]], [[-1.0]]]])
+    beta = [sp(0.25), sp(0.75), sp(-0.75)]
+    alpha = oracle.ssd_attention(dt_raw, dt_bias, A_log, B, C)[0, :, :, 0]
+    want = np.zeros((3, 3))
+    Bv, Cv = [1.5, -2.0, 0.5], [0.5, 3.0, -1.0]
+    for t in range(3):
+        for s_ in range(t + 1):
+            dec = sum(-2.0 * beta[k] for k in range(s_ + 1, t + 1))
+            want[t, s_] = Cv[t] * Bv[s_] * math.exp(dec) * beta[s_]
+    np.testing.assert_allclose(alpha, want, rtol=1e-14, atol=0)
+    assert alpha[2, 0] == pytest.approx(-1.0 * 1.5 * math.exp(-2.0 * (beta[1] + beta[2])) * beta[0], rel=1e-14)
+
+
 def test_ssd_equals_mamba1_with_tied_A():
     """Mamba-2 is Mamba-1 with one decay per head: channel (h, p), dt broadcast over p,
     A[c, n] = A_h, D[c] = D_h ('Mamba-2', section 'The mixer's values')."""
