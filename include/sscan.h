@@ -152,6 +152,22 @@ sscan_status sscan_ssd_step(const sscan_ssd_desc* desc, const float* state_input
                             const void* B, const void* C, const float* D, const void* z, void* y,
                             void* stream);
 
+/* The SSD scan's hidden attention map, an optional output for inspection
+ * ("Mamba-2", section "The hidden attention"): per head the scan is the causal
+ * linear map y_t = sum_s alpha[t, s] x_s + D x_t (before the gate), with
+ *     alpha[b, t, s, h] = (C_t . B_s) * exp(decays_{s+1} + ... + decays_t) * betas_s  for s <= t,
+ * and 0 for s > t; betas = softplus(dt_raw + dt_bias), decays = betas * A,
+ * A = -exp(A_log) ("The mixer's values"); head h reads group h / (nheads / ngroups).
+ * desc as for sscan_ssd_fwd (head_dim and chunk are not used).
+ *   dt_raw        [batch, seqlen, nheads]   act
+ *   dt_bias, A_log [nheads]                 f32
+ *   B, C          [batch, seqlen, ngroups, state_dim] act
+ *   alpha         [batch, seqlen (query t), seqlen (key s), nheads] f32 (out),
+ *                 batch * seqlen^2 * nheads * 4 bytes: meant for modest lengths.
+ * nheads <= 1024 and ngroups * (state_dim + 256) <= 16384, else SSCAN_ERR_UNSUPPORTED. */
+sscan_status sscan_ssd_attention(const sscan_ssd_desc* desc, const void* dt_raw, const float* dt_bias,
+                                 const float* A_log, const void* B, const void* C, float* alpha, void* stream);
+
 /* Causal depthwise conv1d + silu, the step in front of the scan ("Mamba-2",
  * section "The block, in order": x, B, C = silu(conv1d(xBC)), causal, width 4;
  * "Mamba", tokentrails lineage, section "Code": depthwise, width 4).

@@ -113,7 +113,8 @@ sscan_status check_mamba1_desc(const sscan_mamba1_desc* d, bool step) {
   return SSCAN_OK;
 }
 
-sscan_status check_ssd_desc(const sscan_ssd_desc* d, bool step) {
+// map_only: the descriptor of sscan_ssd_attention, which does not read head_dim
+sscan_status check_ssd_desc(const sscan_ssd_desc* d, bool step, bool map_only = false) {
   if (!d) return fail(SSCAN_ERR_NULL, "descriptor is NULL");
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->head_dim <= 0 || d->state_dim <= 0 ||
       d->ngroups <= 0)
@@ -127,7 +128,7 @@ sscan_status check_ssd_desc(const sscan_ssd_desc* d, bool step) {
   if (step && d->seqlen != 1) return fail(SSCAN_ERR_SHAPE, "sscan_ssd_step needs seqlen == 1");
   if (d->act != SSCAN_F32 && d->act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
   if (d->state_dim > 128) return fail(SSCAN_ERR_UNSUPPORTED, "SSD state_dim must be <= 128");
-  if (d->ngroups > 1 && ((d->nheads / d->ngroups) * d->head_dim) % 64 != 0)
+  if (!map_only && d->ngroups > 1 && ((d->nheads / d->ngroups) * d->head_dim) % 64 != 0)
     return fail(SSCAN_ERR_UNSUPPORTED,
                 "with ngroups > 1, (nheads / ngroups) * head_dim must be a multiple of 64");
   if (d->batch > 65535) return fail(SSCAN_ERR_UNSUPPORTED, "batch must be <= 65535");
@@ -327,6 +328,34 @@ sscan_status sscan_ssd_step(const sscan_ssd_desc* d, const float* state_input, f
   a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
   a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = nullptr;
   return hip_status(sscan::launch_ssd_step(a, (hipStream_t)stream), "sscan_ssd_step launch");
+}
+
+sscan_status sscan_ssd_attention(const sscan_ssd_desc* d, const void* dt_raw, const float* dt_bias,
+                                 const float* A_log, const void* B, const void* C, float* alpha, void* stream) {
+  sscan_status st = check_ssd_desc(d, false, true);
+  if (st != SSCAN_OK) return st;
+  const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->state_dim, G = d->ngroups;
+  const size_t es = d->act == SSCAN_BF16 ? 2 : 4;
+  // the map's size must fit a size_t and the kernel's 64-bit indexing
+  const double map_elems = (double)b * (double)L * (double)L * (double)H;
+  if (map_elems * 4.0 > 9.0e18) return fail(SSCAN_ERR_SHAPE, "the attention map exceeds 2^63 bytes");
+  sscan::AttnArgs a{};
+  a.batch = b; a.L = L; a.H = H; a.N = N; a.G = G; a.bf16 = d->act == SSCAN_BF16;
+  if (!sscan::ssd_attention_supported(a))
+    return fail(SSCAN_ERR_UNSUPPORTED, "needs nheads <= 1024 and ngroups * (state_dim + 256) <= 16384");
+  const Buf bufs[] = {
+      {"dt_raw", dt_raw, (size_t)(b * L * H) * es, false},
+      {"dt_bias", dt_bias, (size_t)H * 4, false},
+      {"A_log", A_log, (size_t)H * 4, false},
+      {"B", B, (size_t)(b * L * G * N) * es, false},
+      {"C", C, (size_t)(b * L * G * N) * es, false},
+      {"alpha", alpha, (size_t)b * (size_t)L * (size_t)L * (size_t)H * 4, true},
+  };
+  const bool req[] = {true, true, true, true, true, true};
+  st = check_buffers(bufs, 6, req, nullptr, nullptr);
+  if (st != SSCAN_OK) return st;
+  a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.alpha = alpha;
+  return hip_status(sscan::launch_ssd_attention(a, (hipStream_t)stream), "sscan_ssd_attention launch");
 }
 
 sscan_status sscan_conv1d_silu(const sscan_conv_desc* d, const void* x, const float* weight, const float* bias,

@@ -28,4 +28,17 @@ struct NormArgs {
 };
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
 
+struct AttnArgs {
+  int64_t batch, L, H, N, G;
+  bool bf16;
+  const void* dt;
+  const float* dt_bias;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  float* alpha;
+};
+bool ssd_attention_supported(const AttnArgs& a);
+hipError_t launch_ssd_attention(const AttnArgs& a, hipStream_t s);
+
 }  // namespace sscan

@@ -277,6 +277,34 @@ def test_step_chain_shapes(case):
     check(host(state), hr, act, "state (steps)")
 
 
+ATTN_CASES = [
+    # batch, seqlen, heads, N, groups, act
+    (1, 1, 2, 16, 1, "f32"),
+    (2, 37, 4, 16, 2, "f32"),
+    (1, 300, 3, 64, 1, "f32"),      # two blocks of keys
+    (2, 129, 8, 128, 1, "bf16"),
+    (1, 520, 80, 128, 1, "bf16"),   # three blocks of keys, the 2.7B layer's heads
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "b%d_L%d_H%d_N%d_G%d_%s" % c)
+def test_ssd_attention_map(case):
+    """The hidden attention map against the oracle's, element by element (the map is
+    fp32 from inputs that are exact in fp32, so the fp32 bound applies), and the
+    map rebuilding the GPU scan's y."""
+    b, L, H, N, G, act = case
+    say("attention case", case)
+    inp = gen.make_ssd(b, L, H, 64, N, G, act=act, seed=L + H, gate=False, h0=False, zero_step_frac=0.02)
+    ref = oracle.ssd_attention(inp.dt_raw, inp.dt_bias, inp.A_log, inp.B, inp.C)
+    got = host(bd.sscan_ssd_attention(dev(inp.dt_raw, act), par(inp.dt_bias), par(inp.A_log), dev(inp.B, act),
+                                      dev(inp.C, act)))
+    check(got, ref, "f32", "alpha")
+    assert np.all(got[:, np.triu_indices(L, 1)[0], np.triu_indices(L, 1)[1], :] == 0.0)
+    yg, _, _ = run_ssd(inp)
+    y2 = np.einsum("btsh,bshp->bthp", got, inp.x.astype(np.float64)) + inp.D[None, None, :, None] * inp.x
+    check(yg, y2, act, "y from the map")
+
+
 # ------------------------------------------------------------ invariants and edges
 def test_zero_step_on_gpu():
     inp = gen.make_mamba1(2, 40, 128, 16, act="f32", seed=21, gate=True, h0=True, want_states=True)
