@@ -9,8 +9,9 @@ them rotate so no step finds its inputs in the 256 MiB Infinity Cache. K steps
 are timed between two device synchronizations; each call is also bracketed by
 HIP events on the stream the kernels are launched on. Beside the main line the
 run reports the Falcon-Mamba-7b-width Mamba-1 workload, the Mamba-2 2.7B SSD
-workload and the 512-call decode-step workload, and the fp64 CPU oracle timed
-on this host. Prints one JSON line.
+workload, the 512-call decode-step workload, the Mamba-2 decode step, the
+conv1d + silu and gated RMS norm around the Mamba-2 scan, the hidden attention
+map, and the fp64 CPU oracle timed on this host. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -184,7 +185,7 @@ def bench_ssd(steps, warmup, torch, bd, gen):
                 tokens_per_s=b * L / (wall * 1e-3), bytes=by, hbm_gbs=by / (ev * 1e-3) / 1e9,
                 hbm_frac=by / (ev * 1e-3) / 1e9 / HBM_PEAK_GBS, flops_q256=fl,
                 mfma_tflops=fl / (ev * 1e-3) / 1e12, mfma_frac=fl / (ev * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                inp=inp)
+                inp=inp, base=base)
 
 
 def bench_step(torch, bd, gen, calls=512):
@@ -243,6 +244,125 @@ def bench_step(torch, bd, gen, calls=512):
                 us_per_step_wall=wall, us_per_step_gpu_eager=eager_gpu, us_per_step_graph=graph_us,
                 bytes_per_call=per_call_bytes,
                 graph_gbs=None if not graph_us else per_call_bytes / (graph_us * 1e-6) / 1e9)
+
+
+def hbm_entry(workload, ms_wall, ms_kernel, nbytes, **kw):
+    d = dict(workload=workload, ms_per_step=ms_wall, kernel_ms=ms_kernel, bytes=nbytes,
+             hbm_gbs=nbytes / (ms_kernel * 1e-3) / 1e9, hbm_frac=nbytes / (ms_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    d.update(kw)
+    return d
+
+
+def bench_mixer_ops(steps, warmup, torch, bd, s4):
+    """The steps next to the scan at the Mamba-2 2.7B layer shape (batch 4, 8192 tokens):
+    conv1d + silu over xBC (5120 + 2 x 128 = 5376 channels, width 4, with the carried conv
+    state in and out), and the gated RMS norm over y, z (80 heads x 64 = 5120 wide). Both
+    stream more than the 256 MiB Infinity Cache per call."""
+    base = s4["base"]
+    b, L = base["x"].shape[0], base["x"].shape[1]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5376)
+    Dc, W = 5376, 4
+    xbc = torch.randn((b, L, Dc), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((Dc, W), generator=g, device="cuda") * 0.5).contiguous()
+    bias = torch.randn((Dc,), generator=g, device="cuda") * 0.1
+    cst = torch.randn((b, Dc, W - 1), generator=g, device="cuda")
+    out = torch.empty_like(xbc)
+    cst_out = torch.empty_like(cst)
+
+    def conv(_):
+        bd.sscan_conv1d_silu(xbc, w, bias, cst, out=out, conv_state_out=cst_out)
+
+    wall, ev = time_calls(conv, [None], steps, warmup, torch)
+    cbytes = 2 * b * L * Dc * 2 + Dc * (W + 1) * 4 + 2 * b * Dc * (W - 1) * 4
+    conv_e = hbm_entry("mamba2-2.7b xBC conv1d+silu, bf16 %dx%dx%d, width %d, conv state in/out" % (b, L, Dc, W),
+                       wall, ev, cbytes, tokens_per_s=b * L / (wall * 1e-3))
+    del xbc, out
+
+    rows, width = b * L, base["x"].shape[2] * base["x"].shape[3]
+    y2, z2 = base["x"].view(rows, width), base["z"].view(rows, width)
+    wn = torch.rand((width,), generator=g, device="cuda") + 0.5
+    nout = torch.empty_like(y2)
+
+    def norm(_):
+        bd.sscan_gated_rmsnorm(y2, z2, wn, 1e-5, out=nout)
+
+    wall, ev = time_calls(norm, [None], steps, warmup, torch)
+    nbytes = 3 * rows * width * 2 + width * 4
+    norm_e = hbm_entry("mamba2-2.7b gated RMS norm, bf16 %d rows x %d" % (rows, width), wall, ev, nbytes,
+                       tokens_per_s=rows / (wall * 1e-3))
+    return conv_e, norm_e
+
+
+def bench_ssd_step(torch, bd, s4, nstates=32, calls=64):
+    """Mamba-2 2.7B decode: one-token sscan_ssd_step calls at batch 4 (state [4, 80, 64, 128]
+    fp32, 10.5 MB, updated in place). The calls cycle over `nstates` separate states, 336 MB
+    in all, so that no call finds its state in the 256 MiB Infinity Cache, as in a model whose
+    other layers' states pass through between two steps of a layer. Timed as a HIP graph
+    that replays `calls` launches."""
+    base = s4["base"]
+    one = lambda a, t: a[:, t:t + 1].contiguous()
+    xs = [one(base["x"], t) for t in range(calls)]
+    zs = [one(base["z"], t) for t in range(calls)]
+    dts = [one(base["dt_raw"], t) for t in range(calls)]
+    Bs = [one(base["B"], t) for t in range(calls)]
+    Cs = [one(base["C"], t) for t in range(calls)]
+    ys = [torch.empty_like(xs[0]) for _ in range(calls)]
+    states = [base["state_input"].clone() for _ in range(nstates)]
+
+    def run():
+        for t in range(calls):
+            st = states[t % nstates]
+            bd.sscan_ssd_step(st, xs[t], dts[t], base["dt_bias"], base["A_log"], Bs[t], Cs[t], base["D"], zs[t],
+                              y=ys[t], state_output=st)
+
+    run()
+    torch.cuda.synchronize()
+    prev = bd.set_pointer_checks(False)
+    try:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            run()
+    finally:
+        bd.set_pointer_checks(prev)
+    gr.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        gr.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    bsz, _, H, P = xs[0].shape
+    N = Bs[0].shape[-1]
+    G = Bs[0].shape[2]
+    per_call = 2 * bsz * H * P * N * 4 + 3 * bsz * H * P * 2 + bsz * H * 2 + 2 * bsz * G * N * 2 + 3 * H * 4
+    return dict(workload="mamba2-2.7b decode: sscan_ssd_step, batch %d, %d heads x %d, state %d, fp32 state "
+                         "in place, %d states in rotation" % (bsz, H, P, N, nstates),
+                us_per_step_graph=us, bytes_per_call=per_call, hbm_gbs=per_call / (us * 1e-6) / 1e9,
+                hbm_frac=per_call / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+
+def bench_attention(steps, warmup, torch, bd, s4, L=2048):
+    """The hidden attention map of batch row 0's first L tokens of the Mamba-2 2.7B workload
+    (80 heads, one group, state 128): alpha [1, L, L, 80] fp32, 1.34 GB written per call."""
+    base = s4["base"]
+    dt = base["dt_raw"][:1, :L].contiguous()
+    B = base["B"][:1, :L].contiguous()
+    C = base["C"][:1, :L].contiguous()
+    H = dt.shape[2]
+    alpha = torch.empty((1, L, L, H), dtype=torch.float32, device="cuda")
+
+    def fn(_):
+        bd.sscan_ssd_attention(dt, base["dt_bias"], base["A_log"], B, C, alpha=alpha)
+
+    wall, ev = time_calls(fn, [None], steps, warmup, torch)
+    nbytes = L * L * H * 4 + L * H * 2 + 2 * L * B.shape[2] * B.shape[3] * 2 + 2 * H * 4
+    return hbm_entry("mamba2-2.7b hidden attention map, 1 x %d tokens x %d heads, fp32 out" % (L, H), wall, ev,
+                     nbytes)
 
 
 def cpu_baseline(inp, min_seconds=10.0, max_runs=200):
@@ -311,10 +431,20 @@ def main():
         s4 = bench_ssd(max(10, args.steps // 4), 3, torch, bd, gen)
         log("bench: workload 2 (decode steps)")
         st = bench_step(torch, bd, gen)
+        log("bench: conv1d + silu, gated RMS norm")
+        conv_e, norm_e = bench_mixer_ops(max(10, args.steps // 4), 3, torch, bd, s4)
+        log("bench: Mamba-2 decode steps")
+        sst = bench_ssd_step(torch, bd, s4)
+        log("bench: hidden attention map")
+        att = bench_attention(max(5, args.steps // 10), 2, torch, bd, s4)
         extra = dict(
             mamba1_falcon_width={k: v for k, v in m3.items() if k != "inp"},
-            ssd_mamba2_2p7b={k: v for k, v in s4.items() if k != "inp"},
+            ssd_mamba2_2p7b={k: v for k, v in s4.items() if k not in ("inp", "base")},
             decode_step=st,
+            ssd_decode_step=sst,
+            conv1d_silu=conv_e,
+            gated_rmsnorm=norm_e,
+            ssd_attention_map=att,
         )
     cpu = None
     if not args.no_cpu_baseline:

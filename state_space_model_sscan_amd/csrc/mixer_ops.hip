@@ -1,18 +1,23 @@
 // mixer_ops.hip -- the steps next to the scan: causal depthwise conv1d + silu in
-// front of it, and the gated RMS norm after the Mamba-2 SSD.
+// front of it, and the gated RMS norm after the Mamba-2 SSD. Both are streams
+// over HBM with a few flops per byte, so the kernels are shaped for wide,
+// coalesced accesses: a lane moves 16 bytes of a token row per access.
 //
 // conv1d + silu ("Mamba-2", nnterp encyclopedia, section "The block, in order":
 // x, B, C = silu(conv1d(xBC)), causal, width 4; "Mamba", tokentrails lineage,
-// section "Code": depthwise, width 4): one lane per channel (coalesced over
-// channels) walks a block of 64 tokens with the last W-1 inputs in registers;
-// the W-1 inputs before a block come from x itself or, before the call's first
-// token, from the carried conv state.
+// section "Code": depthwise, width 4): a lane owns 16 bytes of channels (8 bf16
+// or 4 fp32) and walks a run of tokens, four rows in flight at a time, with the
+// last W-1 inputs in registers; the W-1 inputs before the run come from x itself
+// or, before the call's first token, from the carried conv state. Neighbouring
+// lanes take neighbouring channel groups, so a wave reads whole 1 KiB row
+// pieces. Widths that do not split into 16-byte groups take a lane per channel.
 //
 // gated RMS norm ("Mamba-2", section "The block, in order" and the note under
 // it): g = y * silu(z) normalised over the whole width of the row, times the
-// norm's weight. One workgroup per row: pass 1 sums g^2 (wave DPP/shuffle
-// reduction, then across the 4 waves in LDS), pass 2 re-reads the row (L2-hot)
-// and writes g * rsqrt(mean + eps) * weight.
+// norm's weight. One workgroup per row holds its g in registers (16-byte loads
+// of y and z), sums g^2 (wave reduction, then across the 4 waves in LDS) and
+// writes g * rsqrt(mean + eps) * weight. Rows too wide for the registers, or
+// not a whole number of 16-byte groups, re-read the L2-hot row instead.
 #include "device_common.hpp"
 #include "mixer_ops.hpp"
 
@@ -54,6 +59,116 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(ConvArgs a) {
 #pragma unroll
     for (int kk = 0; kk + 1 < W - 1; ++kk) hist[kk] = hist[kk + 1];
     if (W > 1) hist[W > 1 ? W - 2 : 0] = xt;
+  }
+}
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a row as fp32 values: 4 fp32 or 8 bf16 (little-endian pairs).
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void ld(const float* p, float* v) {
+    const v4u r = *(const v4u*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+  }
+  static __device__ __forceinline__ void st(float* p, const float* v) {
+    *(v4u*)p = v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  }
+};
+template <> struct Vec16<uint16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void ld(const uint16_t* p, float* v) {
+    const v4u r = *(const v4u*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(r[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, const float* v) {
+    v4u r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    *(v4u*)p = r;
+  }
+};
+
+constexpr int kConvUnroll = 4;  // token rows a lane has in flight
+
+// One lane: channels [c0, c0 + V) of batch row b, tokens [t0, t0 + tpl). The
+// sum for an output is formed in the order bias, w_0 x_{t-W+1}, ..., w_{W-1} x_t,
+// as in conv1d_silu_kernel, so both kernels give the same bits.
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv1d_silu_vec_kernel(ConvArgs a, int64_t tpl, int64_t ntb) {
+  constexpr int V = Vec16<T>::n;
+  constexpr int U = kConvUnroll;
+  const int64_t nvec = a.Dc / V;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cv = gid % nvec, rest = gid / nvec;
+  const int64_t tb = rest % ntb, b = rest / ntb;
+  if (b >= a.batch) return;
+  const int64_t c0 = cv * V;
+  const int64_t t0 = tb * tpl, t1 = min(a.L, t0 + tpl);
+  const T* xp = (const T*)a.x + b * a.L * a.Dc + c0;
+  T* op = (T*)a.out + b * a.L * a.Dc + c0;
+  float wt[W][V], bias[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+#pragma unroll
+    for (int kk = 0; kk < W; ++kk) wt[kk][j] = a.weight[(c0 + j) * W + kk];
+    bias[j] = a.bias ? a.bias[c0 + j] : 0.0f;
+  }
+  // win[0 .. W-2]: the inputs at t-W+1 .. t-1; win[W-1 ..]: the rows in flight
+  float win[W - 1 + U][V];
+#pragma unroll
+  for (int kk = 0; kk < W - 1; ++kk) {
+    const int64_t pos = t0 - (W - 1) + kk;
+    if (pos >= 0) {
+      Vec16<T>::ld(xp + pos * a.Dc, win[kk]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        win[kk][j] = a.state_in ? a.state_in[(b * a.Dc + c0 + j) * (W - 1) + (W - 1 + pos)] : 0.0f;
+    }
+  }
+  int64_t t = t0;
+  for (; t + U <= t1; t += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) Vec16<T>::ld(xp + (t + u) * a.Dc, win[W - 1 + u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        float acc = bias[j];
+#pragma unroll
+        for (int kk = 0; kk < W; ++kk) acc = fmaf(wt[kk][j], win[u + kk][j], acc);
+        o[j] = silu(acc);
+      }
+      Vec16<T>::st(op + (t + u) * a.Dc, o);
+    }
+#pragma unroll
+    for (int kk = 0; kk < W - 1; ++kk)
+#pragma unroll
+      for (int j = 0; j < V; ++j) win[kk][j] = win[U + kk][j];
+  }
+  for (; t < t1; ++t) {
+    Vec16<T>::ld(xp + t * a.Dc, win[W - 1]);
+    float o[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float acc = bias[j];
+#pragma unroll
+      for (int kk = 0; kk < W; ++kk) acc = fmaf(wt[kk][j], win[kk][j], acc);
+      o[j] = silu(acc);
+    }
+    Vec16<T>::st(op + t * a.Dc, o);
+#pragma unroll
+    for (int kk = 0; kk < W - 1; ++kk)
+#pragma unroll
+      for (int j = 0; j < V; ++j) win[kk][j] = win[kk + 1][j];
   }
 }
 
@@ -107,24 +222,111 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormArgs a) {
   }
 }
 
+// Row held in registers: thread i owns the 16-byte groups i, i + 256, ...
+template <typename T, int VPL>
+__global__ __launch_bounds__(256) void gated_rmsnorm_vec_kernel(NormArgs a) {
+  constexpr int V = Vec16<T>::n;
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nvec = (int)(a.width / V);
+  const T* y = (const T*)a.y + row * a.width;
+  const T* z = (const T*)a.z + row * a.width;
+  T* out = (T*)a.out + row * a.width;
+  float g[VPL][V];
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < nvec) {
+      float zv[V];
+      Vec16<T>::ld(y + (int64_t)i * V, g[k]);
+      Vec16<T>::ld(z + (int64_t)i * V, zv);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        g[k][j] *= silu(zv[j]);
+        ss = fmaf(g[k][j], g[k][j], ss);
+      }
+    }
+  }
+  const float total = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(total / (float)a.width + a.eps);
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < nvec) {
+      float wv[V], o[V];
+      Vec16<float>::ld(a.weight + (int64_t)i * V, wv);
+      if (V == 8) Vec16<float>::ld(a.weight + (int64_t)i * V + 4, wv + 4);
+#pragma unroll
+      for (int j = 0; j < V; ++j) o[j] = g[k][j] * inv * wv[j];
+      Vec16<T>::st(out + (int64_t)i * V, o);
+    }
+  }
+}
+
+// Tokens per lane for the vector kernel: the longest run (fewer re-read history
+// rows) that still gives about 8 waves per SIMD.
+int64_t conv_tokens_per_lane(int64_t lanes_per_run_block, int64_t L) {
+  int64_t tpl = 128;
+  while (tpl > 16 && lanes_per_run_block * ((L + tpl - 1) / tpl) < 256 * 4 * 8 * 64) tpl >>= 1;
+  return tpl;
+}
+
+template <typename T, int W>
+void launch_conv_vec(const ConvArgs& a, hipStream_t s) {
+  const int64_t nvec = a.Dc / Vec16<T>::n;
+  const int64_t tpl = conv_tokens_per_lane(a.batch * nvec, a.L);
+  const int64_t ntb = (a.L + tpl - 1) / tpl;
+  const int64_t lanes = a.batch * ntb * nvec;
+  hipLaunchKernelGGL((conv1d_silu_vec_kernel<T, W>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a,
+                     tpl, ntb);
+}
+
 template <typename T>
 void launch_conv_t(const ConvArgs& a, hipStream_t s) {
   const unsigned cb = (unsigned)((a.Dc + 255) / 256);
   if (a.L > 0) {
-    const dim3 grid(cb, (unsigned)((a.L + kConvTokens - 1) / kConvTokens), (unsigned)a.batch);
-    switch (a.W) {
-      case 1: hipLaunchKernelGGL((conv1d_silu_kernel<T, 1>), grid, dim3(256), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((conv1d_silu_kernel<T, 2>), grid, dim3(256), 0, s, a); break;
-      case 3: hipLaunchKernelGGL((conv1d_silu_kernel<T, 3>), grid, dim3(256), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((conv1d_silu_kernel<T, 4>), grid, dim3(256), 0, s, a); break;
-      case 5: hipLaunchKernelGGL((conv1d_silu_kernel<T, 5>), grid, dim3(256), 0, s, a); break;
-      case 6: hipLaunchKernelGGL((conv1d_silu_kernel<T, 6>), grid, dim3(256), 0, s, a); break;
-      case 7: hipLaunchKernelGGL((conv1d_silu_kernel<T, 7>), grid, dim3(256), 0, s, a); break;
-      default: hipLaunchKernelGGL((conv1d_silu_kernel<T, 8>), grid, dim3(256), 0, s, a); break;
+    const int64_t vec_lanes = a.batch * ((a.L + 15) / 16) * (a.Dc / Vec16<T>::n);
+    if (a.Dc % Vec16<T>::n == 0 && a.W >= 2 && a.W <= 4 && vec_lanes / 256 < (int64_t(1) << 30)) {
+      switch (a.W) {
+        case 2: launch_conv_vec<T, 2>(a, s); break;
+        case 3: launch_conv_vec<T, 3>(a, s); break;
+        default: launch_conv_vec<T, 4>(a, s); break;
+      }
+    } else {
+      const dim3 grid(cb, (unsigned)((a.L + kConvTokens - 1) / kConvTokens), (unsigned)a.batch);
+      switch (a.W) {
+        case 1: hipLaunchKernelGGL((conv1d_silu_kernel<T, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((conv1d_silu_kernel<T, 2>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((conv1d_silu_kernel<T, 3>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((conv1d_silu_kernel<T, 4>), grid, dim3(256), 0, s, a); break;
+        case 5: hipLaunchKernelGGL((conv1d_silu_kernel<T, 5>), grid, dim3(256), 0, s, a); break;
+        case 6: hipLaunchKernelGGL((conv1d_silu_kernel<T, 6>), grid, dim3(256), 0, s, a); break;
+        case 7: hipLaunchKernelGGL((conv1d_silu_kernel<T, 7>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((conv1d_silu_kernel<T, 8>), grid, dim3(256), 0, s, a); break;
+      }
     }
   }
   if (a.state_out && a.W > 1)
     hipLaunchKernelGGL(conv_state_kernel<T>, dim3(cb, (unsigned)a.batch), dim3(256), 0, s, a);
+}
+
+template <typename T>
+void launch_norm_t(const NormArgs& a, hipStream_t s) {
+  constexpr int V = Vec16<T>::n;
+  const dim3 grid((unsigned)a.rows);
+  const int64_t nvec = a.width / V;
+  if (a.width % V != 0 || nvec > 256 * 8) {
+    hipLaunchKernelGGL(gated_rmsnorm_kernel<T>, grid, dim3(256), 0, s, a);
+  } else if (nvec <= 256) {
+    hipLaunchKernelGGL((gated_rmsnorm_vec_kernel<T, 1>), grid, dim3(256), 0, s, a);
+  } else if (nvec <= 512) {
+    hipLaunchKernelGGL((gated_rmsnorm_vec_kernel<T, 2>), grid, dim3(256), 0, s, a);
+  } else if (nvec <= 1024) {
+    hipLaunchKernelGGL((gated_rmsnorm_vec_kernel<T, 4>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gated_rmsnorm_vec_kernel<T, 8>), grid, dim3(256), 0, s, a);
+  }
 }
 
 }  // namespace
@@ -138,8 +340,8 @@ hipError_t launch_conv1d_silu(const ConvArgs& a, hipStream_t s) {
 
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  if (a.bf16) hipLaunchKernelGGL(gated_rmsnorm_kernel<uint16_t>, dim3((unsigned)a.rows), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(gated_rmsnorm_kernel<float>, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+  if (a.bf16) launch_norm_t<uint16_t>(a, s);
+  else launch_norm_t<float>(a, s);
   return hipGetLastError();
 }
 

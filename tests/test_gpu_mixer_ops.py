@@ -40,6 +40,10 @@ CONV_CASES = [
     (1, 1000, 1792, 4, "bf16", True, True),  # mamba2-130m's xBC width
     (2, 130, 64, 1, "f32", False, True),
     (2, 70, 64, 7, "f32", True, True),
+    (2, 40, 100, 4, "bf16", True, True),     # bf16 width not a whole number of 16-byte groups
+    (2, 517, 5376, 4, "bf16", True, True),   # mamba2-2.7b's xBC width, many token runs, ragged tail
+    (3, 129, 96, 3, "f32", True, True),
+    (1, 67, 64, 2, "bf16", False, True),
 ]
 
 
@@ -70,7 +74,8 @@ def test_conv1d_state_chain_equals_whole():
     assert np.array_equal(host(sd), host(st))
 
 
-NORM_CASES = [(1, 1536, "f32"), (37, 1536, "bf16"), (5, 5120, "bf16"), (3, 333, "f32"), (700, 1536, "bf16")]
+NORM_CASES = [(1, 1536, "f32"), (37, 1536, "bf16"), (5, 5120, "bf16"), (3, 333, "f32"), (700, 1536, "bf16"),
+              (4, 16384, "bf16"), (6, 4104, "f32"), (3, 20000, "f32")]
 
 
 @pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "r%d_w%d_%s" % c)
