@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSCAN_ABI_VERSION 1
+#define SSCAN_ABI_VERSION 2
 
 typedef enum { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
 
@@ -164,9 +164,16 @@ sscan_status sscan_ssd_step(const sscan_ssd_desc* desc, const float* state_input
  *   B, C          [batch, seqlen, ngroups, state_dim] act
  *   alpha         [batch, seqlen (query t), seqlen (key s), nheads] f32 (out),
  *                 batch * seqlen^2 * nheads * 4 bytes: meant for modest lengths.
- * nheads <= 1024 and ngroups * (state_dim + 256) <= 16384, else SSCAN_ERR_UNSUPPORTED. */
+ *   workspace     device buffer of workspace_bytes >= sscan_ssd_attention_workspace_size()
+ *                 (batch * seqlen * nheads * 12 bytes: the running decay sums in fp64
+ *                 and the betas); contents on entry do not matter; must not overlap
+ *                 the other buffers (SSCAN_ERR_WORKSPACE when too small or NULL).
+ * Every entry is written (zeros above the diagonal). SSCAN_ERR_UNSUPPORTED when the
+ * map has 2^31 or more tiles of 32 query x 32 key tokens x up to 128 heads. */
+size_t sscan_ssd_attention_workspace_size(const sscan_ssd_desc* desc);
 sscan_status sscan_ssd_attention(const sscan_ssd_desc* desc, const void* dt_raw, const float* dt_bias,
-                                 const float* A_log, const void* B, const void* C, float* alpha, void* stream);
+                                 const float* A_log, const void* B, const void* C, float* alpha,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal depthwise conv1d + silu, the step in front of the scan ("Mamba-2",
  * section "The block, in order": x, B, C = silu(conv1d(xBC)), causal, width 4;

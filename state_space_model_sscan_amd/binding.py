@@ -20,7 +20,7 @@ F32, BF16 = 0, 1
 STATUS_NAMES = ["SSCAN_OK", "SSCAN_ERR_NULL", "SSCAN_ERR_SHAPE", "SSCAN_ERR_DTYPE", "SSCAN_ERR_UNSUPPORTED",
                 "SSCAN_ERR_NOT_DEVICE", "SSCAN_ERR_ALIGN", "SSCAN_ERR_ALIAS", "SSCAN_ERR_WORKSPACE", "SSCAN_ERR_HIP"]
 EXPORTS = ["sscan_mamba1_workspace_size", "sscan_mamba1_fwd", "sscan_step", "sscan_ssd_workspace_size",
-           "sscan_ssd_fwd", "sscan_ssd_step", "sscan_ssd_attention", "sscan_conv1d_silu", "sscan_gated_rmsnorm",
+           "sscan_ssd_fwd", "sscan_ssd_step", "sscan_ssd_attention_workspace_size", "sscan_ssd_attention", "sscan_conv1d_silu", "sscan_gated_rmsnorm",
            "sscan_status_string",
            "sscan_last_error", "sscan_abi_version", "sscan_set_pointer_checks"]
 
@@ -77,7 +77,9 @@ def lib():
     L.sscan_ssd_fwd.restype = I
     L.sscan_ssd_step.argtypes = [SD] + [P] * 12
     L.sscan_ssd_step.restype = I
-    L.sscan_ssd_attention.argtypes = [SD] + [P] * 7
+    L.sscan_ssd_attention_workspace_size.argtypes = [SD]
+    L.sscan_ssd_attention_workspace_size.restype = S
+    L.sscan_ssd_attention.argtypes = [SD] + [P] * 7 + [S, P]
     L.sscan_ssd_attention.restype = I
     L.sscan_conv1d_silu.argtypes = [ctypes.POINTER(ConvDesc)] + [P] * 7
     L.sscan_conv1d_silu.restype = I
@@ -250,9 +252,10 @@ def sscan_ssd_step(state_input, x, dt_raw, dt_bias, A_log, B, C, D, z=None, y=No
     return y, state_output
 
 
-def sscan_ssd_attention(dt_raw, dt_bias, A_log, B, C, alpha=None, stream=None):
+def sscan_ssd_attention(dt_raw, dt_bias, A_log, B, C, alpha=None, workspace=None, stream=None):
     """The SSD scan's hidden attention map. dt_raw: [b, L, H]; B, C: [b, L, G, N] (same dtype).
-    Returns alpha [b, L (query), L (key), H] f32: y_t = sum_s alpha[t, s] x_s + D x_t before the gate."""
+    Returns alpha [b, L (query), L (key), H] f32: y_t = sum_s alpha[t, s] x_s + D x_t before the gate.
+    The workspace (b * L * H * 12 bytes) is allocated here when not given."""
     _same("B", B, dt_raw.dtype)
     _same("C", C, dt_raw.dtype)
     for n, t in (("dt_bias", dt_bias), ("A_log", A_log)):
@@ -262,8 +265,12 @@ def sscan_ssd_attention(dt_raw, dt_bias, A_log, B, C, alpha=None, stream=None):
     desc = SSDDesc(b, L, H, 1, N, G, 0, _act_code(dt_raw), 0)
     if alpha is None:
         alpha = torch.empty((b, L, L, H), dtype=torch.float32, device=dt_raw.device)
+    need = int(lib().sscan_ssd_attention_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dt_raw.device)
+    wb = workspace.numel() * workspace.element_size()
     check(lib().sscan_ssd_attention(ctypes.byref(desc), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
-                                    _ptr(alpha), _stream(stream)))
+                                    _ptr(alpha), _ptr(workspace), wb, _stream(stream)))
     return alpha
 
 

@@ -330,8 +330,21 @@ sscan_status sscan_ssd_step(const sscan_ssd_desc* d, const float* state_input, f
   return hip_status(sscan::launch_ssd_step(a, (hipStream_t)stream), "sscan_ssd_step launch");
 }
 
+static sscan::AttnArgs attn_args(const sscan_ssd_desc* d) {
+  sscan::AttnArgs a{};
+  a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads; a.N = d->state_dim; a.G = d->ngroups;
+  a.bf16 = d->act == SSCAN_BF16;
+  return a;
+}
+
+size_t sscan_ssd_attention_workspace_size(const sscan_ssd_desc* d) {
+  if (check_ssd_desc(d, false, true) != SSCAN_OK) return 0;
+  return sscan::ssd_attention_ws(attn_args(d));
+}
+
 sscan_status sscan_ssd_attention(const sscan_ssd_desc* d, const void* dt_raw, const float* dt_bias,
-                                 const float* A_log, const void* B, const void* C, float* alpha, void* stream) {
+                                 const float* A_log, const void* B, const void* C, float* alpha, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   sscan_status st = check_ssd_desc(d, false, true);
   if (st != SSCAN_OK) return st;
   const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->state_dim, G = d->ngroups;
@@ -339,10 +352,10 @@ sscan_status sscan_ssd_attention(const sscan_ssd_desc* d, const void* dt_raw, co
   // the map's size must fit a size_t and the kernel's 64-bit indexing
   const double map_elems = (double)b * (double)L * (double)L * (double)H;
   if (map_elems * 4.0 > 9.0e18) return fail(SSCAN_ERR_SHAPE, "the attention map exceeds 2^63 bytes");
-  sscan::AttnArgs a{};
-  a.batch = b; a.L = L; a.H = H; a.N = N; a.G = G; a.bf16 = d->act == SSCAN_BF16;
+  sscan::AttnArgs a = attn_args(d);
   if (!sscan::ssd_attention_supported(a))
-    return fail(SSCAN_ERR_UNSUPPORTED, "needs nheads <= 1024 and ngroups * (state_dim + 256) <= 16384");
+    return fail(SSCAN_ERR_UNSUPPORTED, "the map needs fewer than 2^31 tiles of 32 x 32 tokens x 128 heads");
+  const size_t need = sscan::ssd_attention_ws(a);
   const Buf bufs[] = {
       {"dt_raw", dt_raw, (size_t)(b * L * H) * es, false},
       {"dt_bias", dt_bias, (size_t)H * 4, false},
@@ -350,11 +363,17 @@ sscan_status sscan_ssd_attention(const sscan_ssd_desc* d, const void* dt_raw, co
       {"B", B, (size_t)(b * L * G * N) * es, false},
       {"C", C, (size_t)(b * L * G * N) * es, false},
       {"alpha", alpha, (size_t)b * (size_t)L * (size_t)L * (size_t)H * 4, true},
+      {"workspace", workspace, need, true},
   };
-  const bool req[] = {true, true, true, true, true, true};
-  st = check_buffers(bufs, 6, req, nullptr, nullptr);
+  const bool req[] = {true, true, true, true, true, true, true};
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SSCAN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  st = check_buffers(bufs, 7, req, nullptr, nullptr);
   if (st != SSCAN_OK) return st;
   a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.alpha = alpha;
+  a.ws_P = (double*)workspace;
+  a.ws_beta = (float*)(a.ws_P + b * L * H);
   return hip_status(sscan::launch_ssd_attention(a, (hipStream_t)stream), "sscan_ssd_attention launch");
 }
 

@@ -7,14 +7,28 @@
 // and 0 above the diagonal; betas = softplus(dt_raw + dt_bias), decays = betas * A,
 // A = -exp(A_log) (section "The mixer's values"); head h reads group h / (H / G).
 //
-// One workgroup per query token t and batch row. It stages C_t, then walks the
-// keys downward from s = t in blocks of 256: first every thread forms one
-// C_t . B_s per group, then one thread per head walks the block's keys in
-// descending order, keeping the decay sum decays_{s+1} + ... + decays_t in fp64
-// (a sum of same-sign terms, formed in the order the definition adds them, with
-// no difference of running sums) and writing alpha[b, t, s, h], the heads of one
-// key contiguous. The entries above the diagonal are written as zeros. The map
-// is [batch, seqlen, seqlen, heads] and is meant for inspection at modest lengths.
+// The map is [batch, t, s, heads] fp32: writing it is the whole cost, so the
+// work is shaped for the store stream.
+//
+// attn_prefix_kernel: one wave per (batch row, head) forms, in fp64,
+//     P[t] = decays_0 + ... + decays_t     (times log2 e)
+// and betas_t into the caller's workspace. Each lane sums a contiguous run of
+// tokens, the runs' totals are scanned across the wave, and each lane then
+// rewalks its run from its offset. P is a sum of same-sign terms, so
+// exponent(t, s) = P[t] - P[s] = decays_{s+1} + ... + decays_t is exact to
+// 2^-53 |P| in fp64, far below the fp32 result.
+//
+// ssd_attention_kernel: a work item is one batch row, one key tile of 32
+// tokens [s0, s0 + 32), one query tile of 32 tokens, and a chunk of at
+// most 128 heads (whole groups, or part of one group when a group has more
+// than 128 heads). For every query row t of a tile the item writes keys
+// s0..s0+31 x the chunk's heads, one contiguous run per row; a lane writes 16
+// bytes (4 heads of one key) at a time when the heads per group are a
+// multiple of 4, else one value; the stores are marked non-temporal, as the
+// map is not read back here. A lane keeps P and betas of its keys in
+// registers, the tile's rows of P sit in LDS, and C_t . B_s for the tile comes
+// from a small LDS-staged product per group. Query tiles above the key tile
+// are zeros; on the diagonal tile the entries with s > t are zeros.
 #include "device_common.hpp"
 #include "mixer_ops.hpp"
 
@@ -22,77 +36,295 @@ namespace sscan {
 
 namespace {
 
-constexpr int kKeys = 256;      // keys per block of the walk (= threads)
-constexpr int kMaxHeadsPerThread = 4;
+constexpr int kT = 32;        // tokens per tile side
+constexpr int kRange = 1;     // query tiles per work item (1 measured best: many short items)
+constexpr int kMaxHC = 128;   // heads per chunk
+constexpr int kMaxGPC = 8;    // groups per chunk
+constexpr int kKC = 64;       // state entries per staging step of C . B
+constexpr int kCP = kKC + 1;  // row pitch of the staged C (floats)
+constexpr double kLog2eD = 1.4426950408889634;
+
+struct AttnPlan {
+  int64_t hpg;     // heads per group
+  int64_t HC;      // heads per chunk (the LDS row pitch)
+  int64_t GPC;     // groups per chunk (1 when hpg > kMaxHC)
+  int64_t cpg;     // chunks per group when hpg > kMaxHC
+  int64_t nchunks, nkt, nqr;
+};
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kPrefixBatch = 16;  // dt loads in flight per lane
 
 template <typename T>
-__global__ __launch_bounds__(256) void ssd_attention_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int64_t L = a.L, H = a.H, N = a.N, G = a.G;
-  const int64_t t = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  float* sC = smem;          // [G][N]: C_t
-  float* sCB = smem + G * N;  // [G][kKeys]: C_t . B_s for the keys of the block
-  const T* Cb = (const T*)a.C + (b * L + t) * G * N;
-  for (int64_t e = tid; e < G * N; e += 256) sC[e] = Act<T>::ld(Cb + e);
-  const int64_t hpg = H / G;
-  // this thread's heads: tid, tid + 256, ...
-  double run[kMaxHeadsPerThread];  // decays_{s+1} + ... + decays_t for the next key s
-  float A[kMaxHeadsPerThread], bias[kMaxHeadsPerThread];
+__global__ __launch_bounds__(256) void attn_prefix_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (batch row, head)
+  if (w >= a.batch * a.H) return;                                   // whole waves leave
+  const int64_t b = w / a.H, h = w % a.H;
+  const float A = -expf(a.A_log[h]);
+  const float bias = a.dt_bias[h];
+  const T* dt = (const T*)a.dt + b * a.L * a.H + h;
+  const int64_t per = (a.L + 63) / 64;
+  const int64_t lo = min(a.L, lane * per), hi = min(a.L, lo + per);
+  double sum = 0.0;
+  for (int64_t j0 = lo; j0 < hi; j0 += kPrefixBatch) {
+    float bv[kPrefixBatch];
 #pragma unroll
-  for (int i = 0; i < kMaxHeadsPerThread; ++i) {
-    const int64_t h = tid + 256 * i;
-    run[i] = 0.0;
-    A[i] = h < H ? -expf(a.A_log[h]) : 0.f;
-    bias[i] = h < H ? a.dt_bias[h] : 0.f;
+    for (int u = 0; u < kPrefixBatch; ++u)
+      bv[u] = j0 + u < hi ? softplus(Act<T>::ld(dt + (j0 + u) * a.H) + bias) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kPrefixBatch; ++u) sum += (double)bv[u] * (double)A;
   }
-  float* out = a.alpha + (b * L + t) * L * H;  // row t: [s][h]
-  for (int64_t hi = t; hi >= 0; hi -= kKeys) {
-    const int64_t lo = hi - kKeys + 1 > 0 ? hi - kKeys + 1 : 0;  // keys lo .. hi
-    __syncthreads();  // sC staged; the previous block's sCB read
-    {
-      const int64_t s = lo + tid;
-      if (s <= hi) {
-        for (int64_t g = 0; g < G; ++g) {
-          const T* Bs = (const T*)a.B + ((b * L + s) * G + g) * N;
-          float acc = 0.f;
-          for (int64_t n = 0; n < N; ++n) acc = fmaf(sC[g * N + n], Act<T>::ld(Bs + n), acc);
-          sCB[g * kKeys + tid] = acc;
+  // inclusive scan of the runs' totals over the wave, then shifted by one lane
+  double incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  double P = __shfl_up(incl, 1, 64);
+  if (lane == 0) P = 0.0;
+  double* wp = a.ws_P + b * a.L * a.H + h;
+  float* wb = a.ws_beta + b * a.L * a.H + h;
+  for (int64_t j0 = lo; j0 < hi; j0 += kPrefixBatch) {
+    float bv[kPrefixBatch];
+#pragma unroll
+    for (int u = 0; u < kPrefixBatch; ++u)
+      bv[u] = j0 + u < hi ? softplus(Act<T>::ld(dt + (j0 + u) * a.H) + bias) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kPrefixBatch; ++u) {
+      P += (double)bv[u] * (double)A;
+      if (j0 + u < hi) {
+        wp[(j0 + u) * a.H] = P * kLog2eD;
+        wb[(j0 + u) * a.H] = bv[u];
+      }
+    }
+  }
+}
+
+template <typename T, int VW>
+__global__ __launch_bounds__(256) void ssd_attention_kernel(AttnArgs a, AttnPlan p) {
+  constexpr int SPT = kT * kMaxHC / VW / 256;  // slots (VW heads of one key) per thread
+  extern __shared__ __attribute__((aligned(16))) double smem_d[];
+  const int tid = threadIdx.x;
+  const int64_t L = a.L, H = a.H, N = a.N;
+  int64_t item = blockIdx.x;
+  const int64_t qr = item % p.nqr;
+  item /= p.nqr;
+  const int64_t kt = item % p.nkt;
+  item /= p.nkt;
+  const int64_t chunk = item % p.nchunks;
+  const int64_t b = item / p.nchunks;
+  int64_t h_lo, h_hi, g_lo, ngc;
+  if (p.hpg <= kMaxHC) {
+    h_lo = chunk * p.HC;
+    h_hi = min(H, h_lo + p.HC);
+    g_lo = h_lo / p.hpg;
+    ngc = (h_hi - h_lo) / p.hpg;
+  } else {
+    const int64_t g = chunk / p.cpg, sub = chunk % p.cpg;
+    h_lo = g * p.hpg + sub * kMaxHC;
+    h_hi = min(g * p.hpg + p.hpg, h_lo + kMaxHC);
+    g_lo = g;
+    ngc = 1;
+  }
+  const int hc = (int)(h_hi - h_lo);
+  const int HCp = (int)p.HC;
+  const int64_t s0 = kt * kT;
+  const int64_t q_first = qr * kRange;
+  const int64_t q_end = min(p.nkt, q_first + kRange);
+
+  double* sPq = smem_d;                     // [kT][HCp]: P at the tile's rows
+  float* sCB = (float*)(sPq + kT * HCp);    // [GPC][kT (t)][kT (s)]
+  float* sC = sCB + p.GPC * kT * kT;        // [kT (t)][kCP]
+  float* sB = sC + kT * kCP;                // [kKC][kT (s)]
+
+  const int nslot = kT * hc / VW;
+  float* arow = a.alpha + (b * L) * L * H + h_lo;  // + (t * L + s) * H + head offset
+  const double* Pb = a.ws_P + b * L * H + h_lo;
+  const float* betab = a.ws_beta + b * L * H + h_lo;
+
+  double pk[SPT][VW];  // P at the slot's key
+  float bt[SPT][VW];   // betas at the slot's key
+  int cbi[SPT];        // the slot's column of C . B: group * kT * kT + key
+  if (q_end - 1 >= kt) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int slot = tid + 256 * k;
+      const int e = slot * VW;
+      const int sl = e / hc, ho = e % hc;
+      const bool ok = slot < nslot && s0 + sl < L;
+#pragma unroll
+      for (int i = 0; i < VW; ++i) {
+        pk[k][i] = ok ? Pb[(s0 + sl) * H + ho + i] : 0.0;
+        bt[k][i] = ok ? betab[(s0 + sl) * H + ho + i] : 0.0f;
+      }
+      cbi[k] = (int)(((h_lo + ho) / p.hpg - g_lo) * kT * kT) + sl;
+    }
+  }
+
+  for (int64_t qt = q_first; qt < q_end; ++qt) {
+    const int64_t t0 = qt * kT;
+    const int64_t nrow = min((int64_t)kT, L - t0);
+    if (qt < kt) {
+      // above the diagonal: zeros
+      for (int64_t r = 0; r < nrow; ++r) {
+        float* orow = arow + ((t0 + r) * L + s0) * H;
+        for (int slot = tid; slot < nslot; slot += 256) {
+          const int e = slot * VW;
+          const int sl = e / hc, ho = e % hc;
+          if (s0 + sl >= L) continue;
+          if (VW == 4) __builtin_nontemporal_store(f32x4v{0.f, 0.f, 0.f, 0.f}, (f32x4v*)(orow + sl * H + ho));
+          else orow[sl * H + ho] = 0.f;
         }
+      }
+      continue;
+    }
+    __syncthreads();  // the previous tile's rows are written: sPq and sCB are free
+    for (int e = tid; e < kT * hc; e += 256) {
+      const int r = e / hc, hh = e % hc;
+      sPq[r * HCp + hh] = r < nrow ? Pb[(t0 + r) * H + hh] : 0.0;
+    }
+    // C_t . B_s for the tile, per group of the chunk
+    {
+      const int tq = tid >> 3, sk = (tid & 7) * 4;
+      for (int64_t gi = 0; gi < ngc; ++gi) {
+        const int64_t g = g_lo + gi;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t n0 = 0; n0 < N; n0 += kKC) {
+          // stage C[t0 + r][g][n0 ..] and B[s0 + r][g][n0 ..] (B transposed)
+#pragma unroll
+          for (int rep = 0; rep < kKC / 32; ++rep) {
+            const int r = tid >> 3, c = (tid & 7) * 4 + 32 * rep;
+            const int64_t t = t0 + r, s = s0 + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int64_t n = n0 + c + i;
+              sC[r * kCP + c + i] = (t < L && n < N) ? Act<T>::ld((const T*)a.C + ((b * L + t) * a.G + g) * N + n) : 0.f;
+              sB[(c + i) * kT + r] = (s < L && n < N) ? Act<T>::ld((const T*)a.B + ((b * L + s) * a.G + g) * N + n) : 0.f;
+            }
+          }
+          __syncthreads();
+#pragma unroll 8
+          for (int k = 0; k < kKC; ++k) {
+            const float cv = sC[tq * kCP + k];
+            const f32x4v bv = *(const f32x4v*)(sB + k * kT + sk);
+            acc[0] = fmaf(cv, bv[0], acc[0]);
+            acc[1] = fmaf(cv, bv[1], acc[1]);
+            acc[2] = fmaf(cv, bv[2], acc[2]);
+            acc[3] = fmaf(cv, bv[3], acc[3]);
+          }
+          __syncthreads();
+        }
+        *(f32x4v*)(sCB + (gi * kT + tq) * kT + sk) = f32x4v{acc[0], acc[1], acc[2], acc[3]};
       }
     }
     __syncthreads();
+    // the rows: alpha[t][s0 + sl][h] = CB[t][s] * exp2(P[t] - P[s]) * betas_s for s <= t
+    for (int64_t r = 0; r < nrow; ++r) {
+      const int64_t t = t0 + r;
+      float* orow = arow + (t * L + s0) * H;
 #pragma unroll
-    for (int i = 0; i < kMaxHeadsPerThread; ++i) {
-      const int64_t h = tid + 256 * i;
-      if (h >= H) continue;
-      const int64_t g = h / hpg;
-      double r = run[i];
-      for (int64_t s = hi; s >= lo; --s) {
-        const float beta = softplus(Act<T>::ld((const T*)a.dt + (b * L + s) * H + h) + bias[i]);
-        out[s * H + h] = sCB[g * kKeys + (s - lo)] * fast_exp2((float)r * kLog2e) * beta;
-        r += (double)beta * (double)A[i];  // the decay of key s joins the sum for keys below it
+      for (int k = 0; k < SPT; ++k) {
+        const int slot = tid + 256 * k;
+        const int e = slot * VW;
+        const int sl = e / hc, ho = e % hc;
+        if (slot >= nslot || s0 + sl >= L) continue;
+        float o[VW];
+        if (s0 + sl > t) {
+#pragma unroll
+          for (int i = 0; i < VW; ++i) o[i] = 0.f;
+        } else {
+#pragma unroll
+          for (int i = 0; i < VW; ++i) {
+            const int gi_off = VW == 1 ? (int)(((h_lo + ho + i) / p.hpg - g_lo) * kT * kT) + sl : cbi[k];
+            const float cb = sCB[gi_off + r * kT];
+            const float e2 = (float)(sPq[r * HCp + ho + i] - pk[k][i]);
+            o[i] = cb * fast_exp2(e2) * bt[k][i];
+          }
+        }
+        if (VW == 4) __builtin_nontemporal_store(f32x4v{o[0], o[1 % VW], o[2 % VW], o[3 % VW]}, (f32x4v*)(orow + sl * H + ho));
+        else orow[sl * H + ho] = o[0];
       }
-      run[i] = r;
     }
   }
-  // above the diagonal: zeros
-  for (int64_t e = (t + 1) * H + tid; e < L * H; e += 256) out[e] = 0.f;
+}
+
+AttnPlan make_plan(const AttnArgs& a) {
+  AttnPlan p{};
+  p.hpg = a.H / a.G;
+  if (p.hpg <= kMaxHC) {
+    int64_t gpc = kMaxHC / p.hpg;
+    if (gpc > kMaxGPC) gpc = kMaxGPC;
+    if (gpc > a.G) gpc = a.G;
+    p.GPC = gpc;
+    p.HC = gpc * p.hpg;
+    p.cpg = 1;
+    p.nchunks = (a.G + gpc - 1) / gpc;
+  } else {
+    p.GPC = 1;
+    p.HC = kMaxHC;
+    p.cpg = (p.hpg + kMaxHC - 1) / kMaxHC;
+    p.nchunks = a.G * p.cpg;
+  }
+  p.nkt = (a.L + kT - 1) / kT;
+  p.nqr = (p.nkt + kRange - 1) / kRange;
+  return p;
+}
+
+size_t lds_bytes(const AttnPlan& p) {
+  return (size_t)kT * p.HC * sizeof(double) + (size_t)p.GPC * kT * kT * sizeof(float) +
+         (size_t)kT * kCP * sizeof(float) + (size_t)kKC * kT * sizeof(float);
+}
+
+// the largest plan: 128 heads and 8 groups per chunk
+constexpr size_t lds_bytes_max() {
+  return (size_t)kT * kMaxHC * sizeof(double) + (size_t)kMaxGPC * kT * kT * sizeof(float) +
+         (size_t)kT * kCP * sizeof(float) + (size_t)kKC * kT * sizeof(float);
+}
+
+// Dynamic LDS beyond 64 KiB (up to 81 KiB here, of the 160 KiB a gfx950
+// workgroup may hold) has to be allowed per kernel once.
+template <typename T, int VW>
+hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, unsigned items, size_t lds, hipStream_t s) {
+  static bool allowed = false;
+  if (lds > 65536 && !allowed) {
+    const hipError_t e = hipFuncSetAttribute((const void*)ssd_attention_kernel<T, VW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes_max());
+    if (e != hipSuccess) return e;
+    allowed = true;
+  }
+  hipLaunchKernelGGL((ssd_attention_kernel<T, VW>), dim3(items), dim3(256), lds, s, a, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 bool ssd_attention_supported(const AttnArgs& a) {
-  return a.H <= 256 * kMaxHeadsPerThread && a.G * a.N + a.G * kKeys <= 16384;  // 64 KiB of LDS
+  if (a.G <= 0 || a.H % a.G != 0) return false;
+  const AttnPlan p = make_plan(a);
+  const double items = (double)a.batch * (double)p.nchunks * (double)p.nkt * (double)p.nqr;
+  return items < 2147483647.0;
+}
+
+size_t ssd_attention_ws(const AttnArgs& a) {
+  return (size_t)a.batch * (size_t)a.L * (size_t)a.H * (sizeof(double) + sizeof(float));
 }
 
 hipError_t launch_ssd_attention(const AttnArgs& a, hipStream_t s) {
   if (a.batch == 0 || a.L == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.L, (unsigned)a.batch), blk(256);
-  const size_t lds = (size_t)(a.G * a.N + a.G * kKeys) * sizeof(float);
-  if (a.bf16) hipLaunchKernelGGL(ssd_attention_kernel<uint16_t>, grid, blk, lds, s, a);
-  else hipLaunchKernelGGL(ssd_attention_kernel<float>, grid, blk, lds, s, a);
-  return hipGetLastError();
+  const AttnPlan p = make_plan(a);
+  const unsigned items = (unsigned)(a.batch * p.nchunks * p.nkt * p.nqr);
+  const size_t lds = lds_bytes(p);
+  const bool vec = p.hpg % 4 == 0;
+  const unsigned pblocks = (unsigned)((a.batch * a.H + 3) / 4);
+  if (a.bf16) {
+    hipLaunchKernelGGL(attn_prefix_kernel<uint16_t>, dim3(pblocks), dim3(256), 0, s, a);
+    return vec ? launch_attn<uint16_t, 4>(a, p, items, lds, s) : launch_attn<uint16_t, 1>(a, p, items, lds, s);
+  }
+  hipLaunchKernelGGL(attn_prefix_kernel<float>, dim3(pblocks), dim3(256), 0, s, a);
+  return vec ? launch_attn<float, 4>(a, p, items, lds, s) : launch_attn<float, 1>(a, p, items, lds, s);
 }
 
 }  // namespace sscan

@@ -234,19 +234,78 @@ __device__ __forceinline__ void st_run(float* p, const float (&v)[NQ]) {
   }
 }
 
-// One token per call: four lanes per channel, lane q holding the contiguous
-// quarter [q NQ, q NQ + NQ) of its state_dim entries, so that a quad reads and
-// writes the channel's state as whole 16-byte pieces. The state is read,
-// updated, then y is read from the updated state ("Mamba", section "The
-// state"). The four partial read-outs are summed with a DPP butterfly inside the
-// quad, and lane 0 of the quad stores y. When state_dim is below the padded NP,
-// the entries are read one by one with a bound check.
+// Lanes per channel of the one-token step: 4 below 64 state entries, else 16.
+template <int NP>
+constexpr int step_lanes() { return NP >= 64 ? 16 : 4; }
+
+// Entry i of lane q. With 4 lanes a lane holds the contiguous quarter
+// [q NQ, q NQ + NQ); with 16 lanes it holds 4-entry pieces at 64 c + 4 q, so
+// that the 16 lanes of a channel read 256 contiguous bytes of fp32 state per
+// load instruction.
+template <int NP>
+__device__ __forceinline__ int step_entry(int q, int i) {
+  constexpr int K = step_lanes<NP>(), NQ = NP / K;
+  return K == 4 ? q * NQ + i : 64 * (i >> 2) + 4 * q + (i & 3);
+}
+
+// NQ entries of lane q from a row whose every entry is present (N == NP).
+template <int NP, typename E>
+__device__ __forceinline__ void step_ld(const E* row, int q, float (&o)[NP / step_lanes<NP>()]) {
+  constexpr int K = step_lanes<NP>(), NQ = NP / K;
+  if constexpr (K == 4) {
+    ld_run<NQ>(row + q * NQ, o);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NQ / 4; ++c) {
+      float t[4];
+      ld_run<4>(row + 64 * c + 4 * q, t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[4 * c + i] = t[i];
+    }
+  }
+}
+
+template <int NP>
+__device__ __forceinline__ void step_st(float* row, int q, const float (&v)[NP / step_lanes<NP>()]) {
+  constexpr int K = step_lanes<NP>(), NQ = NP / K;
+  if constexpr (K == 4) {
+    st_run<NQ>(row + q * NQ, v);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NQ / 4; ++c) {
+      const float t[4] = {v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+      st_run<4>(row + 64 * c + 4 * q, t);
+    }
+  }
+}
+
+// Sum over the K lanes of a channel (xor butterfly inside the lane group).
+template <int K>
+__device__ __forceinline__ float step_sum(float v) {
+  if constexpr (K == 4) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  } else {
+#pragma unroll
+    for (int off = K / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  }
+  return v;
+}
+
+// One token per call: K lanes per channel (step_lanes), each holding NP / K of
+// its state_dim entries (step_entry), so that a channel's state, A_log, B and C
+// move as whole pieces of 16 bytes or more. The state is read, updated, then y
+// is read from the updated state ("Mamba", section "The state"). The partial
+// read-outs are summed over the lane group, and its lane 0 stores y. When
+// state_dim is below the padded NP, the entries are read one by one with a
+// bound check.
 template <typename T, int NP, bool SSD, bool GATE>
 __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
-  constexpr int NQ = NP / 4;  // entries per lane
+  constexpr int K = step_lanes<NP>();
+  constexpr int NQ = NP / K;  // entries per lane
   const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q = (int)(gl & 3);
-  const int64_t c = gl >> 2;
+  const int q = (int)(gl % K);
+  const int64_t c = gl / K;
   const int64_t b = blockIdx.y;
   const bool active = c < k.Dc;
   const int64_t cc = active ? c : k.Dc - 1;  // inactive lanes compute on a valid channel, store nothing
@@ -255,17 +314,16 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
   const int64_t sidx = (b * k.Dc + cc) * k.N;
   const T* Bp = (const T*)k.B + (b * k.G + g) * k.N;
   const T* Cp = (const T*)k.C + (b * k.G + g) * k.N;
-  const int n0 = q * NQ;
   const bool full = k.N == NP;  // every entry present: rows are NP-aligned runs
   float bv[NQ], cv[NQ], hv[NQ];
   if (full) {
-    ld_run<NQ>(Bp + n0, bv);
-    ld_run<NQ>(Cp + n0, cv);
-    ld_run<NQ>(k.h0 + sidx + n0, hv);
+    step_ld<NP>(Bp, q, bv);
+    step_ld<NP>(Cp, q, cv);
+    step_ld<NP>(k.h0 + sidx, q, hv);
   } else {
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      const int n = n0 + i;
+      const int n = step_entry<NP>(q, i);
       bv[i] = n < k.N ? Act<T>::ld(Bp + n) : 0.0f;
       cv[i] = n < k.N ? Act<T>::ld(Cp + n) : 0.0f;
       hv[i] = n < k.N ? k.h0[sidx + n] : 0.0f;
@@ -279,21 +337,21 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
       sb = fmaf(bv[i], bv[i], sb);
       sc = fmaf(cv[i], cv[i], sc);
     }
-    // sum over the quad (lanes q = 0..3 of this channel)
-    sb += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sb), 0xB1, 0xF, 0xF, false));
-    sc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sc), 0xB1, 0xF, 0xF, false));
-    sb += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sb), 0x4E, 0xF, 0xF, false));
-    sc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sc), 0x4E, 0xF, 0xF, false));
+    sb = step_sum<K>(sb);
+    sc = step_sum<K>(sc);
     ib = 1.0f / sqrtf(sb / (float)k.N + k.bc_eps);
     ic = 1.0f / sqrtf(sc / (float)k.N + k.bc_eps);
   }
   float av[NQ];  // A_log of the entries (Mamba-1)
   if constexpr (!SSD) {
     if (full) {
-      ld_run<NQ>(k.A_log + cc * k.N + n0, av);
+      step_ld<NP>(k.A_log + cc * k.N, q, av);
     } else {
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) av[i] = n0 + i < k.N ? k.A_log[cc * k.N + n0 + i] : 0.0f;
+      for (int i = 0; i < NQ; ++i) {
+        const int n = step_entry<NP>(q, i);
+        av[i] = n < k.N ? k.A_log[cc * k.N + n] : 0.0f;
+      }
     }
   }
   const int64_t idx = b * k.Dc + cc;  // seqlen 1
@@ -310,18 +368,19 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
     h[i] = fmaf(dec, hv[i], dtx * (bv[i] * ib));
     acc = fmaf(cv[i] * ic, h[i], acc);
   }
-  acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
-  acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+  acc = step_sum<K>(acc);
   float yv = acc + k.D[hd] * xv;
   if (GATE) yv *= silu(Act<T>::ld((const T*)k.z + idx));
   if (active) {
     if (q == 0) Act<T>::st((T*)k.y + idx, yv);
     if (full) {
-      st_run<NQ>(k.h_out + sidx + n0, h);
+      step_st<NP>(k.h_out + sidx, q, h);
     } else {
 #pragma unroll
-      for (int i = 0; i < NQ; ++i)
-        if (n0 + i < k.N) k.h_out[sidx + n0 + i] = h[i];
+      for (int i = 0; i < NQ; ++i) {
+        const int n = step_entry<NP>(q, i);
+        if (n < k.N) k.h_out[sidx + n] = h[i];
+      }
     }
   }
 }
@@ -375,10 +434,13 @@ void dispatch_pass1(const TLK& k, int64_t batch, hipStream_t s) {
 
 template <typename T, bool SSD>
 void dispatch_step(const TLK& k, int64_t batch, bool gate, hipStream_t s) {
-  const dim3 grid((unsigned)((k.Dc * 4 + 255) / 256), (unsigned)batch), blk(256);
-#define SSCAN_STEP(NP)                                                                           \
-  if (gate) hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, true>), grid, blk, 0, s, k);   \
-  else hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, false>), grid, blk, 0, s, k);
+  const dim3 blk(256);
+#define SSCAN_STEP(NP)                                                                                   \
+  {                                                                                                      \
+    const dim3 grid((unsigned)((k.Dc * step_lanes<NP>() + 255) / 256), (unsigned)batch);                \
+    if (gate) hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, true>), grid, blk, 0, s, k);         \
+    else hipLaunchKernelGGL((tokenloop_step_kernel<T, NP, SSD, false>), grid, blk, 0, s, k);             \
+  }
   switch (padded_n(k.N)) {
     case 8: { SSCAN_STEP(8) break; }
     case 16: { SSCAN_STEP(16) break; }

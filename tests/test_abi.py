@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(bd.EXPORTS)
-    assert L.sscan_abi_version() == 1
+    assert L.sscan_abi_version() == 2
 
 
 def test_status_strings():
@@ -223,3 +223,24 @@ def test_conv_and_norm_errors():
     assert status(L.sscan_gated_rmsnorm(4, 0, 0, y, z, w, 1e-5, o, None)) == "SSCAN_ERR_SHAPE"
     assert status(L.sscan_gated_rmsnorm(4, 64, 5, y, z, w, 1e-5, o, None)) == "SSCAN_ERR_DTYPE"
     assert status(L.sscan_gated_rmsnorm(4, 64, 0, y, z, w, 1e-5, y, None)) == "SSCAN_ERR_ALIAS"
+
+
+def test_attention_workspace_and_pointers():
+    """sscan_ssd_attention: the workspace query, a missing or short workspace, host
+    pointers, and a workspace that overlaps the map, all refused before any launch."""
+    L = bd.lib()
+    h = Host()
+    b, Ln, H, N, G = 2, 40, 8, 16, 2
+    d = bd.SSDDesc(b, Ln, H, 1, N, G, 0, 0, 0)
+    need = L.sscan_ssd_attention_workspace_size(ctypes.byref(d))
+    assert need == b * Ln * H * 12
+    p = [h.buf(b * Ln * H * 4), h.buf(H * 4), h.buf(H * 4), h.buf(b * Ln * G * N * 4), h.buf(b * Ln * G * N * 4),
+         h.buf(b * Ln * Ln * H * 4)]
+    ws = h.buf(need)
+    assert status(L.sscan_ssd_attention(ctypes.byref(d), *p, None, 0, None)) == "SSCAN_ERR_WORKSPACE"
+    assert status(L.sscan_ssd_attention(ctypes.byref(d), *p, ws, need - 1, None)) == "SSCAN_ERR_WORKSPACE"
+    assert status(L.sscan_ssd_attention(ctypes.byref(d), *p, ws, need, None)) == "SSCAN_ERR_NOT_DEVICE"
+    assert status(L.sscan_ssd_attention(ctypes.byref(d), *p, p[5], need, None)) == "SSCAN_ERR_ALIAS"
+    bad = bd.SSDDesc(b, Ln, H, 1, N, 3, 0, 0, 0)   # 3 groups do not divide 8 heads
+    assert L.sscan_ssd_attention_workspace_size(ctypes.byref(bad)) == 0
+    assert status(L.sscan_ssd_attention(ctypes.byref(bad), *p, ws, need, None)) == "SSCAN_ERR_SHAPE"

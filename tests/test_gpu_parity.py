@@ -246,6 +246,8 @@ STEP_CASES = [
     (True, 2, 6, 3, 16, "bf16", True, 0.0),
     (True, 1, 5, 2, 64, "f32", False, 0.0),
     (True, 2, 4, 2, 128, "bf16", True, 0.0),
+    (True, 2, 4, 3, 128, "f32", True, 0.0),
+    (True, 1, 3, 2, 100, "bf16", False, 0.0),  # 100 of a padded 128: entry-wise, 16 lanes a channel
 ]
 
 
@@ -283,7 +285,10 @@ ATTN_CASES = [
     (2, 37, 4, 16, 2, "f32"),
     (1, 300, 3, 64, 1, "f32"),      # two blocks of keys
     (2, 129, 8, 128, 1, "bf16"),
-    (1, 520, 80, 128, 1, "bf16"),   # three blocks of keys, the 2.7B layer's heads
+    (1, 520, 80, 128, 1, "bf16"),   # the 2.7B layer's heads; 17 key tiles, ragged, long gaps
+    (1, 200, 128, 64, 8, "bf16"),   # 8 groups of 16 heads in one chunk
+    (1, 150, 40, 32, 20, "f32"),    # 2 heads per group: one value per lane, 3 chunks of groups
+    (1, 100, 300, 16, 1, "f32"),    # a group wider than a chunk: 128 + 128 + 44 heads
 ]
 
 
