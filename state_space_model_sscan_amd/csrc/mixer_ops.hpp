@@ -37,8 +37,8 @@ struct AttnArgs {
   const void* B;
   const void* C;
   float* alpha;
-  double* ws_P;     // [batch, L, H]: decays_0 + ... + decays_t, times log2(e)
-  float* ws_beta;   // [batch, L, H]: betas
+  double* ws_P;     // [batch, H, L]: decays_0 + ... + decays_t, times log2(e)
+  float* ws_beta;   // [batch, H, L]: betas
 };
 bool ssd_attention_supported(const AttnArgs& a);
 size_t ssd_attention_ws(const AttnArgs& a);

@@ -10,11 +10,12 @@
 // The map is [batch, t, s, heads] fp32: writing it is the whole cost, so the
 // work is shaped for the store stream.
 //
-// attn_prefix_kernel: one wave per (batch row, head) forms, in fp64,
+// attn_prefix_kernel: one workgroup per (batch row, head) forms, in fp64,
 //     P[t] = decays_0 + ... + decays_t     (times log2 e)
-// and betas_t into the caller's workspace. Each lane sums a contiguous run of
-// tokens, the runs' totals are scanned across the wave, and each lane then
-// rewalks its run from its offset. P is a sum of same-sign terms, so
+// and betas_t into the caller's workspace, head-major ([batch, head, token]).
+// Each thread sums a contiguous run of tokens, the runs' totals are scanned
+// across the workgroup, and each thread then rewalks its run from its offset.
+// P is a sum of same-sign terms, so
 // exponent(t, s) = P[t] - P[s] = decays_{s+1} + ... + decays_t is exact to
 // 2^-53 |P| in fp64, far below the fp32 result.
 //
@@ -54,19 +55,24 @@ struct AttnPlan {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kPrefixBatch = 16;  // dt loads in flight per lane
+constexpr int kPrefixBatch = 8;  // dt loads in flight per thread
 
+// One workgroup per (batch row, head): thread i sums the contiguous run of
+// tokens [i per, (i + 1) per), the run totals are scanned over the workgroup
+// (within each wave, then across the 4 waves through LDS), and each thread
+// rewalks its run from its offset, writing P and betas head-major, so that a
+// wave's stores are contiguous.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_prefix_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (batch row, head)
-  if (w >= a.batch * a.H) return;                                   // whole waves leave
-  const int64_t b = w / a.H, h = w % a.H;
+  __shared__ double wave_total[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t bh = blockIdx.x;  // batch row * H + head
+  const int64_t b = bh / a.H, h = bh % a.H;
   const float A = -expf(a.A_log[h]);
   const float bias = a.dt_bias[h];
   const T* dt = (const T*)a.dt + b * a.L * a.H + h;
-  const int64_t per = (a.L + 63) / 64;
-  const int64_t lo = min(a.L, lane * per), hi = min(a.L, lo + per);
+  const int64_t per = (a.L + 255) / 256;
+  const int64_t lo = min(a.L, tid * per), hi = min(a.L, lo + per);
   double sum = 0.0;
   for (int64_t j0 = lo; j0 < hi; j0 += kPrefixBatch) {
     float bv[kPrefixBatch];
@@ -76,17 +82,19 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < kPrefixBatch; ++u) sum += (double)bv[u] * (double)A;
   }
-  // inclusive scan of the runs' totals over the wave, then shifted by one lane
   double incl = sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double v = __shfl_up(incl, off, 64);
     if (lane >= off) incl += v;
   }
+  if (lane == 63) wave_total[wv] = incl;
   double P = __shfl_up(incl, 1, 64);
   if (lane == 0) P = 0.0;
-  double* wp = a.ws_P + b * a.L * a.H + h;
-  float* wb = a.ws_beta + b * a.L * a.H + h;
+  __syncthreads();
+  for (int q = 0; q < wv; ++q) P += wave_total[q];
+  double* wp = a.ws_P + bh * a.L;
+  float* wb = a.ws_beta + bh * a.L;
   for (int64_t j0 = lo; j0 < hi; j0 += kPrefixBatch) {
     float bv[kPrefixBatch];
 #pragma unroll
@@ -96,8 +104,8 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(AttnArgs a) {
     for (int u = 0; u < kPrefixBatch; ++u) {
       P += (double)bv[u] * (double)A;
       if (j0 + u < hi) {
-        wp[(j0 + u) * a.H] = P * kLog2eD;
-        wb[(j0 + u) * a.H] = bv[u];
+        wp[j0 + u] = P * kLog2eD;
+        wb[j0 + u] = bv[u];
       }
     }
   }
@@ -142,8 +150,8 @@ __global__ __launch_bounds__(256) void ssd_attention_kernel(AttnArgs a, AttnPlan
 
   const int nslot = kT * hc / VW;
   float* arow = a.alpha + (b * L) * L * H + h_lo;  // + (t * L + s) * H + head offset
-  const double* Pb = a.ws_P + b * L * H + h_lo;
-  const float* betab = a.ws_beta + b * L * H + h_lo;
+  const double* Pb = a.ws_P + (b * H + h_lo) * L;  // [head][token]
+  const float* betab = a.ws_beta + (b * H + h_lo) * L;
 
   double pk[SPT][VW];  // P at the slot's key
   float bt[SPT][VW];   // betas at the slot's key
@@ -157,8 +165,8 @@ __global__ __launch_bounds__(256) void ssd_attention_kernel(AttnArgs a, AttnPlan
       const bool ok = slot < nslot && s0 + sl < L;
 #pragma unroll
       for (int i = 0; i < VW; ++i) {
-        pk[k][i] = ok ? Pb[(s0 + sl) * H + ho + i] : 0.0;
-        bt[k][i] = ok ? betab[(s0 + sl) * H + ho + i] : 0.0f;
+        pk[k][i] = ok ? Pb[(ho + i) * L + s0 + sl] : 0.0;
+        bt[k][i] = ok ? betab[(ho + i) * L + s0 + sl] : 0.0f;
       }
       cbi[k] = (int)(((h_lo + ho) / p.hpg - g_lo) * kT * kT) + sl;
     }
@@ -183,8 +191,8 @@ __global__ __launch_bounds__(256) void ssd_attention_kernel(AttnArgs a, AttnPlan
     }
     __syncthreads();  // the previous tile's rows are written: sPq and sCB are free
     for (int e = tid; e < kT * hc; e += 256) {
-      const int r = e / hc, hh = e % hc;
-      sPq[r * HCp + hh] = r < nrow ? Pb[(t0 + r) * H + hh] : 0.0;
+      const int r = e % kT, hh = e / kT;
+      sPq[r * HCp + hh] = r < nrow ? Pb[hh * L + t0 + r] : 0.0;
     }
     // C_t . B_s for the tile, per group of the chunk
     {
@@ -305,7 +313,7 @@ bool ssd_attention_supported(const AttnArgs& a) {
   if (a.G <= 0 || a.H % a.G != 0) return false;
   const AttnPlan p = make_plan(a);
   const double items = (double)a.batch * (double)p.nchunks * (double)p.nkt * (double)p.nqr;
-  return items < 2147483647.0;
+  return items < 2147483647.0 && (double)a.batch * (double)a.H < 2147483647.0;
 }
 
 size_t ssd_attention_ws(const AttnArgs& a) {
@@ -318,7 +326,7 @@ hipError_t launch_ssd_attention(const AttnArgs& a, hipStream_t s) {
   const unsigned items = (unsigned)(a.batch * p.nchunks * p.nkt * p.nqr);
   const size_t lds = lds_bytes(p);
   const bool vec = p.hpg % 4 == 0;
-  const unsigned pblocks = (unsigned)((a.batch * a.H + 3) / 4);
+  const unsigned pblocks = (unsigned)(a.batch * a.H);
   if (a.bf16) {
     hipLaunchKernelGGL(attn_prefix_kernel<uint16_t>, dim3(pblocks), dim3(256), 0, s, a);
     return vec ? launch_attn<uint16_t, 4>(a, p, items, lds, s) : launch_attn<uint16_t, 1>(a, p, items, lds, s);
