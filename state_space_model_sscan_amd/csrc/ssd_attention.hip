@@ -30,6 +30,8 @@
 // registers, the tile's rows of P sit in LDS, and C_t . B_s for the tile comes
 // from a small LDS-staged product per group. Query tiles above the key tile
 // are zeros; on the diagonal tile the entries with s > t are zeros.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "mixer_ops.hpp"
 
@@ -293,15 +295,21 @@ constexpr size_t lds_bytes_max() {
 }
 
 // Dynamic LDS beyond 64 KiB (up to 81 KiB here, of the 160 KiB a gfx950
-// workgroup may hold) has to be allowed per kernel once.
+// workgroup may hold) has to be allowed per kernel, once on each device.
 template <typename T, int VW>
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, unsigned items, size_t lds, hipStream_t s) {
-  static bool allowed = false;
-  if (lds > 65536 && !allowed) {
-    const hipError_t e = hipFuncSetAttribute((const void*)ssd_attention_kernel<T, VW>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes_max());
+  static std::atomic<uint64_t> allowed{0};  // bit d: allowed on device d
+  if (lds > 65536) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    allowed = true;
+    const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+    if (!bit || !(allowed.load(std::memory_order_relaxed) & bit)) {
+      e = hipFuncSetAttribute((const void*)ssd_attention_kernel<T, VW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds_bytes_max());
+      if (e != hipSuccess) return e;
+      allowed.fetch_or(bit, std::memory_order_relaxed);
+    }
   }
   hipLaunchKernelGGL((ssd_attention_kernel<T, VW>), dim3(items), dim3(256), lds, s, a, p);
   return hipGetLastError();
