@@ -68,7 +68,9 @@ typedef enum {
 
 /* Mamba-1 problem. channels is the mixer's inner width (d_inner). ngroups must
  * divide channels; channel c reads group c / (channels / ngroups). When
- * ngroups > 1, channels / ngroups must be a multiple of 64. state_dim in 1..64.
+ * ngroups > 1, channels / ngroups must be a multiple of 64. state_dim in 1..128
+ * (up to 64 take the prompt kernels with 1 to 16 lanes per channel; 65..128 the
+ * one-lane-per-channel token loop, with the state in registers).
  * bc_rms_eps > 0 applies the weightless RMS norm b / sqrt(mean(b^2) + eps) to
  * every [state_dim] vector of B and of C before the scan ("Falcon-Mamba",
  * section "Where the norms sit"); <= 0 reads B and C as given. */

@@ -106,7 +106,7 @@ sscan_status check_mamba1_desc(const sscan_mamba1_desc* d, bool step) {
   if (d->channels % d->ngroups != 0) return fail(SSCAN_ERR_SHAPE, "ngroups must divide channels");
   if (step && d->seqlen != 1) return fail(SSCAN_ERR_SHAPE, "sscan_step needs seqlen == 1");
   if (d->act != SSCAN_F32 && d->act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
-  if (d->state_dim > 64) return fail(SSCAN_ERR_UNSUPPORTED, "Mamba-1 state_dim must be <= 64");
+  if (d->state_dim > 128) return fail(SSCAN_ERR_UNSUPPORTED, "Mamba-1 state_dim must be <= 128");
   if (d->ngroups > 1 && (d->channels / d->ngroups) % 64 != 0)
     return fail(SSCAN_ERR_UNSUPPORTED, "with ngroups > 1, channels / ngroups must be a multiple of 64");
   if (d->batch > 65535) return fail(SSCAN_ERR_UNSUPPORTED, "batch must be <= 65535");

@@ -86,7 +86,9 @@ static hipError_t zero_length(const float* h0, float* h_out, int64_t nst, hipStr
 Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t G, int64_t es) {
   // a batch row (of x/dt/z/y, or of B/C) that the 32-bit buffer offsets of the
   // fast kernels cannot span: token-loop kernel
-  if (L * Dc * es >= (int64_t(1) << 31) || L * G * N * es >= (int64_t(1) << 31)) {
+  // or more than 64 states (the fast kernels hold at most 64 per channel): the
+  // token-loop kernel
+  if (L * Dc * es >= (int64_t(1) << 31) || L * G * N * es >= (int64_t(1) << 31) || N > 64) {
     Mamba1Plan t = tokenloop_plan(batch, L, Dc, N);
     t.lanes_per_channel = 0;
     return t;

@@ -86,7 +86,7 @@ def test_null_descriptor():
     (dict(state_dim=0), "SSCAN_ERR_SHAPE"),
     (dict(ngroups=3), "SSCAN_ERR_SHAPE"),
     (dict(act=7), "SSCAN_ERR_DTYPE"),
-    (dict(state_dim=65), "SSCAN_ERR_UNSUPPORTED"),
+    (dict(state_dim=129), "SSCAN_ERR_UNSUPPORTED"),
     (dict(channels=192, ngroups=2), "SSCAN_ERR_UNSUPPORTED"),
     (dict(batch=70000), "SSCAN_ERR_UNSUPPORTED"),
 ])

@@ -42,6 +42,9 @@ M1_CASES = [
     (8, 77, 4096, 16, "f32", False, True, True, 1e-6),     # two lanes per channel
     (8, 45, 4096, 32, "f32", True, True, False, 0.0),      # 32 states, two lanes per channel
     (3, 333, 256, 64, "bf16", True, True, True, 0.0),      # 64 states, four lanes per channel
+    (2, 300, 64, 128, "bf16", True, True, True, 1e-6),     # 128 states: the token loop
+    (1, 129, 96, 100, "f32", True, False, False, 0.0),     # 100 of a padded 128
+    (1, 3000, 64, 128, "f32", True, True, False, 0.0),     # 128 states, several slices
 ]
 
 
@@ -247,6 +250,8 @@ STEP_CASES = [
     (True, 1, 5, 2, 64, "f32", False, 0.0),
     (True, 2, 4, 2, 128, "bf16", True, 0.0),
     (True, 2, 4, 3, 128, "f32", True, 0.0),
+    (False, 2, 4, 64, 128, "bf16", True, 1e-6),
+    (False, 1, 3, 32, 100, "f32", False, 0.0),
     (True, 1, 3, 2, 100, "bf16", False, 0.0),  # 100 of a padded 128: entry-wise, 16 lanes a channel
 ]
 
