@@ -11,7 +11,8 @@ HIP events on the stream the kernels are launched on. Beside the main line the
 run reports the Falcon-Mamba-7b-width Mamba-1 workload, the Mamba-2 2.7B SSD
 workload, the 512-call decode-step workload, the Mamba-2 decode step, the
 conv1d + silu and gated RMS norm around the Mamba-2 scan, the hidden attention
-map, and the fp64 CPU oracle timed on this host. Prints one JSON line.
+map, the SSD with per-token states, and the fp64 CPU oracle timed on this host.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -346,6 +347,30 @@ def bench_ssd_step(torch, bd, s4, nstates=32, calls=64):
                 hbm_frac=per_call / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
+def bench_ssd_states(steps, warmup, torch, bd, gen):
+    """sscan_ssd_fwd with per-token states at the Mamba2-130m mixer shape (24 heads x 64,
+    state 128, bf16) over one sequence of 512 tokens: the states [1, 512, 24, 64, 128] fp32
+    (403 MB) are the output that dominates."""
+    inp = gen.make_ssd(1, 512, 24, 64, 128, act="bf16", seed=130, gate=True, h0=True, want_states=True)
+    base = upload(inp, torch)
+    b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
+    y = torch.empty_like(base["x"])
+    h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    states = torch.empty((b, L, H, P, N), dtype=torch.float32, device="cuda")
+    ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def fn(_):
+        bd.sscan_ssd_fwd(base["x"], base["dt_raw"], base["dt_bias"], base["A_log"], base["B"], base["C"], base["D"],
+                         base["z"], base["state_input"], y=y, state_output=h, states=states, workspace=ws,
+                         chunk=inp.chunk)
+
+    wall, ev = time_calls(fn, [None], steps, warmup, torch)
+    nbytes = ssd_bytes(inp) + b * L * H * P * N * 4
+    return hbm_entry("mamba2-130m mixer with per-token states, bf16 1x512 tokens x 24 heads x 64, state 128",
+                     wall, ev, nbytes, tokens_per_s=b * L / (wall * 1e-3))
+
+
 def bench_attention(steps, warmup, torch, bd, s4, L=2048):
     """The hidden attention map of batch row 0's first L tokens of the Mamba-2 2.7B workload
     (80 heads, one group, state 128): alpha [1, L, L, 80] fp32, 1.34 GB written per call."""
@@ -437,6 +462,8 @@ def main():
         sst = bench_ssd_step(torch, bd, s4)
         log("bench: hidden attention map")
         att = bench_attention(max(5, args.steps // 10), 2, torch, bd, s4)
+        log("bench: SSD with per-token states")
+        sts = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
         extra = dict(
             mamba1_falcon_width={k: v for k, v in m3.items() if k != "inp"},
             ssd_mamba2_2p7b={k: v for k, v in s4.items() if k not in ("inp", "base")},
@@ -445,6 +472,7 @@ def main():
             conv1d_silu=conv_e,
             gated_rmsnorm=norm_e,
             ssd_attention_map=att,
+            ssd_per_token_states=sts,
         )
     cpu = None
     if not args.no_cpu_baseline:

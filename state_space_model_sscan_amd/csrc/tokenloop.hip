@@ -26,10 +26,11 @@ __global__ void copy_or_zero_kernel(const float* src, float* dst, int64_t n) {
 // Slices for the token-loop prompt scan (a pure function of the shape).
 Mamba1Plan tokenloop_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N) {
   Mamba1Plan p{1, L > 0 ? L : 1, 0, 1};
-  const int64_t waves = batch * ((Dc + 63) / 64);
+  const int64_t lanes = N > 32 ? 16 : 1;  // tokenloop_group_kernel above 32 states
+  const int64_t waves = batch * ((Dc * lanes + 63) / 64);
   const int64_t target = 2048;  // two waves per SIMD on 256 CUs x 4 SIMDs
   int64_t ns = waves > 0 ? (target + waves - 1) / waves : 1;
-  const int64_t max_ns = L / 128 > 1 ? L / 128 : 1;  // slices of at least 128 tokens
+  const int64_t max_ns = L / 64 > 1 ? L / 64 : 1;  // slices of at least 64 tokens
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
   if (ns > 1) {

@@ -155,9 +155,22 @@ __global__ __launch_bounds__(64) void tokenloop_scan_kernel(TLK k) {
           yv = fmaf(sC[i][n], h[n], yv);
         }
         if (STATES && active) {
+          if constexpr (NP % 4 == 0) {
+            if (k.N == NP) {  // whole 16-byte pieces: rows of N floats are 16-byte aligned
+              typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-          for (int n = 0; n < NP; ++n)
-            if (n < k.N) k.states[idx * k.N + n] = h[n];
+              for (int n = 0; n < NP; n += 4)
+                *(f32x4_t*)(k.states + idx * NP + n) = f32x4_t{h[n], h[n + 1], h[n + 2], h[n + 3]};
+            } else {
+#pragma unroll
+              for (int n = 0; n < NP; ++n)
+                if (n < k.N) k.states[idx * k.N + n] = h[n];
+            }
+          } else {
+#pragma unroll
+            for (int n = 0; n < NP; ++n)
+              if (n < k.N) k.states[idx * k.N + n] = h[n];
+          }
         }
         if (GATE) yv *= silu(Act<T>::ld(zp + idx));
         if (active) Act<T>::st(yp + idx, yv);
@@ -385,10 +398,219 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
   }
 }
 
+// Token loop for wide states (padded state_dim 64 or 128): 16 lanes per channel,
+// each holding the entries step_entry() gives it, 16 channels per 256-thread
+// block. One lane per channel would leave a 128-entry state in 256 registers,
+// a few waves on the chip and, with per-token states, 4-byte stores 512 bytes
+// apart; here the 16 lanes of a channel store 256 contiguous bytes per
+// instruction. Per tile of tokens the block stages B and C (fp32, normed when
+// asked) and, per channel, x, z and the step dt = softplus(dt_raw + dt_bias) in
+// LDS; the read-out is a sum over the 16 lanes. Slices and the carry between
+// them work as in tokenloop_scan_kernel, with the same workspace layout.
+constexpr int kGroupTile = 32;  // tokens per staging of the group kernel
+
+template <typename T, int NP, bool SSD, bool GATE, bool STATES, bool PASS1>
+__global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
+  constexpr int K = step_lanes<NP>();
+  static_assert(K == 16, "wide states only");
+  constexpr int NQ = NP / K;
+  constexpr int TILE = kGroupTile;
+  constexpr int CPB = 256 / K;  // channels per block
+  __shared__ __attribute__((aligned(16))) float sB[TILE][NP];
+  __shared__ __attribute__((aligned(16))) float sC[TILE][NP];
+  __shared__ float sX[TILE][CPB], sDT[TILE][CPB], sZ[TILE][CPB];
+  __shared__ float sNB[TILE], sNC[TILE];
+  const int tid = threadIdx.x;
+  const int q = tid % K, cl = tid / K;
+  const int64_t c0 = (int64_t)blockIdx.x * CPB;
+  const int64_t c = c0 + cl;
+  const bool active = c < k.Dc;
+  const int64_t cc = active ? c : k.Dc - 1;
+  const int s = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int64_t t_begin = (int64_t)s * k.slice_len;
+  const int64_t t_end = min(k.L, t_begin + (int64_t)k.slice_len);
+  const int g = (int)(c0 / k.per_group);  // the host guarantees one group per block
+  const int64_t hd = SSD ? cc / k.P : cc;
+  const bool full = k.N == NP;
+
+  float A2[SSD ? 1 : NQ], h[NQ];
+  if constexpr (SSD) {
+    A2[0] = -expf(k.A_log[hd]) * kLog2e;
+  } else {
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) {
+      const int n = step_entry<NP>(q, e);
+      A2[e] = n < k.N ? -expf(k.A_log[cc * k.N + n]) * kLog2e : 0.0f;
+    }
+  }
+  const int64_t sbase = (b * k.Dc + cc) * k.N;
+#pragma unroll
+  for (int e = 0; e < NQ; ++e) h[e] = 0.0f;
+  if (!PASS1 && k.h0) {
+    if (full) {
+      step_ld<NP>(k.h0 + sbase, q, h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < NQ; ++e) {
+        const int n = step_entry<NP>(q, e);
+        h[e] = n < k.N ? k.h0[sbase + n] : 0.0f;
+      }
+    }
+  }
+  if (!PASS1) {
+    for (int j = 0; j < s; ++j) {
+      const int64_t base = (b * k.nslices + j) * k.Dc + cc;
+      const float sdt = k.ws_sdt[base];
+      float wh[NQ];
+      if (full) {
+        step_ld<NP>(k.ws_h + base * NP, q, wh);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) {
+          const int n = step_entry<NP>(q, e);
+          wh[e] = n < k.N ? k.ws_h[base * k.N + n] : 0.0f;
+        }
+      }
+      const float dec0 = SSD ? fast_exp2(A2[0] * sdt) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < NQ; ++e) h[e] = fmaf(SSD ? dec0 : fast_exp2(A2[SSD ? 0 : e] * sdt), h[e], wh[e]);
+    }
+  }
+
+  const float Dv = PASS1 ? 0.0f : k.D[hd];
+  const T* xp = (const T*)k.x;
+  const T* dp = (const T*)k.dt;
+  const T* zp = (const T*)k.z;
+  T* yp = (T*)k.y;
+  const int64_t dt_stride = SSD ? k.H : k.Dc;
+  float sdt = 0.0f;
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TILE) {
+    const int nt = (int)min((int64_t)TILE, t_end - t0);
+    __syncthreads();  // the previous tile is consumed
+    for (int e = tid; e < TILE * NP; e += 256) {
+      const int t = e / NP, n = e % NP;
+      const int64_t row = b * k.L + t0 + t;
+      const bool ok = t < nt && n < k.N;
+      sB[t][n] = ok ? Act<T>::ld((const T*)k.B + (row * k.G + g) * k.N + n) : 0.0f;
+      if (!PASS1) sC[t][n] = ok ? Act<T>::ld((const T*)k.C + (row * k.G + g) * k.N + n) : 0.0f;
+    }
+    for (int e = tid; e < TILE * CPB; e += 256) {
+      const int t = e / CPB, ch = e % CPB;
+      const int64_t cx = min(c0 + ch, k.Dc - 1);
+      const int64_t row = b * k.L + t0 + t;
+      const int64_t hx = SSD ? cx / k.P : cx;
+      const bool ok = t < nt;
+      sX[t][ch] = ok ? Act<T>::ld(xp + row * k.Dc + cx) : 0.0f;
+      sDT[t][ch] = ok ? softplus(Act<T>::ld(dp + row * dt_stride + hx) + k.dt_bias[hx]) : 0.0f;
+      if (GATE && !PASS1) sZ[t][ch] = ok ? Act<T>::ld(zp + row * k.Dc + cx) : 0.0f;
+    }
+    __syncthreads();
+    if (k.bc_eps > 0.0f) {
+      if (tid < TILE) {
+        float sb = 0.0f, sc = 0.0f;
+        for (int n = 0; n < NP; ++n) {
+          sb = fmaf(sB[tid][n], sB[tid][n], sb);
+          if (!PASS1) sc = fmaf(sC[tid][n], sC[tid][n], sc);
+        }
+        sNB[tid] = 1.0f / sqrtf(sb / (float)k.N + k.bc_eps);
+        sNC[tid] = 1.0f / sqrtf(sc / (float)k.N + k.bc_eps);
+      }
+      __syncthreads();
+    }
+    for (int i = 0; i < nt; ++i) {
+      const float xv = sX[i][cl];
+      const float dtv = sDT[i][cl];
+      const float dtx = dtv * xv;
+      const float ib = k.bc_eps > 0.0f ? sNB[i] : 1.0f;
+      const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
+      float bv[NQ];
+      step_ld<NP>(&sB[i][0], q, bv);
+      if (PASS1) {
+        sdt += dtv;
+#pragma unroll
+        for (int e = 0; e < NQ; ++e)
+          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * (bv[e] * ib));
+      } else {
+        float cv[NQ];
+        step_ld<NP>(&sC[i][0], q, cv);
+        const float ic = k.bc_eps > 0.0f ? sNC[i] : 1.0f;
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) {
+          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * (bv[e] * ib));
+          acc = fmaf(cv[e] * ic, h[e], acc);
+        }
+        acc = step_sum<K>(acc);
+        const int64_t idx = (b * k.L + t0 + i) * k.Dc + cc;
+        if (STATES && active) {
+          if (full) {
+            step_st<NP>(k.states + idx * NP, q, h);
+          } else {
+#pragma unroll
+            for (int e = 0; e < NQ; ++e) {
+              const int n = step_entry<NP>(q, e);
+              if (n < k.N) k.states[idx * k.N + n] = h[e];
+            }
+          }
+        }
+        float yv = acc + Dv * xv;
+        if (GATE) yv *= silu(sZ[i][cl]);
+        if (active && q == 0) Act<T>::st(yp + idx, yv);
+      }
+    }
+  }
+
+  if (PASS1) {
+    if (active) {
+      const int64_t base = (b * k.nslices + s) * k.Dc + c;
+      if (full) {
+        step_st<NP>(k.ws_h + base * NP, q, h);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) {
+          const int n = step_entry<NP>(q, e);
+          if (n < k.N) k.ws_h[base * k.N + n] = h[e];
+        }
+      }
+      if (q == 0) k.ws_sdt[base] = sdt;
+    }
+  } else if (s == k.nslices - 1 && active) {
+    if (full) {
+      step_st<NP>(k.h_out + (b * k.Dc + c) * NP, q, h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < NQ; ++e) {
+        const int n = step_entry<NP>(q, e);
+        if (n < k.N) k.h_out[(b * k.Dc + c) * k.N + n] = h[e];
+      }
+    }
+  }
+}
+
 static int padded_n(int64_t N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : N <= 64 ? 64 : 128; }
 
 template <typename T, int NP, bool SSD>
 static void launch_scan(const TLK& k, int64_t batch, bool gate, bool states, hipStream_t s) {
+  if constexpr (NP >= 64) {  // wide states: 16 lanes per channel
+    const dim3 blk(256);
+    const int64_t cb = (k.Dc + 15) / 16;
+    if (k.nslices > 1) {
+      const dim3 grid1((unsigned)cb, (unsigned)(k.nslices - 1), (unsigned)batch);
+      hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, false, false, true>), grid1, blk, 0, s, k);
+    }
+    const dim3 grid((unsigned)cb, (unsigned)k.nslices, (unsigned)batch);
+    if (gate && states)
+      hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, true, true, false>), grid, blk, 0, s, k);
+    else if (gate)
+      hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, true, false, false>), grid, blk, 0, s, k);
+    else if (states)
+      hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, false, true, false>), grid, blk, 0, s, k);
+    else
+      hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, false, false, false>), grid, blk, 0, s, k);
+    return;
+  }
   const dim3 blk(64);
   const int64_t cb = (k.Dc + 63) / 64;
   if (k.nslices > 1) {
