@@ -176,6 +176,9 @@ SSD_CASES = [
     (1, 300, 3, 32, 64, 1, "f32", True, True, False),
     (1, 700, 2, 64, 16, 1, "bf16", False, False, False),
     (1, 2100, 2, 64, 128, 1, "bf16", True, True, False),
+    (2, 300, 4, 32, 128, 2, "f32", True, True, True),    # token loop, 16 lanes a channel: groups, slices, states
+    (1, 150, 2, 64, 100, 1, "bf16", True, True, True),   # 100 of a padded 128, slices, states
+    (1, 1100, 2, 128, 64, 1, "bf16", True, True, False), # head_dim 128: the token loop
 ]
 
 
