@@ -609,23 +609,23 @@ static void launch_scan(const TLK& k, int64_t batch, bool gate, bool states, hip
       hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, false, true, false>), grid, blk, 0, s, k);
     else
       hipLaunchKernelGGL((tokenloop_group_kernel<T, NP, SSD, false, false, false>), grid, blk, 0, s, k);
-    return;
+  } else {  // one lane per channel
+    const dim3 blk(64);
+    const int64_t cb = (k.Dc + 63) / 64;
+    if (k.nslices > 1) {
+      const dim3 grid1((unsigned)cb, (unsigned)(k.nslices - 1), (unsigned)batch);
+      hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, true>), grid1, blk, 0, s, k);
+    }
+    const dim3 grid((unsigned)cb, (unsigned)k.nslices, (unsigned)batch);
+    if (gate && states)
+      hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, true, true, false>), grid, blk, 0, s, k);
+    else if (gate)
+      hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, true, false, false>), grid, blk, 0, s, k);
+    else if (states)
+      hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, true, false>), grid, blk, 0, s, k);
+    else
+      hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, false>), grid, blk, 0, s, k);
   }
-  const dim3 blk(64);
-  const int64_t cb = (k.Dc + 63) / 64;
-  if (k.nslices > 1) {
-    const dim3 grid1((unsigned)cb, (unsigned)(k.nslices - 1), (unsigned)batch);
-    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, true>), grid1, blk, 0, s, k);
-  }
-  const dim3 grid((unsigned)cb, (unsigned)k.nslices, (unsigned)batch);
-  if (gate && states)
-    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, true, true, false>), grid, blk, 0, s, k);
-  else if (gate)
-    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, true, false, false>), grid, blk, 0, s, k);
-  else if (states)
-    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, true, false>), grid, blk, 0, s, k);
-  else
-    hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, false>), grid, blk, 0, s, k);
 }
 
 template <typename T, bool SSD>
@@ -644,12 +644,11 @@ template <typename T, bool SSD>
 void dispatch_pass1(const TLK& k, int64_t batch, hipStream_t s) {
   const dim3 grid1((unsigned)((k.Dc + 63) / 64), (unsigned)(k.nslices - 1), (unsigned)batch), blk(64);
 #define SSCAN_P1(NP) hipLaunchKernelGGL((tokenloop_scan_kernel<T, NP, SSD, false, false, true>), grid1, blk, 0, s, k);
-  switch (padded_n(k.N)) {
+  switch (padded_n(k.N)) {  // the fast Mamba-1 kernels it serves take state_dim <= 64
     case 8: { SSCAN_P1(8) break; }
     case 16: { SSCAN_P1(16) break; }
     case 32: { SSCAN_P1(32) break; }
-    case 64: { SSCAN_P1(64) break; }
-    default: { SSCAN_P1(128) break; }
+    default: { SSCAN_P1(64) break; }
   }
 #undef SSCAN_P1
 }
