@@ -293,13 +293,14 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       pf.z[it] = __builtin_amdgcn_raw_buffer_load_b128(rZ, (int)(x_lane + it * 8 * xz_row), 0, 0);
   };
   // y of the previous chunk: sY (written by the epilogue in its layout) to memory
-  // as whole rows, through ry_prev (empty before the first chunk: no stores)
+  // as whole rows, through ry_prev (empty before the first chunk: no stores);
+  // non-temporal (y is not read again here; measured about 1% faster)
   __amdgpu_buffer_rsrc_t ry_prev = rsrc(k.y, 0);
   auto store_y = [&]() {
 #pragma unroll
     for (int it = 0; it < 2; ++it)
       __builtin_amdgcn_raw_buffer_store_b128(lds128(sY + (x_r + 8 * it) * LDX + x_p * 8), ry_prev,
-                                             (int)(x_lane + it * 8 * xz_row), 0, 0);
+                                             (int)(x_lane + it * 8 * xz_row), 0, 2);
   };
 
   // The current item: chain (b, h) of group g, chunks [c, c_end); per-head constants.
