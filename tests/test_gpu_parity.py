@@ -287,6 +287,25 @@ def test_step_chain_shapes(case):
     check(host(state), hr, act, "state (steps)")
 
 
+@pytest.mark.parametrize("G", [2, 8])
+def test_ssd_step_with_groups(G):
+    """Mamba-2 decode steps with several B/C groups (Codestral's 8 groups of 16 heads
+    at G = 8): head h reads group h // (H / G)."""
+    H = 16
+    inp = gen.make_ssd(2, 3, H, 64, 128, G, act="bf16", seed=40 + G, gate=True, h0=True)
+    say("ssd step groups", G)
+    yr, hr, _ = oracle.run_inputs(inp)
+    state = par(inp.h0).clone()
+    ys = []
+    for t in range(inp.seqlen):
+        one = lambda a: dev(a[:, t:t + 1], "bf16")
+        y1, _ = bd.sscan_ssd_step(state, one(inp.x), one(inp.dt_raw), par(inp.dt_bias), par(inp.A_log), one(inp.B),
+                                  one(inp.C), par(inp.D), one(inp.z), state_output=state)
+        ys.append(host(y1))
+    check(np.concatenate(ys, 1), yr, "bf16", "y (steps)")
+    check(host(state), hr, "bf16", "state (steps)")
+
+
 ATTN_CASES = [
     # batch, seqlen, heads, N, groups, act
     (1, 1, 2, 16, 1, "f32"),
