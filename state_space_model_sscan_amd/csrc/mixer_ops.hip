@@ -65,6 +65,8 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(ConvArgs a) {
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // 16 bytes of a row as fp32 values: 4 fp32 or 8 bf16 (little-endian pairs).
+// Stores are non-temporal: the outputs are not read again by these kernels
+// (measured 3-4% faster on both streams).
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
   static constexpr int n = 4;
@@ -74,7 +76,7 @@ template <> struct Vec16<float> {
     for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
   }
   static __device__ __forceinline__ void st(float* p, const float* v) {
-    *(v4u*)p = v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_nontemporal_store(v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}, (v4u*)p);
   }
 };
 template <> struct Vec16<uint16_t> {
@@ -91,7 +93,7 @@ template <> struct Vec16<uint16_t> {
     v4u r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-    *(v4u*)p = r;
+    __builtin_nontemporal_store(r, (v4u*)p);
   }
 };
 
