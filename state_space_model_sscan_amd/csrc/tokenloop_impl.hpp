@@ -545,8 +545,12 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
         acc = step_sum<K>(acc);
         const int64_t idx = (b * k.L + t0 + i) * k.Dc + cc;
         if (STATES && active) {
-          if (full) {
-            step_st<NP>(k.states + idx * NP, q, h);
+          if (full) {  // non-temporal: the per-token states are not read again here
+            typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int c4 = 0; c4 < NQ / 4; ++c4)
+              __builtin_nontemporal_store(f32x4_t{h[4 * c4], h[4 * c4 + 1], h[4 * c4 + 2], h[4 * c4 + 3]},
+                                          (f32x4_t*)(k.states + idx * NP + 64 * c4 + 4 * q));
           } else {
 #pragma unroll
             for (int e = 0; e < NQ; ++e) {
