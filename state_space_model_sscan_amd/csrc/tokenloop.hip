@@ -28,7 +28,9 @@ Mamba1Plan tokenloop_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N) {
   Mamba1Plan p{1, L > 0 ? L : 1, 0, 1};
   const int64_t lanes = N > 32 ? 16 : 1;  // tokenloop_group_kernel above 32 states
   const int64_t waves = batch * ((Dc * lanes + 63) / 64);
-  const int64_t target = 2048;  // two waves per SIMD on 256 CUs x 4 SIMDs
+  // two waves per SIMD on 256 CUs x 4 SIMDs; four for the 16-lane kernel, whose
+  // slices are short enough that more of them shorten both passes
+  const int64_t target = lanes == 16 ? 4096 : 2048;
   int64_t ns = waves > 0 ? (target + waves - 1) / waves : 1;
   const int64_t max_ns = L / 64 > 1 ? L / 64 : 1;  // slices of at least 64 tokens
   if (ns > max_ns) ns = max_ns;
