@@ -449,3 +449,62 @@ def test_decode_steps_replayed_from_a_hip_graph():
     yr, hr, _ = oracle.run_inputs(inp)
     check(host(eager_y), yr, "f32", "y (steps)")
     check(host(eager_h), hr, "f32", "state (steps)")
+
+
+def test_prompt_entry_points_replayed_from_a_hip_graph():
+    """The prompt paths captured together into one HIP graph and replayed three times,
+    with eager work between the replays: the SSD chunk kernel (its work queues and the
+    flags of segments handing the state on are cleared by a kernel inside the graph),
+    the sliced Mamba-1 scan, conv1d + silu, the gated norm and the attention map. Every
+    replay must give the eager run's bits."""
+    s = gen.make_ssd(1, 2048, 8, 64, 128, act="bf16", seed=61, gate=True, h0=True)
+    m = gen.make_mamba1(1, 3000, 64, 16, act="f32", seed=62, gate=True, h0=True)
+    sx, sdt, sB, sC, sz = (dev(a, "bf16") for a in (s.x, s.dt_raw, s.B, s.C, s.z))
+    mx, mdt, mB, mC, mz = (dev(a, "f32") for a in (m.x, m.dt_raw, m.B, m.C, m.z))
+    s_par = [par(a) for a in (s.dt_bias, s.A_log, s.D, s.h0)]
+    m_par = [par(a) for a in (m.dt_bias, m.A_log, m.D, m.h0)]
+    s_ws = torch.empty(max(bd.sscan_ssd_workspace_size(bd.ssd_desc(sx, sB)), 1), dtype=torch.uint8, device="cuda")
+    m_ws = torch.empty(max(bd.sscan_mamba1_workspace_size(bd.mamba1_desc(mx, mB)), 1), dtype=torch.uint8,
+                       device="cuda")
+    a_ws = torch.empty(1 * 512 * 8 * 12, dtype=torch.uint8, device="cuda")
+    sy, sh = torch.empty_like(sx), torch.empty_like(s_par[3])
+    my, mh = torch.empty_like(mx), torch.empty_like(m_par[3])
+    w = par(np.linspace(-0.5, 0.5, 64 * 4, dtype=np.float32).reshape(64, 4))
+    cy, cst = torch.empty_like(mx), torch.empty((1, 64, 3), dtype=torch.float32, device="cuda")
+    ny = torch.empty_like(sx.view(1, 2048, 512))
+    nw = par(np.linspace(0.5, 1.5, 512, dtype=np.float32))
+    alpha = torch.empty((1, 512, 512, 8), dtype=torch.float32, device="cuda")
+    sdt5, sB5, sC5 = sdt[:, :512].contiguous(), sB[:, :512].contiguous(), sC[:, :512].contiguous()
+    outs = [sy, sh, my, mh, cy, cst, ny, alpha]
+
+    def run():
+        bd.sscan_ssd_fwd(sx, sdt, s_par[0], s_par[1], sB, sC, s_par[2], sz, s_par[3], y=sy, state_output=sh,
+                         workspace=s_ws)
+        bd.sscan_mamba1_fwd(mx, mdt, m_par[0], m_par[1], mB, mC, m_par[2], mz, m_par[3], y=my, state_output=mh,
+                            workspace=m_ws)
+        bd.sscan_conv1d_silu(mx, w, None, None, out=cy, conv_state_out=cst)
+        bd.sscan_gated_rmsnorm(sx.view(1, 2048, 512), sz.view(1, 2048, 512), nw, 1e-5, out=ny)
+        bd.sscan_ssd_attention(sdt5, s_par[0], s_par[1], sB5, sC5, alpha=alpha, workspace=a_ws)
+
+    say("graph of the prompt entry points")
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    prev = bd.set_pointer_checks(False)
+    g = torch.cuda.CUDAGraph()
+    try:
+        with torch.cuda.graph(g):
+            run()
+    finally:
+        bd.set_pointer_checks(prev)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(7.0)         # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), (rep, i)
+    yr, hr, _ = oracle.run_inputs(s)
+    check(host(eager[0]), yr, "bf16", "ssd y")
+    check(host(eager[1]), hr, "bf16", "ssd state")
