@@ -16,10 +16,13 @@
 // A_h = -exp(A_log[h]), shared by every p and n; D per head. The stored state
 // [b, H, P, N] is [b, channels, N] with channels = H*P.
 //
-// Mapping: one lane per channel, its state_dim entries in registers; one wave
-// (64 lanes) per block of 64 channels of one batch row. B and C of a token are
-// shared by every channel of the group, so the wave stages them (fp32, normed)
-// in LDS once per tile of tokens and every lane reads them by broadcast.
+// Mapping, up to 32 states (tokenloop_scan_kernel): one lane per channel, its
+// state_dim entries in registers; one wave (64 lanes) per block of 64 channels
+// of one batch row. B and C of a token are shared by every channel of the
+// group, so the wave stages them (fp32, normed) in LDS once per tile of tokens
+// and every lane reads them by broadcast. From 33 states up
+// (tokenloop_group_kernel, below): 16 lanes per channel. The one-token decode
+// step (tokenloop_step_kernel) uses 4 or 16 lanes per channel.
 // exp(dt*A) is computed as exp2(dt * A*log2(e)) with A*log2(e) kept per lane.
 //
 // Sequence parallelism: the tokens of a batch row are cut into `nslices`
