@@ -37,7 +37,8 @@
  *     sscan_step and sscan_ssd_step may update the state in place
  *     (state_output == state_input).
  *   - Thread-safe: the only global state is a thread-local error string and the
- *     process-wide pointer-check switch (an atomic, see sscan_set_pointer_checks).
+ *     process-wide switches of sscan_set_pointer_checks and sscan_set_tuning
+ *     (atomics).
  */
 #ifndef SSCAN_H
 #define SSCAN_H
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCAN_ABI_VERSION 2
+#define SSCAN_ABI_VERSION 3
 
 typedef enum { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
 
@@ -68,9 +69,10 @@ typedef enum {
 
 /* Mamba-1 problem. channels is the mixer's inner width (d_inner). ngroups must
  * divide channels; channel c reads group c / (channels / ngroups). When
- * ngroups > 1, channels / ngroups must be a multiple of 64. state_dim in 1..128
- * (up to 64 take the prompt kernels with 1 to 16 lanes per channel; 65..128 the
- * one-lane-per-channel token loop, with the state in registers).
+ * ngroups > 1, channels / ngroups must be a multiple of 64. state_dim in 1..256:
+ * 16, 32 or 64 with channels a multiple of 4 take the prompt kernel with a
+ * 16-lane row per channel; other state_dim up to 64 the one with 1, 2 or 4 lanes
+ * per channel; 65..256 the token loop with 16 lanes per channel.
  * bc_rms_eps > 0 applies the weightless RMS norm b / sqrt(mean(b^2) + eps) to
  * every [state_dim] vector of B and of C before the scan ("Falcon-Mamba",
  * section "Where the norms sit"); <= 0 reads B and C as given. */
@@ -128,6 +130,12 @@ sscan_status sscan_step(const sscan_mamba1_desc* desc, const float* state_input,
 /* Bytes of workspace sscan_ssd_fwd needs for this problem (0 if none). */
 size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
 
+/* Byte offset, in the workspace of an sscan_ssd_fwd call that takes the MFMA
+ * chunk path (act bf16, head_dim 64, state_dim 128, states NULL), of a 32-bit
+ * word that is 0 after the call unless a state hand-off between two segments of
+ * a head's sequence gave up waiting (see sscan_ssd_fwd). */
+#define SSCAN_SSD_GIVEUP_WORD_OFFSET 512
+
 /* Mamba-2 SSD scan over a prompt ("Mamba-2", sections "The mixer's values",
  * "The block, in order", "The hidden attention" and "The state").
  *   x, z          [batch, seqlen, nheads, head_dim] act (z NULL: no gate)
@@ -139,7 +147,14 @@ size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
  *   state_output  [batch, nheads, head_dim, state_dim] f32 (out)
  *   states        [batch, seqlen, nheads, head_dim, state_dim] f32 (out) or NULL
  * The state is stored value side (head_dim) first and state_dim innermost: entry
- * [b, h, p, n] is the pages' [b, h, key n, value p]. */
+ * [b, h, p, n] is the pages' [b, h, key n, value p]. state_dim in 1..128.
+ * The MFMA chunk path cuts a head's sequence into segments that different
+ * workgroups scan, each handing its final state to the next through the
+ * workspace. The kernel's own scheduling guarantees every hand-off wait ends;
+ * its bound exists only so that the kernel always terminates. A wait that gives
+ * up sets the word at SSCAN_SSD_GIVEUP_WORD_OFFSET and starts its segment from a
+ * NaN state, so every output that depends on the missing hand-off (the rest of
+ * that head's y, and its state_output) is NaN, never silently wrong. */
 sscan_status sscan_ssd_fwd(const sscan_ssd_desc* desc, const void* x, const void* dt_raw,
                            const float* dt_bias, const float* A_log, const void* B, const void* C,
                            const float* D, const void* z, const float* state_input, void* y,
@@ -218,6 +233,22 @@ int sscan_abi_version(void);
  * (hipPointerGetAttributes); 0: skip that check (shape, alignment and alias
  * checks still run). Process-wide; returns the previous setting. */
 int sscan_set_pointer_checks(int enabled);
+
+/* Tuning and test overrides of the launch plans. Process-wide (atomics), read
+ * when a call plans its launch; value 0 restores the library's own choice.
+ * Returns the previous value, or -1 (and changes nothing) for an unknown knob or
+ * a negative value. A knob changed between a *_workspace_size query and the
+ * call it sizes can change the workspace the call needs: the call then returns
+ * SSCAN_ERR_WORKSPACE instead of launching. */
+typedef enum {
+  SSCAN_TUNE_M1_LANES = 1,          /* lanes per channel of the Mamba-1 prompt kernels: 1, 2, 4 or 16
+                                       (others, and shapes the kernel cannot take, are ignored) */
+  SSCAN_TUNE_SSD_SEGMENT_CHUNKS = 2, /* chunks per segment of the SSD chunk path */
+  SSCAN_TUNE_SSD_WORKGROUPS = 3,    /* workgroups of the SSD chunk path */
+  SSCAN_TUNE_SSD_GIVE_UP = 4        /* nonzero: every state hand-off wait of the SSD chunk path gives
+                                       up at once (for testing what a wait that gives up does) */
+} sscan_tune_knob;
+int64_t sscan_set_tuning(int knob, int64_t value);
 
 #ifdef __cplusplus
 }

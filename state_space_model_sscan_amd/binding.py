@@ -22,7 +22,12 @@ STATUS_NAMES = ["SSCAN_OK", "SSCAN_ERR_NULL", "SSCAN_ERR_SHAPE", "SSCAN_ERR_DTYP
 EXPORTS = ["sscan_mamba1_workspace_size", "sscan_mamba1_fwd", "sscan_step", "sscan_ssd_workspace_size",
            "sscan_ssd_fwd", "sscan_ssd_step", "sscan_ssd_attention_workspace_size", "sscan_ssd_attention", "sscan_conv1d_silu", "sscan_gated_rmsnorm",
            "sscan_status_string",
-           "sscan_last_error", "sscan_abi_version", "sscan_set_pointer_checks"]
+           "sscan_last_error", "sscan_abi_version", "sscan_set_pointer_checks", "sscan_set_tuning"]
+
+# Knobs of sscan_set_tuning (include/sscan.h).
+TUNE_M1_LANES, TUNE_SSD_SEGMENT_CHUNKS, TUNE_SSD_WORKGROUPS, TUNE_SSD_GIVE_UP = 1, 2, 3, 4
+# Byte offset of the give-up word in the workspace of an SSD call on the MFMA chunk path.
+SSD_GIVEUP_WORD_OFFSET = 512
 
 
 class Mamba1Desc(ctypes.Structure):
@@ -93,6 +98,8 @@ def lib():
     L.sscan_abi_version.restype = I
     L.sscan_set_pointer_checks.argtypes = [I]
     L.sscan_set_pointer_checks.restype = I
+    L.sscan_set_tuning.argtypes = [I, ctypes.c_int64]
+    L.sscan_set_tuning.restype = ctypes.c_int64
     _lib = L
     return L
 
@@ -104,6 +111,21 @@ def check(status: int):
 
 def set_pointer_checks(enabled: bool) -> bool:
     return bool(lib().sscan_set_pointer_checks(1 if enabled else 0))
+
+
+def set_tuning(knob: int, value: int) -> int:
+    """Set a process-wide launch-plan override (0: the library's choice); returns the previous value."""
+    prev = int(lib().sscan_set_tuning(int(knob), int(value)))
+    if prev < 0:
+        raise ValueError("unknown tuning knob %r or negative value %r" % (knob, value))
+    return prev
+
+
+def _shape(name, t, shape):
+    """The C ABI cannot see buffer sizes: every tensor's shape is checked here, before the call."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
 
 
 def _act_code(t: torch.Tensor) -> int:
@@ -160,6 +182,30 @@ def sscan_ssd_workspace_size(desc: SSDDesc) -> int:
     return int(lib().sscan_ssd_workspace_size(ctypes.byref(desc)))
 
 
+def _check_mamba1(b, L, Dc, N, G, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output):
+    for n, t, sh in (("dt_raw", dt_raw, (b, L, Dc)), ("dt_bias", dt_bias, (Dc,)), ("A_log", A_log, (Dc, N)),
+                     ("B", B, (b, L, G, N)), ("C", C, (b, L, G, N)), ("D", D, (Dc,)), ("z", z, (b, L, Dc)),
+                     ("state_input", state_input, (b, Dc, N)), ("y", y, (b, L, Dc)),
+                     ("state_output", state_output, (b, Dc, N))):
+        _shape(n, t, sh)
+    _same("y", y, x.dtype)
+    _f32("state_output", state_output)
+
+
+def _check_ssd(b, L, H, P, N, G, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output):
+    for n, t, sh in (("dt_raw", dt_raw, (b, L, H)), ("dt_bias", dt_bias, (H,)), ("A_log", A_log, (H,)),
+                     ("B", B, (b, L, G, N)), ("C", C, (b, L, G, N)), ("D", D, (H,)), ("z", z, (b, L, H, P)),
+                     ("state_input", state_input, (b, H, P, N)), ("y", y, (b, L, H, P)),
+                     ("state_output", state_output, (b, H, P, N))):
+        _shape(n, t, sh)
+    _same("y", y, x.dtype)
+    _f32("state_output", state_output)
+
+
+def _workspace_bytes(workspace):
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
+
+
 def sscan_mamba1_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, y=None,
                      state_output=None, states=None, workspace=None, bc_rms_eps=0.0, want_states=False,
                      stream=None):
@@ -171,7 +217,10 @@ def sscan_mamba1_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=Non
     for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
         _f32(n, t)
     b, L, Dc = x.shape
-    N = B.shape[3]
+    G, N = B.shape[2], B.shape[3]
+    _check_mamba1(b, L, Dc, N, G, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output)
+    _shape("states", states, (b, L, Dc, N))
+    _f32("states", states)
     if y is None:
         y = torch.empty_like(x)
     if state_output is None:
@@ -181,7 +230,7 @@ def sscan_mamba1_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=Non
     ws_bytes = sscan_mamba1_workspace_size(desc)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wb = _workspace_bytes(workspace)
     check(lib().sscan_mamba1_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B),
                                  _ptr(C), _ptr(D), _ptr(z), _ptr(state_input), _ptr(y), _ptr(state_output),
                                  _ptr(states), _ptr(workspace), wb, _stream(stream)))
@@ -197,6 +246,13 @@ def sscan_step(state_input, x, dt_raw, dt_bias, A_log, B, C, D, z=None, y=None, 
         _same(n, t, x.dtype)
     for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
         _f32(n, t)
+    if state_input is None:
+        raise ValueError("sscan_step needs state_input")
+    b, L, Dc = x.shape
+    if L != 1:
+        raise ValueError("sscan_step takes one token: x must be [b, 1, channels]")
+    _check_mamba1(b, 1, Dc, B.shape[3], B.shape[2], x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y,
+                  state_output)
     if y is None:
         y = torch.empty_like(x)
     if state_output is None:
@@ -217,7 +273,10 @@ def sscan_ssd_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, 
     for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
         _f32(n, t)
     b, L, H, P = x.shape
-    N = B.shape[3]
+    G, N = B.shape[2], B.shape[3]
+    _check_ssd(b, L, H, P, N, G, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output)
+    _shape("states", states, (b, L, H, P, N))
+    _f32("states", states)
     if y is None:
         y = torch.empty_like(x)
     if state_output is None:
@@ -227,7 +286,7 @@ def sscan_ssd_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, 
     ws_bytes = sscan_ssd_workspace_size(desc)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wb = _workspace_bytes(workspace)
     check(lib().sscan_ssd_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B),
                               _ptr(C), _ptr(D), _ptr(z), _ptr(state_input), _ptr(y), _ptr(state_output),
                               _ptr(states), _ptr(workspace), wb, _stream(stream)))
@@ -242,6 +301,13 @@ def sscan_ssd_step(state_input, x, dt_raw, dt_bias, A_log, B, C, D, z=None, y=No
         _same(n, t, x.dtype)
     for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
         _f32(n, t)
+    if state_input is None:
+        raise ValueError("sscan_ssd_step needs state_input")
+    b, L, H, P = x.shape
+    if L != 1:
+        raise ValueError("sscan_ssd_step takes one token: x must be [b, 1, heads, head_dim]")
+    _check_ssd(b, 1, H, P, B.shape[3], B.shape[2], x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y,
+               state_output)
     if y is None:
         y = torch.empty_like(x)
     if state_output is None:
@@ -262,6 +328,10 @@ def sscan_ssd_attention(dt_raw, dt_bias, A_log, B, C, alpha=None, workspace=None
         _f32(n, t)
     b, L, H = dt_raw.shape
     G, N = B.shape[2], B.shape[3]
+    for n, t, sh in (("dt_bias", dt_bias, (H,)), ("A_log", A_log, (H,)), ("B", B, (b, L, G, N)),
+                     ("C", C, (b, L, G, N)), ("alpha", alpha, (b, L, L, H))):
+        _shape(n, t, sh)
+    _f32("alpha", alpha)
     desc = SSDDesc(b, L, H, 1, N, G, 0, _act_code(dt_raw), 0)
     if alpha is None:
         alpha = torch.empty((b, L, L, H), dtype=torch.float32, device=dt_raw.device)
@@ -280,8 +350,13 @@ def sscan_conv1d_silu(x, weight, bias=None, conv_state_in=None, out=None, conv_s
     conv state [b, Dc, W-1] f32. Returns (out, conv_state_out or None)."""
     b, L, Dc = x.shape
     W = weight.shape[1]
-    for n, t in (("weight", weight), ("bias", bias), ("conv_state_in", conv_state_in)):
+    for n, t in (("weight", weight), ("bias", bias), ("conv_state_in", conv_state_in),
+                 ("conv_state_out", conv_state_out)):
         _f32(n, t)
+    for n, t, sh in (("weight", weight, (Dc, W)), ("bias", bias, (Dc,)), ("conv_state_in", conv_state_in,
+                     (b, Dc, W - 1)), ("out", out, (b, L, Dc)), ("conv_state_out", conv_state_out, (b, Dc, W - 1))):
+        _shape(n, t, sh)
+    _same("out", out, x.dtype)
     desc = ConvDesc(b, L, Dc, W, _act_code(x), 0)
     if out is None:
         out = torch.empty_like(x)
@@ -295,7 +370,11 @@ def sscan_conv1d_silu(x, weight, bias=None, conv_state_in=None, out=None, conv_s
 def sscan_gated_rmsnorm(y, z, weight, eps, out=None, stream=None):
     """out = (y * silu(z)) / sqrt(mean over the last axis + eps) * weight. y, z: [..., width]."""
     _same("z", z, y.dtype)
+    _same("out", out, y.dtype)
     _f32("weight", weight)
+    _shape("z", z, y.shape)
+    _shape("out", out, y.shape)
+    _shape("weight", weight, (y.shape[-1],))
     width = y.shape[-1]
     rows = y.numel() // width if width else 0
     if out is None:

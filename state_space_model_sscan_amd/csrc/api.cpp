@@ -16,6 +16,7 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<int> g_pointer_checks{1};
+std::atomic<int64_t> g_knobs[sscan::kKnobCount];  // zero-initialised: every knob at the library's choice
 
 sscan_status fail(sscan_status st, const char* fmt, ...) {
   char buf[512];
@@ -106,7 +107,7 @@ sscan_status check_mamba1_desc(const sscan_mamba1_desc* d, bool step) {
   if (d->channels % d->ngroups != 0) return fail(SSCAN_ERR_SHAPE, "ngroups must divide channels");
   if (step && d->seqlen != 1) return fail(SSCAN_ERR_SHAPE, "sscan_step needs seqlen == 1");
   if (d->act != SSCAN_F32 && d->act != SSCAN_BF16) return fail(SSCAN_ERR_DTYPE, "act must be F32 or BF16");
-  if (d->state_dim > 128) return fail(SSCAN_ERR_UNSUPPORTED, "Mamba-1 state_dim must be <= 128");
+  if (d->state_dim > 256) return fail(SSCAN_ERR_UNSUPPORTED, "Mamba-1 state_dim must be <= 256");
   if (d->ngroups > 1 && (d->channels / d->ngroups) % 64 != 0)
     return fail(SSCAN_ERR_UNSUPPORTED, "with ngroups > 1, channels / ngroups must be a multiple of 64");
   if (d->batch > 65535) return fail(SSCAN_ERR_UNSUPPORTED, "batch must be <= 65535");
@@ -144,11 +145,20 @@ sscan::SSDArgs ssd_args(const sscan_ssd_desc* d) {
 
 }  // namespace
 
+int64_t sscan::knob(int which) {
+  return which > 0 && which < kKnobCount ? g_knobs[which].load(std::memory_order_relaxed) : 0;
+}
+
 extern "C" {
 
 int sscan_abi_version(void) { return SSCAN_ABI_VERSION; }
 
 int sscan_set_pointer_checks(int enabled) { return g_pointer_checks.exchange(enabled ? 1 : 0); }
+
+int64_t sscan_set_tuning(int knob, int64_t value) {
+  if (knob <= 0 || knob >= sscan::kKnobCount || value < 0) return -1;
+  return g_knobs[knob].exchange(value);
+}
 
 const char* sscan_last_error(void) { return g_last_error.c_str(); }
 

@@ -6,6 +6,17 @@
 
 namespace sscan {
 
+// Process-wide tuning and test overrides (sscan_set_tuning in sscan.h), read
+// when a launch is planned. 0 means the library's own choice.
+enum Knob {
+  kKnobM1Lanes = 1,          // lanes per channel of the Mamba-1 prompt kernel: 1, 2, 4 or 16
+  kKnobSsdSegmentChunks = 2, // chunks per segment of the SSD chunk kernel
+  kKnobSsdWorkgroups = 3,    // workgroups of the SSD chunk kernel
+  kKnobSsdGiveUp = 4,        // nonzero: every state hand-off wait of the chunk kernel gives up at once
+  kKnobCount = 5
+};
+int64_t knob(int which);
+
 struct Mamba1Args {
   int64_t batch, L, Dc, N, G;
   bool bf16;

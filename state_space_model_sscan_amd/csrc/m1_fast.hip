@@ -1,6 +1,4 @@
 // m1_fast.hip -- host launch of the Mamba-1 prompt kernel (m1_fast_impl.hpp).
-#include <cstdlib>
-
 #include "m1_row_impl.hpp"
 
 namespace sscan {
@@ -33,15 +31,7 @@ hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const flo
   if (K == 16) {  // a 16-lane row per channel, 16 channels per 256-thread block
     const int64_t nb = ((a.Dc + 15) / 16) * plan.nslices * a.batch;
     const dim3 grid((unsigned)nb);
-    // Blocks per CU: unused dynamic LDS caps how many the dispatcher may stack
-    // on one CU, so that the grid spreads evenly over the 256 CUs.
-    size_t dyn = 0;
-    if (const char* e = getenv("SSCAN_M1_BPC")) {
-      const int bpc = atoi(e);
-      const size_t stat = (size_t)2 * 2 * np * 68 * 4;
-      const size_t want = (160 * 1024) / (bpc + 1) + 1024;
-      if (bpc > 0 && want > stat) dyn = want - stat;
-    }
+    const size_t dyn = 0;
     if (a.bf16) {
       if (np == 16) launch_m1_row_np<uint16_t, 16>(k, gate, st, grid, dyn, s);
       else if (np == 32) launch_m1_row_np<uint16_t, 32>(k, gate, st, grid, dyn, s);

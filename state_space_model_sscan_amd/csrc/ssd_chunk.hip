@@ -59,8 +59,7 @@
 // consecutive rows. So within each 8 tokens k0..k0+7 the MFMA k order is
 // 0, 2, 4, 6, 1, 3, 5, 7 (kperm); the other operands follow it: w is stored in
 // that order and the masked M with its columns permuted the same way.
-#include <stdlib.h>
-#include <string.h>
+#include <math.h>
 
 #include <algorithm>
 
@@ -204,7 +203,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   __shared__ __attribute__((aligned(16))) uint16_t sZ[Q * LDX];  // z of the chunk
   __shared__ __attribute__((aligned(16))) uint16_t sY[Q * LDX];  // y of the chunk, stored after the next barrier
   __shared__ __attribute__((aligned(16))) float sCS[Q], sDT[Q], sW[Q], sE[Q];
-  __shared__ int sTicket[2];  // [0]: the first item; [1]: the item after the current one
+  __shared__ int sTicket[3];  // [0]: the first item; [1]: the item after the current one;
+                              // [2]: the current item's hand-off wait gave up
 
   // the wave index through readfirstlane: a scalar, so branches on it stay uniform
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, li = l & 15,
@@ -360,7 +360,10 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   // so. The producer of that segment holds an item dequeued earlier than this
   // one, so it is running and never waits on this workgroup: the wait ends. Its
   // bound (2^20 polls, about a second) only guarantees that the kernel
-  // terminates; a wait that gives up raises queue[128], which ends every other.
+  // terminates; a wait that gives up raises queue[128], which ends every other
+  // wait, and starts its item from a NaN state: every output that depends on a
+  // hand-off that did not happen (the rest of that chain's y and its final
+  // state) comes out NaN rather than silently wrong.
   // carry and the flags move through device-coherent loads and stores (the sc1
   // cache policy, as device-scope atomics use), which need no cache write-back
   // or invalidation (either would flush the L2 that the other workgroups share);
@@ -371,20 +374,26 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     if (seg > 0) {
       if (tid == 0) {
         unsigned* flag = kargs()->queue + 256 + ch;
-        bool done = false;
-        for (int n = 0; n < (1 << 20) && !done; ++n) {
-          done = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg ||
-                 __hip_atomic_load(kargs()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-          if (!done) __builtin_amdgcn_s_sleep(2);
+        bool ready = false, quit = false;
+        for (int n = 0; n < (1 << 20) && !ready && !quit; ++n) {
+          ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg;
+          quit = !ready && __hip_atomic_load(kargs()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+          if (!ready && !quit) __builtin_amdgcn_s_sleep(2);
         }
-        if (!done) __hip_atomic_store(kargs()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!ready) __hip_atomic_store(kargs()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sTicket[2] = ready ? 0 : 1;
       }
       __syncthreads();
-      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + ch * (P * NS), P * NS * 4);
+      if (__builtin_amdgcn_readfirstlane(sTicket[2]) != 0) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        hacc[nt] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
+        for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{NAN, NAN, NAN, NAN};
+      } else {
+        const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + ch * (P * NS), P * NS * 4);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          hacc[nt] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
+      }
     } else if (kargs()->h0) {
       const float* src = kargs()->h0 + ch * (P * NS) + s_lane;
 #pragma unroll
@@ -650,9 +659,11 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 }
 
 // Zeroes the queue counters, the give-up word and the per-chain flags (a kernel, not a memset, so
-// that the call can be captured in a graph).
-__global__ void ssd_queue_reset(unsigned* q, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) q[i] = 0;
+// that the call can be captured in a graph). give_up != 0 raises the give-up word instead, so that
+// every hand-off wait ends at once (the test of what a wait that gives up does to the outputs).
+__global__ void ssd_queue_reset(unsigned* q, int n, unsigned give_up) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    q[i] = i == 128 ? give_up : 0u;
 }
 
 namespace {
@@ -699,17 +710,13 @@ SsdPlan ssd_plan(const SSDArgs& a) {
       }
     }
   }
-  // tuning override "chunks per segment[,workgroups]"
-  if (const char* e = getenv("SSCAN_SSD_SEGMENT")) {
-    const int64_t sc = atoll(e);
-    const char* comma = strchr(e, ',');
-    if (sc > 0) {
-      best_seg = std::min(sc, nchunks);
-      best_ns = (nchunks + best_seg - 1) / best_seg;
-      if (best_ns * nchains >= (int64_t(1) << 30)) best_seg = nchunks, best_ns = 1;
-    }
-    if (comma && atoll(comma + 1) > 0) grid = std::min<int64_t>(atoll(comma + 1), 1 << 20);
+  // tuning overrides: chunks per segment, workgroups
+  if (const int64_t sc = knob(kKnobSsdSegmentChunks); sc > 0) {
+    best_seg = std::min(sc, nchunks);
+    best_ns = (nchunks + best_seg - 1) / best_seg;
+    if (best_ns * nchains >= (int64_t(1) << 30)) best_seg = nchunks, best_ns = 1;
   }
+  if (const int64_t wg = knob(kKnobSsdWorkgroups); wg > 0) grid = std::min<int64_t>(wg, 1 << 20);
   p.seg_chunks = (int)best_seg;
   p.nseg = (int)best_ns;
   p.nq = (int)queues(grid);
@@ -745,7 +752,7 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
   const int nwords = 256 + p.nchains;
   hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nwords + 255) / 256)), dim3(256), 0, s, k.queue,
-                     nwords);
+                     nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
   hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
   return hipGetLastError();
 }

@@ -1,7 +1,5 @@
 // tokenloop.hip -- host side of the token-loop scan: slicing plan and launches.
 // The kernels are in tokenloop_impl.hpp, instantiated in tl_*.hip.
-#include <cstdlib>
-
 #include "tokenloop_impl.hpp"
 
 namespace sscan {
@@ -104,8 +102,8 @@ Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t 
   int64_t K = N > 32 ? 2 : 1;  // 64 states in one lane would spill
   while (K < 4 && waves(K) < 2048) K *= 2;
   if (row_ok) K = 16;
-  if (const char* e = getenv("SSCAN_M1_LANES")) {  // tuning override: 1, 2, 4 or 16
-    const int64_t v = atoi(e);
+  {  // tuning override: 1, 2, 4 or 16 lanes per channel
+    const int64_t v = knob(kKnobM1Lanes);
     if ((v == 1 && N <= 32) || v == 2 || v == 4 || (v == 16 && row_ok)) K = v;
   }
   p.lanes_per_channel = K;

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
   }
 }
 
-// Token loop for wide states (padded state_dim 64 or 128): 16 lanes per channel,
+// Token loop for wide states (padded state_dim 64, 128 or 256): 16 lanes per channel,
 // each holding the entries step_entry() gives it, 16 channels per 256-thread
 // block. One lane per channel would leave a 128-entry state in 256 registers,
 // a few waves on the chip and, with per-token states, 4-byte stores 512 bytes
@@ -410,14 +410,16 @@ __global__ __launch_bounds__(256) void tokenloop_step_kernel(TLK k) {
 // asked) and, per channel, x, z and the step dt = softplus(dt_raw + dt_bias) in
 // LDS; the read-out is a sum over the 16 lanes. Slices and the carry between
 // them work as in tokenloop_scan_kernel, with the same workspace layout.
-constexpr int kGroupTile = 32;  // tokens per staging of the group kernel
+// Tokens per staging of the group kernel: 32, or 16 for 256 states (B and C of a
+// tile then take 32 KiB of LDS).
+template <int NP> constexpr int group_tile() { return NP >= 256 ? 16 : 32; }
 
 template <typename T, int NP, bool SSD, bool GATE, bool STATES, bool PASS1>
 __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
   constexpr int K = step_lanes<NP>();
   static_assert(K == 16, "wide states only");
   constexpr int NQ = NP / K;
-  constexpr int TILE = kGroupTile;
+  constexpr int TILE = group_tile<NP>();
   constexpr int CPB = 256 / K;  // channels per block
   __shared__ __attribute__((aligned(16))) float sB[TILE][NP];
   __shared__ __attribute__((aligned(16))) float sC[TILE][NP];
@@ -596,7 +598,9 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
   }
 }
 
-static int padded_n(int64_t N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : N <= 64 ? 64 : 128; }
+static int padded_n(int64_t N) {
+  return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
+}
 
 template <typename T, int NP, bool SSD>
 static void launch_scan(const TLK& k, int64_t batch, bool gate, bool states, hipStream_t s) {
@@ -642,7 +646,10 @@ void dispatch_scan(const TLK& k, int64_t batch, bool gate, bool states, hipStrea
     case 16: launch_scan<T, 16, SSD>(k, batch, gate, states, s); break;
     case 32: launch_scan<T, 32, SSD>(k, batch, gate, states, s); break;
     case 64: launch_scan<T, 64, SSD>(k, batch, gate, states, s); break;
-    default: launch_scan<T, 128, SSD>(k, batch, gate, states, s); break;
+    case 128: launch_scan<T, 128, SSD>(k, batch, gate, states, s); break;
+    default:  // 129 to 256 states: Mamba-1 only (the host refuses wider SSD states)
+      if constexpr (!SSD) launch_scan<T, 256, SSD>(k, batch, gate, states, s);
+      break;
   }
 }
 
@@ -674,7 +681,11 @@ void dispatch_step(const TLK& k, int64_t batch, bool gate, hipStream_t s) {
     case 16: { SSCAN_STEP(16) break; }
     case 32: { SSCAN_STEP(32) break; }
     case 64: { SSCAN_STEP(64) break; }
-    default: { SSCAN_STEP(128) break; }
+    case 128: { SSCAN_STEP(128) break; }
+    default: {  // Mamba-1 only, as in dispatch_scan
+      if constexpr (!SSD) SSCAN_STEP(256)
+      break;
+    }
   }
 #undef SSCAN_STEP
 }

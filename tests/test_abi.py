@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(bd.EXPORTS)
-    assert L.sscan_abi_version() == 2
+    assert L.sscan_abi_version() == 3
 
 
 def test_status_strings():
@@ -86,14 +86,14 @@ def test_null_descriptor():
     (dict(state_dim=0), "SSCAN_ERR_SHAPE"),
     (dict(ngroups=3), "SSCAN_ERR_SHAPE"),
     (dict(act=7), "SSCAN_ERR_DTYPE"),
-    (dict(state_dim=129), "SSCAN_ERR_UNSUPPORTED"),
+    (dict(state_dim=257), "SSCAN_ERR_UNSUPPORTED"),
     (dict(channels=192, ngroups=2), "SSCAN_ERR_UNSUPPORTED"),
     (dict(batch=70000), "SSCAN_ERR_UNSUPPORTED"),
 ])
 def test_mamba1_descriptor_errors(kw, want):
     h = Host()
     d = desc(**kw)
-    if d.batch >= 0 and d.channels > 0 and d.state_dim > 0 and d.batch < 70000:
+    if d.batch >= 0 and d.channels > 0 and 0 < d.state_dim <= 256 and d.batch < 70000:
         a = m1_args(h, d)
     else:
         a = m1_args(h, desc())
@@ -244,3 +244,101 @@ def test_attention_workspace_and_pointers():
     bad = bd.SSDDesc(b, Ln, H, 1, N, 3, 0, 0, 0)   # 3 groups do not divide 8 heads
     assert L.sscan_ssd_attention_workspace_size(ctypes.byref(bad)) == 0
     assert status(L.sscan_ssd_attention(ctypes.byref(bad), *p, ws, need, None)) == "SSCAN_ERR_SHAPE"
+
+
+def test_tuning_knobs_are_validated_and_restored():
+    L = bd.lib()
+    assert L.sscan_set_tuning(99, 1) == -1          # unknown knob: nothing changes
+    assert L.sscan_set_tuning(0, 1) == -1
+    assert L.sscan_set_tuning(bd.TUNE_M1_LANES, -2) == -1
+    assert bd.set_tuning(bd.TUNE_M1_LANES, 4) == 0
+    assert bd.set_tuning(bd.TUNE_M1_LANES, 0) == 4   # the previous value comes back
+    with pytest.raises(ValueError):
+        bd.set_tuning(42, 1)
+
+
+def test_launch_plans_are_stable_and_follow_the_knobs():
+    """The workspace queries are pure functions of the shape and the knobs: repeated
+    queries agree, a knob changes the plan only while it is set, and a call whose
+    workspace was sized under another setting is refused, not run."""
+    L = bd.lib()
+    m = desc(batch=1, seqlen=16384, channels=128)
+    # many heads, few chunks: the chunk path's workspace is the larger of the two SSD paths'
+    s = sdesc(batch=1, seqlen=256, nheads=400)
+    m0 = L.sscan_mamba1_workspace_size(ctypes.byref(m))
+    s0 = L.sscan_ssd_workspace_size(ctypes.byref(s))
+    for _ in range(3):
+        assert L.sscan_mamba1_workspace_size(ctypes.byref(m)) == m0
+        assert L.sscan_ssd_workspace_size(ctypes.byref(s)) == s0
+    # one segment per chain: no state hand-off buffer
+    bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 64)
+    try:
+        one = L.sscan_ssd_workspace_size(ctypes.byref(s))
+        bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 1)
+        many = L.sscan_ssd_workspace_size(ctypes.byref(s))
+        assert many == one + 400 * 64 * 128 * 4       # the hand-off states of 400 chains
+        # a workspace sized for one segment per chain is too small for one-chunk segments
+        h = Host()
+        b, Ln, H, P, N = 1, 256, 400, 64, 128
+        act = b * Ln * H * P * 2
+        ptrs = [h.buf(act), h.buf(b * Ln * H * 2), h.buf(H * 4), h.buf(H * 4), h.buf(b * Ln * N * 2),
+                h.buf(b * Ln * N * 2), h.buf(H * 4), None, None, h.buf(act), h.buf(b * H * P * N * 4), None,
+                h.buf(one)]
+        assert status(L.sscan_ssd_fwd(ctypes.byref(s), *ptrs, one, None)) == "SSCAN_ERR_WORKSPACE"
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 0)
+    assert L.sscan_ssd_workspace_size(ctypes.byref(s)) == s0
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float32)
+
+
+def test_binding_refuses_misshaped_tensors():
+    """The C ABI cannot see buffer sizes, so the binding checks every tensor's shape
+    and raises before anything reaches the library."""
+    import torch
+    b, L, Dc, N = 2, 8, 64, 16
+    ok = dict(x=_cpu(b, L, Dc), dt_raw=_cpu(b, L, Dc), dt_bias=_cpu(Dc), A_log=_cpu(Dc, N), B=_cpu(b, L, 1, N),
+              C=_cpu(b, L, 1, N), D=_cpu(Dc))
+    bad = [("dt_raw", _cpu(b, L, Dc + 1)), ("dt_bias", _cpu(Dc - 1)), ("A_log", _cpu(N, Dc)), ("C", _cpu(b, L, 1, 8)),
+           ("D", _cpu(1)), ("z", _cpu(b, L - 1, Dc)), ("state_input", _cpu(b, Dc, N + 1)), ("y", _cpu(b, L, Dc, 1)),
+           ("state_output", _cpu(b, N, Dc)), ("states", _cpu(b, L, Dc, 8))]
+    for name, t in bad:
+        kw = dict(ok)
+        kw[name] = t
+        with pytest.raises(ValueError, match=name):
+            bd.sscan_mamba1_fwd(**kw)
+    with pytest.raises(TypeError):
+        bd.sscan_mamba1_fwd(**ok, y=_cpu(b, L, Dc, dtype=torch.bfloat16))
+    # the decode step
+    one = dict(x=_cpu(b, 1, Dc), dt_raw=_cpu(b, 1, Dc), dt_bias=_cpu(Dc), A_log=_cpu(Dc, N), B=_cpu(b, 1, 1, N),
+               C=_cpu(b, 1, 1, N), D=_cpu(Dc))
+    with pytest.raises(ValueError, match="state_input"):
+        bd.sscan_step(_cpu(b, Dc, N - 1), **one)
+    with pytest.raises(ValueError, match="one token"):
+        bd.sscan_step(_cpu(b, Dc, N), **dict(one, x=_cpu(b, 2, Dc)))
+    # SSD
+    H, P, Ns = 4, 64, 128
+    s_ok = dict(x=_cpu(b, L, H, P), dt_raw=_cpu(b, L, H), dt_bias=_cpu(H), A_log=_cpu(H), B=_cpu(b, L, 1, Ns),
+                C=_cpu(b, L, 1, Ns), D=_cpu(H))
+    for name, t in [("dt_raw", _cpu(b, L, H, 1)), ("A_log", _cpu(H, 1)), ("z", _cpu(b, L, H, P + 1)),
+                    ("state_input", _cpu(b, H, Ns, P)), ("state_output", _cpu(b, H, Ns, P)),
+                    ("states", _cpu(b, L, H, P, 1))]:
+        with pytest.raises(ValueError, match=name):
+            bd.sscan_ssd_fwd(**dict(s_ok, **{name: t}))
+    with pytest.raises(ValueError, match="state_input"):
+        bd.sscan_ssd_step(_cpu(b, H, P, Ns + 1), **{k: (v[:, :1].contiguous() if k in ("x", "dt_raw", "B", "C") else v)
+                                                    for k, v in s_ok.items()})
+    # attention map, conv, norm
+    with pytest.raises(ValueError, match="alpha"):
+        bd.sscan_ssd_attention(_cpu(b, L, H), _cpu(H), _cpu(H), _cpu(b, L, 1, 16), _cpu(b, L, 1, 16), alpha=_cpu(b, L, L))
+    with pytest.raises(ValueError, match="weight"):
+        bd.sscan_conv1d_silu(_cpu(b, L, Dc), _cpu(Dc + 1, 4))
+    with pytest.raises(ValueError, match="conv_state_in"):
+        bd.sscan_conv1d_silu(_cpu(b, L, Dc), _cpu(Dc, 4), conv_state_in=_cpu(b, Dc, 4))
+    with pytest.raises(ValueError, match="z"):
+        bd.sscan_gated_rmsnorm(_cpu(4, 64), _cpu(4, 65), _cpu(64), 1e-5)
+    with pytest.raises(ValueError, match="weight"):
+        bd.sscan_gated_rmsnorm(_cpu(4, 64), _cpu(4, 64), _cpu(63), 1e-5)
