@@ -1,11 +1,10 @@
 """GPU parity of the steps next to the scan, the Mamba-2 decode step and the hidden
 attention map at the shapes the benchmark times (the Mamba-2 2.7B layer: batch 4,
 8192 tokens, 80 heads x 64, state 128, xBC width 5376), in the same launch
-configuration. Where the whole output is too large for the fp64 oracle, sampled
-parts are compared: channels of the depthwise conv (channels are independent),
-rows of the norm (rows are independent), and windows of the attention map (an
-entry alpha[t, s] depends only on tokens s..t, so the oracle's map of the
-subsequence [s1, t2) holds alpha[t, s] for s1 <= s <= t < t2)."""
+configuration. The conv, the norm and the decode step are compared whole. The
+attention map (1.3 GB of fp32 at 2048 tokens) is compared on windows: an entry
+alpha[t, s] depends only on tokens s..t, so the oracle's map of the subsequence
+[s1, t2) holds alpha[t, s] for s1 <= s <= t < t2."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +13,7 @@ import oracle
 from state_space_model_sscan_amd import binding as bd
 from state_space_model_sscan_amd import inputs as gen
 
-from _gpu import check, dev, host, par, say
+from _gpu import check, check_all, dev, host, par, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +25,8 @@ def _need_gpu():
     bd.lib()
 
 
-def test_conv1d_at_the_2p7b_xbc_shape_sampled_channels():
+@pytest.mark.timeout(600)
+def test_conv1d_at_the_2p7b_xbc_shape():
     b, L, Dc, W = 4, 8192, 5376, 4
     say("conv at", (b, L, Dc, W))
     g = torch.Generator(device="cuda")
@@ -37,16 +37,13 @@ def test_conv1d_at_the_2p7b_xbc_shape_sampled_channels():
     st = torch.randn((b, Dc, W - 1), generator=g, device="cuda")
     out, st_out = bd.sscan_conv1d_silu(x, w, bias, st)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    ch = np.sort(rng.choice(Dc, 48, replace=False))
-    ch = np.concatenate([ch, [0, 7, 8, Dc - 1]])   # edges of the 8-channel groups
-    ci = torch.from_numpy(ch).cuda()
-    ref, ref_st = oracle.conv1d_silu(host(x[:, :, ci]), host(w[ci]), host(bias[ci]), host(st[:, ci]))
-    check(host(out[:, :, ci]), ref, "bf16", "conv out (sampled channels)")
-    assert np.array_equal(host(st_out[:, ci]), ref_st.astype(np.float32).astype(np.float64))
+    ref, ref_st = oracle.conv1d_silu(host(x), host(w), host(bias), host(st))
+    check(host(out), ref, "bf16", "conv out", path="stream")
+    assert np.array_equal(host(st_out), ref_st.astype(np.float32).astype(np.float64))
 
 
-def test_gated_norm_at_the_2p7b_shape_sampled_rows():
+@pytest.mark.timeout(600)
+def test_gated_norm_at_the_2p7b_shape():
     rows, width = 4 * 8192, 5120
     say("gated norm at", (rows, width))
     g = torch.Generator(device="cuda")
@@ -56,10 +53,8 @@ def test_gated_norm_at_the_2p7b_shape_sampled_rows():
     wt = torch.rand((width,), generator=g, device="cuda") + 0.5
     out = bd.sscan_gated_rmsnorm(y, z, wt, 1e-5)
     torch.cuda.synchronize()
-    r = np.sort(np.random.default_rng(8).choice(rows, 64, replace=False))
-    r = torch.from_numpy(np.concatenate([r, [0, rows - 1]])).cuda()
-    ref = oracle.gated_rmsnorm(host(y[r]), host(z[r]), host(wt), 1e-5)
-    check(host(out[r]), ref, "bf16", "norm out (sampled rows)")
+    ref = oracle.gated_rmsnorm(host(y), host(z), host(wt), 1e-5)
+    check(host(out), ref, "bf16", "norm out", path="stream")
 
 
 def test_ssd_decode_step_at_the_2p7b_shape():
@@ -76,8 +71,7 @@ def test_ssd_decode_step_at_the_2p7b_shape():
                                  one(inp.C), par(inp.D), one(inp.z), state_output=state)
         ys.append(host(y))
     torch.cuda.synchronize()
-    check(np.concatenate(ys, 1), yr, "bf16", "y")
-    check(host(state), hr, "bf16", "state")
+    check_all(inp, (np.concatenate(ys, 1), host(state)), (yr, hr), "mamba1")
 
 
 def test_attention_map_at_2048_tokens_sampled_windows():
