@@ -161,6 +161,26 @@ sscan_status sscan_ssd_fwd(const sscan_ssd_desc* desc, const void* x, const void
                            float* state_output, float* states, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* sscan_ssd_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, and the same kernels and results. What the
+ * workspace would hold (the chunk path's work queues, give-up word and state
+ * hand-offs, or the token loop's slice carries) lives in the library's static
+ * device scratch of SSCAN_NOALLOC_SCRATCH_BYTES, which every GPU the library runs
+ * on holds from the first call until the process ends. A problem that needs more
+ * returns SSCAN_ERR_UNSUPPORTED before any launch (sscan_ssd_workspace_size
+ * gives the need). The call allocates nothing and frees nothing. Every call on
+ * one GPU shares that GPU's scratch, and the kernels clear what must start at
+ * zero, so calls that overlap in time on one GPU (several streams or threads)
+ * race and give wrong results; calls in sequence on one stream are safe. The
+ * give-up word (SSCAN_SSD_GIVEUP_WORD_OFFSET) is in the scratch, not visible to
+ * the caller; a give-up still turns the dependent outputs to NaN. */
+#define SSCAN_NOALLOC_SCRATCH_BYTES (16u << 20)
+sscan_status sscan_ssd_fwd_noalloc(const sscan_ssd_desc* desc, const void* x, const void* dt_raw,
+                                   const float* dt_bias, const float* A_log, const void* B, const void* C,
+                                   const float* D, const void* z, const float* state_input, void* y,
+                                   float* state_output, float* states, void* stream);
+
 /* Mamba-2 one-token decode step: sscan_ssd_fwd with seqlen 1, state_input
  * required, state_output may equal state_input ("Mamba-2", section "The state":
  * on a decode step the update comes before the read). */

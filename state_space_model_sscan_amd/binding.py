@@ -22,7 +22,8 @@ STATUS_NAMES = ["SSCAN_OK", "SSCAN_ERR_NULL", "SSCAN_ERR_SHAPE", "SSCAN_ERR_DTYP
 EXPORTS = ["sscan_mamba1_workspace_size", "sscan_mamba1_fwd", "sscan_step", "sscan_ssd_workspace_size",
            "sscan_ssd_fwd", "sscan_ssd_step", "sscan_ssd_attention_workspace_size", "sscan_ssd_attention", "sscan_conv1d_silu", "sscan_gated_rmsnorm",
            "sscan_status_string",
-           "sscan_last_error", "sscan_abi_version", "sscan_set_pointer_checks", "sscan_set_tuning"]
+           "sscan_last_error", "sscan_abi_version", "sscan_set_pointer_checks", "sscan_set_tuning",
+           "sscan_ssd_fwd_noalloc"]
 
 # Knobs of sscan_set_tuning (include/sscan.h).
 TUNE_M1_LANES, TUNE_SSD_SEGMENT_CHUNKS, TUNE_SSD_WORKGROUPS, TUNE_SSD_GIVE_UP = 1, 2, 3, 4
@@ -80,6 +81,8 @@ def lib():
     L.sscan_ssd_workspace_size.restype = S
     L.sscan_ssd_fwd.argtypes = [SD] + [P] * 13 + [S, P]
     L.sscan_ssd_fwd.restype = I
+    L.sscan_ssd_fwd_noalloc.argtypes = [SD] + [P] * 13
+    L.sscan_ssd_fwd_noalloc.restype = I
     L.sscan_ssd_step.argtypes = [SD] + [P] * 12
     L.sscan_ssd_step.restype = I
     L.sscan_ssd_attention_workspace_size.argtypes = [SD]
@@ -290,6 +293,31 @@ def sscan_ssd_fwd(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, 
     check(lib().sscan_ssd_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log), _ptr(B),
                               _ptr(C), _ptr(D), _ptr(z), _ptr(state_input), _ptr(y), _ptr(state_output),
                               _ptr(states), _ptr(workspace), wb, _stream(stream)))
+    return y, state_output, states
+
+
+def sscan_ssd_fwd_noalloc(x, dt_raw, dt_bias, A_log, B, C, D, z=None, state_input=None, y=None,
+                          state_output=None, states=None, chunk=0, stream=None):
+    """sscan_ssd_fwd without a workspace: the library's static device scratch takes its
+    place (for callers that cannot allocate). Outputs are allocated here when not given.
+    Returns (y, state_output, states or None)."""
+    desc = ssd_desc(x, B, chunk)
+    for n, t in (("dt_raw", dt_raw), ("B", B), ("C", C), ("z", z)):
+        _same(n, t, x.dtype)
+    for n, t in (("dt_bias", dt_bias), ("A_log", A_log), ("D", D), ("state_input", state_input)):
+        _f32(n, t)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _check_ssd(b, L, H, P, N, G, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output)
+    _shape("states", states, (b, L, H, P, N))
+    _f32("states", states)
+    if y is None:
+        y = torch.empty_like(x)
+    if state_output is None:
+        state_output = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    check(lib().sscan_ssd_fwd_noalloc(ctypes.byref(desc), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A_log),
+                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(state_input), _ptr(y),
+                                      _ptr(state_output), _ptr(states), _stream(stream)))
     return y, state_output, states
 
 

@@ -269,10 +269,16 @@ size_t sscan_ssd_workspace_size(const sscan_ssd_desc* d) {
   return w;
 }
 
-sscan_status sscan_ssd_fwd(const sscan_ssd_desc* d, const void* x, const void* dt_raw, const float* dt_bias,
-                           const float* A_log, const void* B, const void* C, const float* D, const void* z,
-                           const float* state_input, void* y, float* state_output, float* states,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// sscan_ssd_fwd and sscan_ssd_fwd_noalloc: noalloc takes the library's static
+// device scratch instead of a caller's workspace.
+sscan_status ssd_fwd(const sscan_ssd_desc* d, const void* x, const void* dt_raw, const float* dt_bias,
+                     const float* A_log, const void* B, const void* C, const float* D, const void* z,
+                     const float* state_input, void* y, float* state_output, float* states, void* workspace,
+                     size_t workspace_bytes, void* stream, bool noalloc, const char* what) {
   sscan_status st = check_ssd_desc(d, false);
   if (st != SSCAN_OK) return st;
   sscan::SSDArgs a = ssd_args(d);
@@ -295,19 +301,48 @@ sscan_status sscan_ssd_fwd(const sscan_ssd_desc* d, const void* x, const void* d
       {"y", y, act_bytes, true},
       {"state_output", state_output, st_bytes, true},
       {"states", states, (size_t)(b * L * H * P * N) * 4, true},
-      {"workspace", workspace, need, true},
+      {"workspace", workspace, noalloc ? 0 : need, true},
   };
   const bool req[] = {true, true, true, true, true, true, true, false, false, true, true, false, true};
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (noalloc) {
+    if (need > sscan::kScratchBytes)
+      return fail(SSCAN_ERR_UNSUPPORTED, "this problem needs %zu bytes of scratch; the static scratch holds %zu",
+                  need, sscan::kScratchBytes);
+  } else if (need > 0 && (!workspace || workspace_bytes < need)) {
     return fail(SSCAN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
+  }
   st = check_buffers(bufs, 13, req, nullptr, nullptr);
   if (st != SSCAN_OK) return st;
+  if (noalloc && need > 0) {
+    const hipError_t e = sscan::scratch_ptr(&workspace);
+    if (e != hipSuccess) return hip_status(e, "the static scratch's device address");
+  }
   a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z;
   a.h0 = state_input; a.y = y; a.h_out = state_output; a.states = states;
   const hipError_t e = chunk ? sscan::launch_ssd_chunk(a, workspace, (hipStream_t)stream)
                              : sscan::launch_ssd_tokenloop(a, workspace, (hipStream_t)stream);
-  return hip_status(e, "sscan_ssd_fwd launch");
+  return hip_status(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+sscan_status sscan_ssd_fwd(const sscan_ssd_desc* d, const void* x, const void* dt_raw, const float* dt_bias,
+                           const float* A_log, const void* B, const void* C, const float* D, const void* z,
+                           const float* state_input, void* y, float* state_output, float* states,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_fwd(d, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output, states, workspace,
+                 workspace_bytes, stream, false, "sscan_ssd_fwd launch");
+}
+
+sscan_status sscan_ssd_fwd_noalloc(const sscan_ssd_desc* d, const void* x, const void* dt_raw, const float* dt_bias,
+                                   const float* A_log, const void* B, const void* C, const float* D, const void* z,
+                                   const float* state_input, void* y, float* state_output, float* states,
+                                   void* stream) {
+  return ssd_fwd(d, x, dt_raw, dt_bias, A_log, B, C, D, z, state_input, y, state_output, states, nullptr, 0, stream,
+                 true, "sscan_ssd_fwd_noalloc launch");
 }
 
 sscan_status sscan_ssd_step(const sscan_ssd_desc* d, const float* state_input, float* state_output, const void* x,

@@ -73,6 +73,11 @@ size_t ssd_tokenloop_ws(const SSDArgs& a);
 hipError_t launch_ssd_tokenloop(const SSDArgs& a, void* ws, hipStream_t s);
 hipError_t launch_ssd_step(const SSDArgs& a, hipStream_t s);
 
+// The static device scratch of the entry point that allocates nothing (scratch.hip):
+// its size, and its device address on the current device (looked up once per device).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_ptr(void** out);
+
 // MFMA chunk SSD (ssd_chunk.hip): bf16, head_dim 64, state_dim 128, no per-token states.
 bool ssd_chunk_supported(const SSDArgs& a);
 size_t ssd_chunk_ws(const SSDArgs& a);
