@@ -1,26 +1,40 @@
 """Benchmark of the selective scan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only-main]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-counters] [--only-main]
 
 A step is one sscan_mamba1_fwd over the Mamba-130m layer workload (batch 8,
 seq 2048, d_inner 1536, state_dim 16, bf16 activations, fp32 state, fused
 silu(z) gate). Inputs are resident in HBM when timing starts; three copies of
 them rotate so no step finds its inputs in the 256 MiB Infinity Cache. K steps
 are timed between two device synchronizations; each call is also bracketed by
-HIP events on the stream the kernels are launched on. Beside the main line the
-run reports the Falcon-Mamba-7b-width Mamba-1 workload, the Mamba-2 2.7B SSD
-workload, the 512-call decode-step workload, the Mamba-2 decode step, the
-conv1d + silu and gated RMS norm around the Mamba-2 scan, the hidden attention
-map, the SSD with per-token states, and the fp64 CPU oracle timed on this host.
-Prints one JSON line.
+HIP events on the stream the kernels are launched on (mean, median and minimum
+are reported). The Falcon-Mamba-7b-width Mamba-1 workload and the Mamba-2 2.7B
+SSD workload get blocks of their own with the same roofline and CPU-baseline
+fields; beside them the decode steps, the conv1d + silu and gated RMS norm
+around the Mamba-2 scan, the hidden attention map and the SSD with per-token
+states are reported.
+
+Roofline: every scan is HBM-bound by its arithmetic intensity; `achieved` is the
+workload's algorithmic bytes (every input read once, every output written once)
+over the kernel time, against the 8 TB/s peak. `traffic` is what the hardware
+counters saw: before any GPU work of its own, the bench runs itself under
+rocprofv3 as a child (--counter-child) in four counter passes (FETCH_SIZE;
+WRITE_SIZE; VALU instruction and busy counters; MFMA counters) and scales the
+byte counters by what they read for a plain elementwise kernel that reads and
+writes 1 GiB. The SSD block adds the MFMA FLOPs those counters count. The CPU
+baseline is the fp64 oracle on bounded samples of the same workloads, timed on
+this host's cores (also on one core for the main workload). Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
+import csv
+import glob
 import json
 import os
-import re
+import shutil
+import signal
+import subprocess
 import sys
 import time
 
@@ -31,67 +45,29 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
-# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one fp32 op per lane per
-# slot; v_exp_f32 takes two slots). Peak in T lane-slots/s.
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+MFMA_FLOPS_PER_MOP = 512         # SQ_INSTS_VALU_MFMA_MOPS_* counts units of 512 FLOPs
 METRIC = "scan tokens/s & % HBM roofline (Mamba-1); SSD tokens/s & % MFMA peak"
-MAIN_KERNEL = "m1_row_kernel<bf16, 16 states, gate> (a 16-lane row per channel)"
-# sources of the main kernel: HBM traffic from hardware counters is reported only
-# while these hash to the value recorded with the counters
-MAIN_KERNEL_SOURCES = ["state_space_model_sscan_amd/csrc/m1_row_impl.hpp",
-                       "state_space_model_sscan_amd/csrc/m1_fast_impl.hpp",
-                       "state_space_model_sscan_amd/csrc/m1_fast.hip",
-                       "state_space_model_sscan_amd/csrc/m1r_bf16_16.hip",
-                       "state_space_model_sscan_amd/csrc/device_common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
-
-
-def sources_hash(paths):
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def recorded_traffic(kernel_key):
-    """HBM bytes per launch measured by FETCH_SIZE/WRITE_SIZE (scaled by a plain copy's
-    reading), from the counter summary in profiles/, if it is for the current source."""
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    m = re.search(r"```json\n(.*?)\n```", text, re.S)
-    if not m:
-        return None
-    rec = json.loads(m.group(1)).get(kernel_key)
-    if not rec or rec.get("sources_sha256_16") != sources_hash(rec.get("sources", [])):
-        return None
-    return rec
+MAIN = 1
+BLOCKS = (3, 4)                  # the other throughput workloads, with blocks of their own
+# Repetitions per workload in the counter child: distinct counts let the parent
+# tell the dispatches of each workload apart in the counter records.
+COUNTER_REPS = {1: 7, 3: 9, 4: 11}
+CALIB_REPS = 13
+COUNTER_PASSES = [
+    ("read", ["FETCH_SIZE"]),
+    ("write", ["WRITE_SIZE"]),
+    ("valu", ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+              "SQ_WAIT_INST_ANY", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]),
+    ("mfma", ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]),
+]
+NUM_CU, NUM_XCD = 256, 8
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def upload(inp, torch):
-    def act(a):
-        if a is None:
-            return None
-        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
-        return (t.to(torch.bfloat16) if inp.act == "bf16" else t).cuda()
-
-    def par(a):
-        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
-
-    return dict(x=act(inp.x), dt_raw=act(inp.dt_raw), B=act(inp.B), C=act(inp.C), z=act(inp.z),
-                dt_bias=par(inp.dt_bias), A_log=par(inp.A_log), D=par(inp.D), state_input=par(inp.h0))
-
-
-def clone_set(d):
-    return {k: (None if v is None else v.clone()) for k, v in d.items()}
-
-
+# ---------------------------------------------------------------- workloads and their byte / FLOP counts
 def mamba1_bytes(inp):
     b, L, Dc, N, G = inp.batch, inp.seqlen, inp.channels, inp.state_dim, inp.ngroups
     es = 2 if inp.act == "bf16" else 4
@@ -114,7 +90,7 @@ def ssd_bytes(inp):
     return rd + wr
 
 
-def ssd_flops(inp, Q=256):
+def ssd_flops(inp, Q):
     """Contraction FLOPs of the chunked SSD at chunk Q (dense Q x Q blocks): C.B^T per
     (batch, chunk, group), and per (batch, chunk, head) the diagonal block M.X, the chunk
     state X^T.(B*w) and the off-diagonal read C.H^T."""
@@ -123,9 +99,57 @@ def ssd_flops(inp, Q=256):
     return b * nch * (G * 2 * Q * Q * N + H * (2 * Q * Q * P + 2 * Q * N * P + 2 * Q * N * P))
 
 
+def make(gen, wid):
+    return gen.make_workload(wid)
+
+
+def upload(inp, torch):
+    def act(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+        return (t.to(torch.bfloat16) if inp.act == "bf16" else t).cuda()
+
+    def par(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+    return dict(x=act(inp.x), dt_raw=act(inp.dt_raw), B=act(inp.B), C=act(inp.C), z=act(inp.z),
+                dt_bias=par(inp.dt_bias), A_log=par(inp.A_log), D=par(inp.D), state_input=par(inp.h0))
+
+
+def clone_set(d):
+    return {k: (None if v is None else v.clone()) for k, v in d.items()}
+
+
+def scan_call(inp, bd, torch, base):
+    """A closure that runs the workload's scan once on a set of its inputs."""
+    if hasattr(inp, "channels"):
+        b, Dc, N = inp.batch, inp.channels, inp.state_dim
+        y = torch.empty_like(base["x"])
+        h = torch.empty((b, Dc, N), dtype=torch.float32, device="cuda")
+        ws_n = bd.sscan_mamba1_workspace_size(bd.mamba1_desc(base["x"], base["B"], inp.bc_eps))
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def fn(s):
+            bd.sscan_mamba1_fwd(s["x"], s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"], s["D"], s["z"],
+                                s["state_input"], y=y, state_output=h, workspace=ws, bc_rms_eps=inp.bc_eps)
+        return fn
+    b, H, P, N = inp.batch, inp.nheads, inp.head_dim, inp.state_dim
+    y = torch.empty_like(base["x"])
+    h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def fn(s):
+        bd.sscan_ssd_fwd(s["x"], s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"], s["D"], s["z"],
+                         s["state_input"], y=y, state_output=h, workspace=ws, chunk=inp.chunk)
+    return fn
+
+
 def time_calls(fn, sets, steps, warmup, torch):
-    """Run fn(set) `warmup` times untimed, then `steps` times timed; returns
-    (wall ms per step, mean event ms per call)."""
+    """`warmup` untimed calls, then `steps` timed calls between two synchronizations,
+    each also bracketed by HIP events on the current stream (the one the library
+    launches on). Returns (wall ms per step, event ms statistics)."""
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
@@ -138,62 +162,256 @@ def time_calls(fn, sets, steps, warmup, torch):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return wall, ev
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return wall, dict(mean=float(ms.mean()), median=float(np.median(ms)), min=float(ms.min()), n=int(ms.size))
 
 
-def bench_mamba1(wid, steps, warmup, torch, bd, gen):
-    inp = gen.make_workload(wid)
+# ---------------------------------------------------------------- hardware counters (rocprofv3 children)
+def counter_child():
+    """Runs under rocprofv3: each throughput workload COUNTER_REPS times, then a plain
+    elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB) CALIB_REPS times."""
+    import torch
+
+    from state_space_model_sscan_amd import binding as bd
+    from state_space_model_sscan_amd import inputs as gen
+
+    bd.lib()
+    for wid, reps in COUNTER_REPS.items():
+        inp = make(gen, wid)
+        base = upload(inp, torch)
+        fn = scan_call(inp, bd, torch, base)
+        for _ in range(reps):
+            fn(base)
+        torch.cuda.synchronize()
+        log("counter child: workload %d x %d" % (wid, reps))
+        del base, fn
+        torch.cuda.empty_cache()
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(CALIB_REPS):
+        torch.add(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log("counter child: calibration x %d" % CALIB_REPS)
+
+
+def _read_counters(outdir):
+    """{(kernel name, grid): {counter: [values per dispatch]}} from a rocprofv3 csv."""
+    files = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
+    rec = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], int(r["Grid_Size"]))
+                disp = int(r["Dispatch_Id"])
+                rec.setdefault(key, {}).setdefault(r["Counter_Name"], {}).setdefault(disp, 0.0)
+                # counters come per die / shader engine in some versions: sum them per dispatch
+                rec[key][r["Counter_Name"]][disp] += float(r["Counter_Value"])
+    return {k: {c: list(d.values()) for c, d in v.items()} for k, v in rec.items()}
+
+
+def collect_counters(timeout_s=240):
+    """The four counter passes of the workloads, each in a child process under rocprofv3.
+    Must run before this process touches the GPU. Returns {pass: records} or an error."""
+    prof = shutil.which("rocprofv3")
+    if not prof:
+        return {"error": "rocprofv3 not found"}
+    top = os.path.join(ROOT, "gpurun_out", "bench_counters")
+    out = {}
+    for name, counters in COUNTER_PASSES:
+        d = os.path.join(top, name)
+        shutil.rmtree(d, ignore_errors=True)
+        os.makedirs(d, exist_ok=True)
+        cmd = [prof, "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "run", "--",
+               sys.executable, os.path.abspath(__file__), "--counter-child"]
+        log("bench: counter pass %s (%s)" % (name, " ".join(counters)))
+        env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+        p = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=open(os.path.join(d, "child.log"), "w"),
+                             cwd="/tmp", env=env, start_new_session=True)
+        try:
+            rc = p.wait(timeout=timeout_s)
+        except subprocess.TimeoutExpired:
+            os.killpg(p.pid, signal.SIGKILL)
+            p.wait()
+            return {"error": "counter pass %s timed out" % name}
+        rec = _read_counters(d)
+        if not rec:  # rocprofv3 may end with a fault after writing whole results; only no data is an error
+            return {"error": "counter pass %s wrote no records (rc %d)" % (name, rc)}
+        out[name] = rec
+    return out
+
+
+def _by_reps(rec, reps, counter):
+    """Mean per dispatch of `counter` over every sscan kernel launched `reps` times,
+    summed over those kernels, and the largest of them (name, mean)."""
+    total, top = 0.0, (None, -1.0)
+    for (kname, grid), cs in rec.items():
+        v = cs.get(counter)
+        if "sscan::" not in kname or v is None or len(v) != reps:
+            continue
+        m = float(np.mean(v))
+        total += m
+        if m > top[1]:
+            top = (kname, m)
+    return total, top
+
+
+def _calibration(rec, counter):
+    best = None
+    for (kname, grid), cs in rec.items():
+        v = cs.get(counter)
+        if "elementwise" in kname and v is not None and len(v) == CALIB_REPS:
+            if best is None or grid > best[0]:
+                best = (grid, float(np.mean(v)))
+    return None if best is None else best[1]
+
+
+def counter_summary(cnt, wid, inp):
+    """Per workload: HBM bytes per call from FETCH_SIZE / WRITE_SIZE (scaled by the
+    calibration kernel's readings), VALU or MFMA figures."""
+    if not cnt or "error" in cnt:
+        return dict(error=(cnt or {}).get("error", "not collected"))
+    reps = COUNTER_REPS[wid]
+    rd, (kname, _) = _by_reps(cnt["read"], reps, "FETCH_SIZE")
+    wr, _ = _by_reps(cnt["write"], reps, "WRITE_SIZE")
+    cf = _calibration(cnt["read"], "FETCH_SIZE")
+    cw = _calibration(cnt["write"], "WRITE_SIZE")
+    gib_kib = float(1 << 20)  # 1 GiB in KiB
+    s = dict(kernel=kname)
+    if cf and cw and rd > 0:
+        fr, fw = gib_kib / cf, gib_kib / cw
+        s.update(read_bytes=rd * 1024 * fr, write_bytes=wr * 1024 * fw,
+                 calibration=dict(fetch_size_kib=cf, write_size_kib=cw, fetch_scale=fr, write_scale=fw,
+                                  kernel="torch elementwise add, 1 GiB read + 1 GiB written"))
+        s["traffic_bytes"] = s["read_bytes"] + s["write_bytes"]
+    v = cnt.get("valu", {})
+    insts, _ = _by_reps(v, reps, "SQ_INSTS_VALU")
+    active, _ = _by_reps(v, reps, "SQ_ACTIVE_INST_VALU")
+    trans, _ = _by_reps(v, reps, "SQ_INSTS_VALU_TRANS_F32")
+    gui, _ = _by_reps(v, reps, "GRBM_GUI_ACTIVE")
+    if insts > 0 and gui > 0:
+        units = inp.batch * inp.seqlen * (inp.channels * inp.state_dim if hasattr(inp, "channels")
+                                          else inp.nheads * inp.head_dim * inp.state_dim)
+        s["valu"] = dict(wave_instructions=insts, transcendental=trans,
+                         instructions_per_state_update=insts * 64 / units,
+                         busy=active / NUM_CU / (gui / NUM_XCD),
+                         note="busy = SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE per die (rocprof's VALUBusy)")
+    m = cnt.get("mfma", {})
+    mops, _ = _by_reps(m, reps, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    if mops > 0:
+        s["mfma_flops"] = mops * MFMA_FLOPS_PER_MOP
+        busy, _ = _by_reps(m, reps, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui, _ = _by_reps(m, reps, "GRBM_GUI_ACTIVE")
+        if gui > 0:
+            s["mfma_busy"] = busy / (NUM_CU * 4) / (gui / NUM_XCD)
+    return s
+
+
+# ---------------------------------------------------------------- the CPU baseline (the oracle)
+def host_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(cpu_model=model, cpu_count=os.cpu_count(), omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
+
+
+def cpu_baseline(inp, min_seconds, threads=None, sample=None):
+    """The fp64 oracle as it stands on `inp` (or a slice of its batch rows), run back to back
+    until at least `min_seconds` are timed. Returns tokens/s and state updates/s."""
+    import oracle
+
+    oracle.build(force=False)
+    full = oracle.threads()
+    if threads:
+        oracle.set_threads(threads)
+    try:
+        used = oracle.threads()
+        runs, total = 0, 0.0
+        while runs < 1 or total < min_seconds:
+            t0 = time.perf_counter()
+            oracle.run_inputs(inp, want_states=False)
+            total += time.perf_counter() - t0
+            runs += 1
+    finally:
+        oracle.set_threads(full)
+    per_tok = inp.channels * inp.state_dim if hasattr(inp, "channels") else inp.nheads * inp.head_dim * inp.state_dim
+    toks = inp.batch * inp.seqlen * runs
+    return dict(value=toks / total, unit="tokens/s", cores=used, kind="oracle",
+                updates_per_s=toks * per_tok / total,
+                sample="%s, fp64, run %d times back to back, %.1f s in all" % (sample, runs, total))
+
+
+def batch_rows(inp, rows):
+    """The same workload restricted to its first `rows` batch rows (rows are independent)."""
+    import copy
+    s = copy.copy(inp)
+    for k in ("x", "dt_raw", "z", "B", "C", "h0"):
+        v = getattr(inp, k)
+        if v is not None:
+            setattr(s, k, v[:rows])
+    s.batch = rows
+    return s
+
+
+# ---------------------------------------------------------------- GPU timing of the workloads
+def bench_workload(wid, steps, warmup, torch, bd, gen, inp=None):
+    inp = inp or make(gen, wid)
     base = upload(inp, torch)
     sets = [base] + [clone_set(base) for _ in range(2)]
-    b, L, Dc, N = inp.batch, inp.seqlen, inp.channels, inp.state_dim
-    y = torch.empty_like(base["x"])
-    h = torch.empty((b, Dc, N), dtype=torch.float32, device="cuda")
-    ws_n = bd.sscan_mamba1_workspace_size(bd.mamba1_desc(base["x"], base["B"], inp.bc_eps))
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-
-    def fn(s):
-        bd.sscan_mamba1_fwd(s["x"], s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"], s["D"], s["z"],
-                            s["state_input"], y=y, state_output=h, workspace=ws, bc_rms_eps=inp.bc_eps)
-
+    fn = scan_call(inp, bd, torch, base)
     wall, ev = time_calls(fn, sets, steps, warmup, torch)
-    upd = b * L * Dc * N
-    by = mamba1_bytes(inp)
-    return dict(workload=gen.WORKLOADS[wid]["name"], ms_per_step=wall, kernel_ms=ev, tokens=b * L,
-                tokens_per_s=b * L / (wall * 1e-3), updates_per_s=upd / (ev * 1e-3), bytes=by,
-                hbm_gbs=by / (ev * 1e-3) / 1e9, hbm_frac=by / (ev * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                valu_tslots=6 * upd / (ev * 1e-3) / 1e12, inp=inp)
+    del sets, base
+    torch.cuda.empty_cache()
+    ssd = not hasattr(inp, "channels")
+    by = ssd_bytes(inp) if ssd else mamba1_bytes(inp)
+    per_tok = inp.nheads * inp.head_dim * inp.state_dim if ssd else inp.channels * inp.state_dim
+    tokens = inp.batch * inp.seqlen
+    ksec = ev["mean"] * 1e-3
+    d = dict(workload=gen.WORKLOADS[wid]["name"], ms_per_step=wall, kernel_ms=ev, tokens=tokens,
+             tokens_per_s=tokens / (wall * 1e-3), updates_per_s=tokens * per_tok / ksec, bytes=by)
+    d["roofline"] = dict(bound="hbm", achieved=by / ksec / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=by / ksec / 1e9 / HBM_PEAK_GBS, traffic=None, algorithmic_bytes=by,
+                         kernel_ms=ev["mean"])
+    if ssd:
+        q64, q256 = ssd_flops(inp, 64), ssd_flops(inp, 256)
+        d["mfma"] = dict(peak_tflops=BF16_MFMA_PEAK_TFLOPS, counted_flops=None, frac=None,
+                         algorithmic_flops_q64=q64, frac_algorithmic_q64=q64 / ksec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                         algorithmic_flops_q256=q256,
+                         frac_algorithmic_q256=q256 / ksec / 1e12 / BF16_MFMA_PEAK_TFLOPS)
+    return d, inp
 
 
-def bench_ssd(steps, warmup, torch, bd, gen):
-    inp = gen.make_workload(4)
-    base = upload(inp, torch)
-    sets = [base] + [clone_set(base) for _ in range(2)]
-    b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
-    y = torch.empty_like(base["x"])
-    h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
-    ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-
-    def fn(s):
-        bd.sscan_ssd_fwd(s["x"], s["dt_raw"], s["dt_bias"], s["A_log"], s["B"], s["C"], s["D"], s["z"],
-                         s["state_input"], y=y, state_output=h, workspace=ws, chunk=inp.chunk)
-
-    wall, ev = time_calls(fn, sets, steps, warmup, torch)
-    by = ssd_bytes(inp)
-    fl = ssd_flops(inp, 256)
-    return dict(workload=gen.WORKLOADS[4]["name"], ms_per_step=wall, kernel_ms=ev, tokens=b * L,
-                tokens_per_s=b * L / (wall * 1e-3), bytes=by, hbm_gbs=by / (ev * 1e-3) / 1e9,
-                hbm_frac=by / (ev * 1e-3) / 1e9 / HBM_PEAK_GBS, flops_q256=fl,
-                mfma_tflops=fl / (ev * 1e-3) / 1e12, mfma_frac=fl / (ev * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                inp=inp, base=base)
+def attach_counters(d, cs):
+    d["counters"] = cs
+    r = d["roofline"]
+    if "traffic_bytes" in cs:
+        r["traffic"] = cs["traffic_bytes"]
+        r["traffic_read"] = cs["read_bytes"]
+        r["traffic_write"] = cs["write_bytes"]
+        r["traffic_over_algorithmic"] = cs["traffic_bytes"] / r["algorithmic_bytes"]
+        r["counter_kernel"] = cs.get("kernel")
+    if "valu" in cs:
+        r["valu"] = cs["valu"]
+    if "mfma" in d and "mfma_flops" in cs:
+        ksec = d["kernel_ms"]["mean"] * 1e-3
+        m = d["mfma"]
+        m["counted_flops"] = cs["mfma_flops"]
+        m["tflops"] = cs["mfma_flops"] / ksec / 1e12
+        m["frac"] = m["tflops"] / BF16_MFMA_PEAK_TFLOPS
+        m["busy"] = cs.get("mfma_busy")
 
 
+# ---------------------------------------------------------------- secondary measurements (the steps next to the scan)
 def bench_step(torch, bd, gen, calls=512):
     """Workload 2 as `calls` one-token sscan_step calls, state updated in place: timed
     eagerly (includes the Python/ctypes cost of each call) and as a HIP graph that
     replays the same `calls` launches (the GPU-side cost per step)."""
-    inp = gen.make_workload(2)
+    inp = make(gen, 2)
     base = upload(inp, torch)
     b, Dc = inp.batch, inp.channels
     xs = [base["x"][:, t:t + 1].contiguous() for t in range(calls)]
@@ -220,8 +438,6 @@ def bench_step(torch, bd, gen, calls=512):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e6 / calls
     eager_gpu = e0.elapsed_time(e1) * 1e3 / calls
-    # the same calls captured once into a HIP graph (pointer checks are host-side queries:
-    # off while capturing), then replayed
     graph_us = None
     try:
         prev = bd.set_pointer_checks(False)
@@ -247,20 +463,19 @@ def bench_step(torch, bd, gen, calls=512):
                 graph_gbs=None if not graph_us else per_call_bytes / (graph_us * 1e-6) / 1e9)
 
 
-def hbm_entry(workload, ms_wall, ms_kernel, nbytes, **kw):
-    d = dict(workload=workload, ms_per_step=ms_wall, kernel_ms=ms_kernel, bytes=nbytes,
-             hbm_gbs=nbytes / (ms_kernel * 1e-3) / 1e9, hbm_frac=nbytes / (ms_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS)
+def hbm_entry(workload, ms_wall, ev, nbytes, **kw):
+    ms = ev["mean"]
+    d = dict(workload=workload, ms_per_step=ms_wall, kernel_ms=ev, bytes=nbytes,
+             hbm_gbs=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
     d.update(kw)
     return d
 
 
-def bench_mixer_ops(steps, warmup, torch, bd, s4):
+def bench_mixer_ops(steps, warmup, torch, bd, L=8192, b=4):
     """The steps next to the scan at the Mamba-2 2.7B layer shape (batch 4, 8192 tokens):
     conv1d + silu over xBC (5120 + 2 x 128 = 5376 channels, width 4, with the carried conv
     state in and out), and the gated RMS norm over y, z (80 heads x 64 = 5120 wide). Both
     stream more than the 256 MiB Infinity Cache per call."""
-    base = s4["base"]
-    b, L = base["x"].shape[0], base["x"].shape[1]
     g = torch.Generator(device="cuda")
     g.manual_seed(5376)
     Dc, W = 5376, 4
@@ -279,9 +494,9 @@ def bench_mixer_ops(steps, warmup, torch, bd, s4):
     conv_e = hbm_entry("mamba2-2.7b xBC conv1d+silu, bf16 %dx%dx%d, width %d, conv state in/out" % (b, L, Dc, W),
                        wall, ev, cbytes, tokens_per_s=b * L / (wall * 1e-3))
     del xbc, out
-
-    rows, width = b * L, base["x"].shape[2] * base["x"].shape[3]
-    y2, z2 = base["x"].view(rows, width), base["z"].view(rows, width)
+    rows, width = b * L, 5120
+    y2 = torch.randn((rows, width), generator=g, device="cuda").to(torch.bfloat16)
+    z2 = torch.randn((rows, width), generator=g, device="cuda").to(torch.bfloat16)
     wn = torch.rand((width,), generator=g, device="cuda") + 0.5
     nout = torch.empty_like(y2)
 
@@ -295,13 +510,14 @@ def bench_mixer_ops(steps, warmup, torch, bd, s4):
     return conv_e, norm_e
 
 
-def bench_ssd_step(torch, bd, s4, nstates=32, calls=64):
+def bench_ssd_step(torch, bd, gen, nstates=32, calls=64):
     """Mamba-2 2.7B decode: one-token sscan_ssd_step calls at batch 4 (state [4, 80, 64, 128]
     fp32, 10.5 MB, updated in place). The calls cycle over `nstates` separate states, 336 MB
     in all, so that no call finds its state in the 256 MiB Infinity Cache, as in a model whose
     other layers' states pass through between two steps of a layer. Timed as a HIP graph
     that replays `calls` launches."""
-    base = s4["base"]
+    inp = gen.make_workload(4, seqlen=calls)
+    base = upload(inp, torch)
     one = lambda a, t: a[:, t:t + 1].contiguous()
     xs = [one(base["x"], t) for t in range(calls)]
     zs = [one(base["z"], t) for t in range(calls)]
@@ -371,140 +587,133 @@ def bench_ssd_states(steps, warmup, torch, bd, gen):
                      wall, ev, nbytes, tokens_per_s=b * L / (wall * 1e-3))
 
 
-def bench_attention(steps, warmup, torch, bd, s4, L=2048):
-    """The hidden attention map of batch row 0's first L tokens of the Mamba-2 2.7B workload
-    (80 heads, one group, state 128): alpha [1, L, L, 80] fp32, 1.34 GB written per call."""
-    base = s4["base"]
-    dt = base["dt_raw"][:1, :L].contiguous()
-    B = base["B"][:1, :L].contiguous()
-    C = base["C"][:1, :L].contiguous()
-    H = dt.shape[2]
+def bench_attention(steps, warmup, torch, bd, gen, L=2048):
+    """The hidden attention map of the first L tokens of one batch row of the Mamba-2 2.7B
+    workload's distributions (80 heads, one group, state 128): alpha [1, L, L, 80] fp32,
+    1.34 GB written per call."""
+    inp = gen.make_workload(4, batch=1, seqlen=L)
+    dt = upload(inp, torch)
+    H = inp.nheads
     alpha = torch.empty((1, L, L, H), dtype=torch.float32, device="cuda")
 
     def fn(_):
-        bd.sscan_ssd_attention(dt, base["dt_bias"], base["A_log"], B, C, alpha=alpha)
+        bd.sscan_ssd_attention(dt["dt_raw"], dt["dt_bias"], dt["A_log"], dt["B"], dt["C"], alpha=alpha)
 
     wall, ev = time_calls(fn, [None], steps, warmup, torch)
-    nbytes = L * L * H * 4 + L * H * 2 + 2 * L * B.shape[2] * B.shape[3] * 2 + 2 * H * 4
+    nbytes = L * L * H * 4 + L * H * 2 + 2 * L * inp.ngroups * inp.state_dim * 2 + 2 * H * 4
     return hbm_entry("mamba2-2.7b hidden attention map, 1 x %d tokens x %d heads, fp32 out" % (L, H), wall, ev,
                      nbytes)
 
 
-def cpu_baseline(inp, min_seconds=10.0, max_runs=200):
-    """The fp64 oracle on the same workload, run whole and repeated until at least
-    `min_seconds` of CPU work have been timed; reports the mean rate over the runs."""
-    import oracle
-
-    oracle.build(force=False)
-    runs, total = 0, 0.0
-    while runs < 2 or (total < min_seconds and runs < max_runs):
-        t0 = time.perf_counter()
-        oracle.run_inputs(inp, want_states=False)
-        total += time.perf_counter() - t0
-        runs += 1
-    toks = inp.batch * inp.seqlen * runs
-    return dict(value=toks / total, unit="tokens/s", cores=oracle.threads(), kind="oracle",
-                sample="the whole workload (%d x %d tokens x %d channels x %d states), fp64, run %d times "
-                       "back to back, %.1f s in all" % (inp.batch, inp.seqlen, inp.channels, inp.state_dim, runs,
-                                                        total))
-
-
-def copy_calibration(torch, gib=1, reps=3):
-    """A plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB), for
-    scaling the FETCH_SIZE / WRITE_SIZE counters."""
-    n = gib * (1 << 30) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(reps):
-        torch.add(a, 1.0, out=b)
-    torch.cuda.synchronize()
-    log("copy calibration: %d x elementwise copy of %d bytes" % (reps, n * 4))
-
-
+# ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-counters", action="store_true", help="skip the rocprofv3 counter passes")
     ap.add_argument("--only-main", action="store_true", help="time only the main workload")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for scaling memory counters)")
+    ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one MI355X). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-
-    import torch
+    if args.counter_child:
+        counter_child()
+        return
 
     from state_space_model_sscan_amd import binding as bd
     from state_space_model_sscan_amd import inputs as gen
 
     bd.lib()  # fails loudly if libsscan.so is missing
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        copy_calibration(torch)
+    # Child processes first (the counter passes), before this process touches the GPU.
+    cnt = None
+    if not args.no_counters and not args.only_main:
+        cnt = collect_counters()
+        if "error" in cnt:
+            log("bench: counters unavailable: %s" % cnt["error"])
 
-    log("bench: workload 1 (main)")
-    m = bench_mamba1(1, args.steps, args.warmup, torch, bd, gen)
-    extra = {}
+    log("bench: inputs")
+    inputs = {MAIN: make(gen, MAIN)}
     if not args.only_main:
-        log("bench: workload 3")
-        m3 = bench_mamba1(3, max(10, args.steps // 4), 3, torch, bd, gen)
-        log("bench: workload 4 (SSD)")
-        s4 = bench_ssd(max(10, args.steps // 4), 3, torch, bd, gen)
-        log("bench: workload 2 (decode steps)")
-        st = bench_step(torch, bd, gen)
-        log("bench: conv1d + silu, gated RMS norm")
-        conv_e, norm_e = bench_mixer_ops(max(10, args.steps // 4), 3, torch, bd, s4)
-        log("bench: Mamba-2 decode steps")
-        sst = bench_ssd_step(torch, bd, s4)
-        log("bench: hidden attention map")
-        att = bench_attention(max(5, args.steps // 10), 2, torch, bd, s4)
-        log("bench: SSD with per-token states")
-        sts = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
-        extra = dict(
-            mamba1_falcon_width={k: v for k, v in m3.items() if k != "inp"},
-            ssd_mamba2_2p7b={k: v for k, v in s4.items() if k not in ("inp", "base")},
-            decode_step=st,
-            ssd_decode_step=sst,
-            conv1d_silu=conv_e,
-            gated_rmsnorm=norm_e,
-            ssd_attention_map=att,
-            ssd_per_token_states=sts,
-        )
-    cpu = None
+        for w in BLOCKS:
+            inputs[w] = make(gen, w)
+
+    cpu = {}
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        cpu = cpu_baseline(m["inp"])
+        m = inputs[MAIN]
+        cpu[MAIN] = cpu_baseline(m, 10.0, sample="the whole workload (%d x %d tokens x %d channels x %d states)"
+                                 % (m.batch, m.seqlen, m.channels, m.state_dim))
+        one = batch_rows(m, 1)
+        cpu[MAIN]["single_thread"] = cpu_baseline(one, 3.0, threads=1,
+                                                  sample="batch row 0 of the workload (1 x %d tokens x %d channels)"
+                                                  % (m.seqlen, m.channels))
+        if not args.only_main:
+            w3 = inputs[3]
+            cpu[3] = cpu_baseline(w3, 5.0, sample="the whole workload (%d x %d tokens x %d channels x %d states)"
+                                  % (w3.batch, w3.seqlen, w3.channels, w3.state_dim))
+            w4 = batch_rows(inputs[4], 1)
+            cpu[4] = cpu_baseline(w4, 3.0, sample="batch row 0 of the workload (1 x %d tokens x %d heads x %d x %d "
+                                  "states)" % (w4.seqlen, w4.nheads, w4.head_dim, w4.state_dim))
 
-    inp = m["inp"]
-    valu_frac = m["valu_tslots"] / VALU_PEAK_TSLOTS
-    tr = recorded_traffic("mamba1_workload1")
-    traffic = None if tr is None else tr["hbm_bytes_per_launch"]
+    import torch
+
+    torch.cuda.set_device(0)
+    log("bench: workload %d (main)" % MAIN)
+    main_d, _ = bench_workload(MAIN, args.steps, args.warmup, torch, bd, gen, inputs[MAIN])
+    if cnt:
+        attach_counters(main_d, counter_summary(cnt, MAIN, inputs[MAIN]))
+    blocks, extra = {}, {}
+    if not args.only_main:
+        for w in BLOCKS:
+            log("bench: workload %d" % w)
+            d, _ = bench_workload(w, max(10, args.steps // 4), 3, torch, bd, gen, inputs[w])
+            if cnt:
+                attach_counters(d, counter_summary(cnt, w, inputs[w]))
+            d["cpu_baseline"] = cpu.get(w)
+            blocks[d["workload"]] = d
+        del inputs
+        log("bench: decode steps")
+        extra["decode_step"] = bench_step(torch, bd, gen)
+        log("bench: conv1d + silu, gated RMS norm")
+        extra["conv1d_silu"], extra["gated_rmsnorm"] = bench_mixer_ops(max(10, args.steps // 4), 3, torch, bd)
+        log("bench: Mamba-2 decode steps")
+        extra["ssd_decode_step"] = bench_ssd_step(torch, bd, gen)
+        log("bench: hidden attention map")
+        extra["ssd_attention_map"] = bench_attention(max(5, args.steps // 10), 2, torch, bd, gen)
+        log("bench: SSD with per-token states")
+        extra["ssd_per_token_states"] = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
+
+    cfg = gen.WORKLOADS[MAIN]
+    roof = dict(main_d["roofline"])
+    roof["kernel_ms_median"] = main_d["kernel_ms"]["median"]
+    roof["kernel_ms_min"] = main_d["kernel_ms"]["min"]
+    roof["updates_per_s"] = main_d["updates_per_s"]
     line = {
         "metric": METRIC,
-        "value": m["tokens_per_s"],
+        "value": main_d["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": m["ms_per_step"],
+        "ms_per_step": main_d["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": m["workload"], "batch": inp.batch, "seq_len": inp.seqlen,
-                   "channels": inp.channels, "state_dim": inp.state_dim, "ngroups": inp.ngroups,
+        "config": {"workload": cfg["name"], "batch": cfg["batch"], "seq_len": cfg["seqlen"],
+                   "channels": cfg["channels"], "state_dim": cfg["state_dim"], "ngroups": 1,
                    "gate": True, "state": "fp32"},
-        "roofline": {"bound": "alu", "achieved": m["valu_tslots"], "peak": VALU_PEAK_TSLOTS,
-                     "unit": "T VALU-slots/s", "frac": valu_frac, "traffic": traffic,
-                     "kernel": MAIN_KERNEL, "kernel_ms": m["kernel_ms"],
-                     "hbm_gbs": m["hbm_gbs"], "hbm_frac": m["hbm_frac"], "algorithmic_bytes": m["bytes"],
-                     "updates_per_s": m["updates_per_s"]},
-        "cpu_baseline": cpu,
+        "roofline": roof,
+        "cpu_baseline": cpu.get(MAIN),
+        "kernel_ms": main_d["kernel_ms"],
+        "counters": main_d.get("counters"),
+        "host": host_info(),
+        "workloads": blocks,
         "secondary": extra,
     }
     print(json.dumps(line), flush=True)

@@ -50,6 +50,8 @@ def _load():
         lib.oracle_gated_rmsnorm.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -57,6 +59,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's later loops (the results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _f64(a):

@@ -56,6 +56,12 @@ int oracle_abi_version(void) { return 1; }
 /* Threads an OpenMP loop of the oracle uses (for reporting the CPU baseline). */
 int oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the threads of the oracle's later loops on the calling thread (for timing the
+ * CPU baseline on one core); the arithmetic of each lane does not depend on it. */
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 /* Weightless RMS norm of every [state_dim] vector of a [rows, state_dim] array
  * ([FM] "Where the norms sit"): out = v / sqrt(mean(v^2) + eps). */
 static void rms_norm_rows(int64_t rows, int64_t n, const double* in, double eps, double* out) {
