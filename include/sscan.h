@@ -265,8 +265,11 @@ typedef enum {
                                        (others, and shapes the kernel cannot take, are ignored) */
   SSCAN_TUNE_SSD_SEGMENT_CHUNKS = 2, /* chunks per segment of the SSD chunk path */
   SSCAN_TUNE_SSD_WORKGROUPS = 3,    /* workgroups of the SSD chunk path */
-  SSCAN_TUNE_SSD_GIVE_UP = 4        /* nonzero: every state hand-off wait of the SSD chunk path gives
+  SSCAN_TUNE_SSD_GIVE_UP = 4,       /* nonzero: every state hand-off wait of the SSD chunk path gives
                                        up at once (for testing what a wait that gives up does) */
+  SSCAN_TUNE_SSD_HEADS_PER_WORKGROUP = 5  /* 2: two neighbouring heads of a group share a workgroup of
+                                       the SSD chunk path, with B, C and C.B^T staged once (by
+                                       default one head per workgroup; same results) */
 } sscan_tune_knob;
 int64_t sscan_set_tuning(int knob, int64_t value);
 

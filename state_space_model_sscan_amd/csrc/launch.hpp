@@ -13,7 +13,8 @@ enum Knob {
   kKnobSsdSegmentChunks = 2, // chunks per segment of the SSD chunk kernel
   kKnobSsdWorkgroups = 3,    // workgroups of the SSD chunk kernel
   kKnobSsdGiveUp = 4,        // nonzero: every state hand-off wait of the chunk kernel gives up at once
-  kKnobCount = 5
+  kKnobSsdHeadsPerWorkgroup = 5,  // 2: two heads per workgroup of the chunk kernel where they share a group
+  kKnobCount = 6
 };
 int64_t knob(int which);
 

@@ -104,10 +104,10 @@ struct SsdK {
   uint16_t* y;
   float* h_out;
   unsigned* queue;  // [16 q]: next item of queue q; [128]: a wait gave up; [256 + ch]: segments of chain ch done
-  float* carry;     // [chains, P, NS]: the state a segment hands to the next one
+  float* carry;     // [batch * H, P, NS]: the state a segment hands to the next one, per head
   int64_t L, H, G;
   int heads_per_group;
-  int nchains;      // batch * H
+  int nchains;      // batch * H / HPW (a chain is a run of HPW heads of one batch row)
   int seg_chunks;   // chunks per segment
   int nseg;         // segments per chain
   int nq;           // work queues; workgroup i serves queue i % nq, which holds chains
@@ -179,16 +179,27 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 // One chunk's staged global loads of one thread, in flight during the previous
 // chunk. Coalesced: 16 lanes cover a 256-byte row of B or C (an instruction, 4
 // rows), 8 lanes a 128-byte row of x (8 rows), so each load touches a few cache
-// lines rather than one per lane. B, C: rows 16w + 4it + l/16, piece l%16; x and
-// z: rows 16w + 8it + l/8, piece l%8; dt (wave kDecayWave only): token l.
+// lines rather than one per lane. B, C (shared by the workgroup's heads): rows
+// tid/16 + 16 HPW it, piece tid%16; x and z (per head): rows 16wq + 8it + l/8,
+// piece l%8; dt (wave kDecayWave of each head only): token l.
+template <int HPW>
 struct Prefetch {
-  u32x4 b[4], c[4], x[2], z[2];
+  u32x4 b[4 / HPW], c[4 / HPW], x[2], z[2];
   uint32_t dt;  // raw bf16 bits
 };
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
+// HPW heads of one batch row per workgroup (1 or 2), four waves per head. With two
+// heads, B and C (shared by every head of a group) are staged once and each C B^T
+// tile is computed once, then masked with each head's decays; the two heads' waves
+// share the SIMDs, so one head's MFMA and memory latencies hide behind the other's
+// work.
+template <int HPW>
+__global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(SsdK k) {
+  constexpr int NW = 4 * HPW;      // waves
+  constexpr int BCIT = 4 / HPW;    // rows of B (and of C) a thread stages
+  constexpr int NT = HPW == 1 ? 3 : 2;  // C B^T tiles a wave computes (some repeated)
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t sC[Q * LDC];
   // C again, each row in the k order of the Y^T = S C^T operand: positions
@@ -198,19 +209,21 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   // (dynamic LDS of kCkBytes: its size then does not lower the occupancy the code
   // is compiled for, which schedules this kernel better)
   extern __shared__ __attribute__((aligned(16))) uint16_t sCk[];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[Q * LDX];
-  __shared__ __attribute__((aligned(16))) uint16_t sM[Q * LDM];
-  __shared__ __attribute__((aligned(16))) uint16_t sZ[Q * LDX];  // z of the chunk
-  __shared__ __attribute__((aligned(16))) uint16_t sY[Q * LDX];  // y of the chunk, stored after the next barrier
-  __shared__ __attribute__((aligned(16))) float sCS[Q], sDT[Q], sW[Q], sE[Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[HPW][Q * LDX];
+  __shared__ __attribute__((aligned(16))) uint16_t sM[HPW][Q * LDM];
+  __shared__ __attribute__((aligned(16))) uint16_t sZ[HPW][Q * LDX];  // z of the chunk
+  __shared__ __attribute__((aligned(16))) uint16_t sY[HPW][Q * LDX];  // y of the chunk, stored after the next barrier
+  __shared__ __attribute__((aligned(16))) float sCS[HPW][Q], sDT[HPW][Q], sW[HPW][Q], sE[HPW][Q];
   __shared__ int sTicket[3];  // [0]: the first item; [1]: the item after the current one;
                               // [2]: the current item's hand-off wait gave up
 
-  // the wave index through readfirstlane: a scalar, so branches on it stay uniform
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, li = l & 15,
-            lg = l >> 4;
+  // the wave index through readfirstlane: a scalar, so branches on it stay uniform;
+  // wave w serves head slot hs = w / 4 of the workgroup's heads, columns 16 wq .. 16 wq + 15
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), hs = w >> 2, wq = w & 3,
+            l = tid & 63, li = l & 15, lg = l >> 4;
   // 32-bit sizes: the host guarantees each batch row of every tensor is < 2^31 bytes
   const int L = (int)k.L, H = (int)k.H, G = (int)k.G;
+  const int hpc = H / HPW;  // chains (runs of HPW heads) per batch row
   const bool gate = k.z != nullptr;
 
   // This workgroup's queue (the dispatcher deals workgroups to the eight compute
@@ -246,47 +259,47 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2), dt_row = (uint32_t)(H * 2);
   // elements per batch row
   const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * H;
-  const int bc_r = 16 * w + (l >> 4), bc_p = l & 15;  // staging row (+ 4 it) and piece of B, C
-  const int x_r = 16 * w + (l >> 3), x_p = l & 7;     // staging row (+ 8 it) and piece of x
+  const int bc_r = tid >> 4, bc_p = tid & 15;         // staging row (+ 16 HPW it) and piece of B, C
+  const int x_r = 16 * wq + (l >> 3), x_p = l & 7;    // staging row (+ 8 it) and piece of x
   const uint32_t bc_lane = (uint32_t)(bc_r * bc_row + bc_p * 16);
   const uint32_t x_lane = (uint32_t)(x_r * xz_row + x_p * 16);
   const uint32_t dt_lane = (uint32_t)(l * dt_row);
 
   // Global access goes through buffer resources based at a chunk's first token
-  // row and this chain's first column, ending at the sequence end (the host
-  // guarantees each batch row is < 2^31 bytes): rows past the end read zeros
-  // and drop their stores in hardware, and the lane offsets stay uniform.
-  // Target of the loads in flight: chain (tb, th, tg), first token tt (tt >= L:
-  // none; every load reads zeros).
+  // row and this wave's head's first column, ending at the sequence end (the host
+  // guarantees each batch row is < 2^31 bytes): rows past the end read zeros and
+  // drop their stores in hardware, and the lane offsets stay uniform.
+  // Target of the loads in flight: batch row tb, this wave's head th, group tg,
+  // first token tt (tt >= L: none; every load reads zeros).
   int tb = 0, th = 0, tg = 0, tt = 0;
   auto tgt_rsrc = [&](const uint16_t* base, uint32_t bat, uint32_t col, uint32_t rowb, bool on = true) {
     const int left = on ? L - tt : 0;
     return rsrc((const char*)(base + (uint64_t)tb * bat + col) + (uint32_t)tt * rowb,
                 left > 0 ? (uint32_t)left * rowb - col * 2 : 0u);
   };
-  auto load_b = [&](Prefetch& pf) {
+  auto load_b = [&](Prefetch<HPW>& pf) {
     const __amdgpu_buffer_rsrc_t rB = tgt_rsrc(k.B, bc_bat, (uint32_t)tg * NS, bc_row);
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-      pf.b[it] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(bc_lane + it * 4 * bc_row), 0, 0);
+    for (int it = 0; it < BCIT; ++it)
+      pf.b[it] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(bc_lane + it * 16 * HPW * bc_row), 0, 0);
   };
-  auto load_c = [&](Prefetch& pf) {
+  auto load_c = [&](Prefetch<HPW>& pf) {
     const __amdgpu_buffer_rsrc_t rC = tgt_rsrc(k.C, bc_bat, (uint32_t)tg * NS, bc_row);
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
-      pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bc_lane + it * 4 * bc_row), 0, 0);
+    for (int it = 0; it < BCIT; ++it)
+      pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bc_lane + it * 16 * HPW * bc_row), 0, 0);
   };
-  auto load_x = [&](Prefetch& pf) {
+  auto load_x = [&](Prefetch<HPW>& pf) {
     const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
-    // only the decay wave uses dt: the other waves' resource is empty (no memory access)
-    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, w == kDecayWave);
+    // only the decay wave of a head uses dt: the other waves' resource is empty (no memory access)
+    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, wq == kDecayWave);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
       pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(x_lane + it * 8 * xz_row), 0, 0);
     pf.dt = __builtin_amdgcn_raw_buffer_load_b16(rD, (int)dt_lane, 0, 0);
   };
   // z of the target chunk, staged like x (without a gate: loads of x, unused)
-  auto load_z = [&](Prefetch& pf) {
+  auto load_z = [&](Prefetch<HPW>& pf) {
     const __amdgpu_buffer_rsrc_t rZ = tgt_rsrc(gate ? k.z : k.x, xz_bat, (uint32_t)th * P, xz_row);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
@@ -299,12 +312,13 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   auto store_y = [&]() {
 #pragma unroll
     for (int it = 0; it < 2; ++it)
-      __builtin_amdgcn_raw_buffer_store_b128(lds128(sY + (x_r + 8 * it) * LDX + x_p * 8), ry_prev,
+      __builtin_amdgcn_raw_buffer_store_b128(lds128(sY[hs] + (x_r + 8 * it) * LDX + x_p * 8), ry_prev,
                                              (int)(x_lane + it * 8 * xz_row), 0, 2);
   };
 
-  // The current item: chain (b, h) of group g, chunks [c, c_end); per-head constants.
-  int b = 0, h = 0, g = 0, c = 0, c_end = 0;
+  // The current item: chain hc (heads hc HPW .. hc HPW + HPW - 1 of batch row b) and this
+  // wave's head h of group g, chunks [c, c_end); per-head constants.
+  int b = 0, hc = 0, h = 0, g = 0, c = 0, c_end = 0;
   int seg = 0;
   float A2 = 0.f, bias = 0.f, Dh = 0.f;
   auto set_item = [&](int it) {
@@ -312,9 +326,10 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     const int nch = qchains();
     seg = it / nch;
     const int ch = qfirst() + it % nch;
-    b = ch / H;
-    h = ch % H;
-    g = h / kk->heads_per_group;
+    b = ch / hpc;
+    hc = ch % hpc;
+    h = hc * HPW + hs;
+    g = h / kk->heads_per_group;  // the host guarantees the chain's heads share a group
     c = seg * kk->seg_chunks;
     c_end = min(c + kk->seg_chunks, max((L + Q - 1) / Q, 1));  // seqlen 0: one empty chunk
     A2 = -expf(kk->A_log[h]) * kLog2e;  // decay per unit step, exp2 domain
@@ -322,44 +337,46 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     Dh = kk->D[h];
   };
 
-  // Chunk at token tt from the prefetch registers into LDS; wave kDecayWave adds the
-  // steps, their inclusive cumulative sum (exp2 domain) and the derived decays.
-  auto stage = [&](Prefetch& pf) {
+  // Chunk at token tt from the prefetch registers into LDS; wave kDecayWave of each
+  // head adds that head's steps, their inclusive cumulative sum (exp2 domain) and the
+  // derived decays.
+  auto stage = [&](Prefetch<HPW>& pf) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      *(u32x4*)(sB + (bc_r + 4 * it) * LDB + bc_p * 8) = pf.b[it];
-      *(u32x4*)(sC + (bc_r + 4 * it) * LDC + bc_p * 8) = pf.c[it];
+    for (int it = 0; it < BCIT; ++it) {
+      const int row = bc_r + 16 * HPW * it;
+      *(u32x4*)(sB + row * LDB + bc_p * 8) = pf.b[it];
+      *(u32x4*)(sC + row * LDC + bc_p * 8) = pf.c[it];
       // states 8 bc_p + e: piece q = bc_p % 4 of the 32 states 32kb.. (kb = bc_p / 4)
       // goes to positions 32kb + 16 (q % 2) + 4 (q / 2) and 8 further on
       const int pk = 32 * (bc_p >> 2) + 16 * (bc_p & 1) + 4 * ((bc_p >> 1) & 1);
-      *(u32x2*)(sCk + (bc_r + 4 * it) * LDC + pk) = u32x2{pf.c[it][0], pf.c[it][1]};
-      *(u32x2*)(sCk + (bc_r + 4 * it) * LDC + pk + 8) = u32x2{pf.c[it][2], pf.c[it][3]};
+      *(u32x2*)(sCk + row * LDC + pk) = u32x2{pf.c[it][0], pf.c[it][1]};
+      *(u32x2*)(sCk + row * LDC + pk + 8) = u32x2{pf.c[it][2], pf.c[it][3]};
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      *(u32x4*)(sX + (x_r + 8 * it) * LDX + x_p * 8) = pf.x[it];
-      *(u32x4*)(sZ + (x_r + 8 * it) * LDX + x_p * 8) = pf.z[it];
+      *(u32x4*)(sX[hs] + (x_r + 8 * it) * LDX + x_p * 8) = pf.x[it];
+      *(u32x4*)(sZ[hs] + (x_r + 8 * it) * LDX + x_p * 8) = pf.z[it];
     }
-    if (w == kDecayWave) {
+    if (wq == kDecayWave) {
       const int nt_valid = max(0, min(Q, L - tt));
       const float dtv = l < nt_valid ? softplus(lo_f(pf.dt) + bias) : 0.0f;  // past the end: a zero step
       const float cs = wave_inclusive_sum(dtv * A2);
       const float cs_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
-      sDT[l] = dtv;
-      sCS[l] = cs;
-      sE[l] = fast_exp2(cs);
-      sW[kslot(l)] = fast_exp2(cs_last - cs) * dtv;  // in k order
+      sDT[hs][l] = dtv;
+      sCS[hs][l] = cs;
+      sE[hs][l] = fast_exp2(cs);
+      sW[hs][kslot(l)] = fast_exp2(cs_last - cs) * dtv;  // in k order
     }
   };
 
-  // state slice: hacc[nt][r] = S[p = 16w + li][n = 16nt + 4lg + r]; stored as [chain, p, n]
+  // state slice: hacc[nt][r] = S[p = 16wq + li][n = 16nt + 4lg + r] of head h; stored as [b, h, p, n]
   f32x4 hacc[8];
-  const int64_t s_lane = (int64_t)(16 * w + li) * NS + 4 * lg;
+  const int64_t s_lane = (int64_t)(16 * wq + li) * NS + 4 * lg;
   // The entering state of the current item: the caller's (or zeros) for a first
-  // segment, else the one the previous segment left in carry, once its flag says
-  // so. The producer of that segment holds an item dequeued earlier than this
-  // one, so it is running and never waits on this workgroup: the wait ends. Its
-  // bound (2^20 polls, about a second) only guarantees that the kernel
+  // segment, else the one the previous segment left in carry, once its chain's
+  // flag says so. The producer of that segment holds an item dequeued earlier
+  // than this one, so it is running and never waits on this workgroup: the wait
+  // ends. Its bound (2^20 polls, about a second) only guarantees that the kernel
   // terminates; a wait that gives up raises queue[128], which ends every other
   // wait, and starts its item from a NaN state: every output that depends on a
   // hand-off that did not happen (the rest of that chain's y and its final
@@ -370,7 +387,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
   // carry moves in 16-byte pieces, so the write-through goes out in whole
   // 64-byte segments.
   auto state_in = [&]() {
-    const int64_t ch = (int64_t)b * H + h;
+    const int64_t ch = (int64_t)b * hpc + hc;  // the chain: its flag
+    const int64_t hh = (int64_t)b * H + h;     // this wave's head: its state
     if (seg > 0) {
       if (tid == 0) {
         unsigned* flag = kargs()->queue + 256 + ch;
@@ -388,14 +406,14 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{NAN, NAN, NAN, NAN};
       } else {
-        const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + ch * (P * NS), P * NS * 4);
+        const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + hh * (P * NS), P * NS * 4);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
           hacc[nt] = __builtin_bit_cast(
               f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
       }
     } else if (kargs()->h0) {
-      const float* src = kargs()->h0 + ch * (P * NS) + s_lane;
+      const float* src = kargs()->h0 + hh * (P * NS) + s_lane;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
     } else {
@@ -408,12 +426,13 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
   };
   // The leaving state: to the caller after the last segment, else to carry and
-  // then the flag. Every thread waits until its stores are complete (visible to
-  // the device) before the barrier; thread 0 raises the flag after it.
+  // then the chain's flag. Every thread waits until its stores are complete
+  // (visible to the device) before the barrier; thread 0 raises the flag after it.
   auto state_out = [&]() {
-    const int64_t ch = (int64_t)b * H + h;
+    const int64_t ch = (int64_t)b * hpc + hc;
+    const int64_t hh = (int64_t)b * H + h;
     if (seg + 1 < kargs()->nseg) {
-      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + ch * (P * NS), P * NS * 4);
+      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + hh * (P * NS), P * NS * 4);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hacc[nt]), rS, (int)((s_lane + 16 * nt) * 4), 0,
@@ -422,18 +441,18 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       __syncthreads();
       if (tid == 0) __hip_atomic_store(kargs()->queue + 256 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      float* dst = kargs()->h_out + ch * (P * NS) + s_lane;
+      float* dst = kargs()->h_out + hh * (P * NS) + s_lane;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
     }
   };
 
   // the tiles of M above the diagonal block row stay zero
-  for (int e = tid; e < Q * LDM; e += 256) sM[e] = 0;
+  for (int e = tid; e < HPW * Q * LDM; e += 256 * HPW) (&sM[0][0])[e] = 0;
 
   set_item(cur);
   tb = b; th = h; tg = g; tt = c * Q;
-  Prefetch pf;
+  Prefetch<HPW> pf;
   load_b(pf);
   load_c(pf);
   load_x(pf);
@@ -457,8 +476,8 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       tt = t0 + Q;
     } else if (nxt >= 0) {
       const int qn = qchains(), ns = nxt / qn, nch = qfirst() + nxt % qn;
-      tb = nch / H;
-      th = nch % H;
+      tb = nch / hpc;
+      th = (nch % hpc) * HPW + hs;
       tg = th / kargs()->heads_per_group;
       tt = ns * kargs()->seg_chunks * Q;
       if (tid == 0) ticket = (int)atomicAdd(qcounter(), 1u);  // the item after that
@@ -475,27 +494,27 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = 32 * kb + 8 * lg;
-      const u32x2 lo = lds_tr(sX + (k0 + 2 * (li >> 2)) * LDX + 16 * w + 4 * (li & 3));
-      const u32x2 hi = lds_tr(sX + (k0 + 1 + 2 * (li >> 2)) * LDX + 16 * w + 4 * (li & 3));
+      const u32x2 lo = lds_tr(sX[hs] + (k0 + 2 * (li >> 2)) * LDX + 16 * wq + 4 * (li & 3));
+      const u32x2 hi = lds_tr(sX[hs] + (k0 + 1 + 2 * (li >> 2)) * LDX + 16 * wq + 4 * (li & 3));
       xa[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
     u32x2 xe[4], zkeep[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      xe[it] = lds64(sX + (16 * it + li) * LDX + 16 * w + 4 * lg);
-      zkeep[it] = lds64(sZ + (16 * it + li) * LDX + 16 * w + 4 * lg);
+      xe[it] = lds64(sX[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
+      zkeep[it] = lds64(sZ[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
     }
 
-    // ---- G^T tiles -> M (lower triangle): wave w takes tiles w, w+4, w+8. Waves 2
-    // and 3 have no tile w+8 and compute tile w twice, writing the same values
-    // again: a branch around the third tile would split the phase into pieces
-    // that each wait for all of their LDS reads.
+    // ---- G^T tiles -> M (lower triangle), each masked with every head's decays:
+    // wave w takes tiles w, w + NW, w + 2 NW. A wave with fewer tiles computes its
+    // first tile again, writing the same values again: a branch around a tile would
+    // split the phase into pieces that each wait for all of their LDS reads.
     {
-      f32x4 acc[3];
-      int Jt[3], It[3];
+      f32x4 acc[NT];
+      int Jt[NT], It[NT];
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int ti = w + 4 * u < 10 ? w + 4 * u : w;
+      for (int u = 0; u < NT; ++u) {
+        const int ti = w + NW * u < 10 ? w + NW * u : w;
         // ti -> (Jt, It), It >= Jt: (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
         Jt[u] = ti < 4 ? 0 : (ti < 7 ? 1 : (ti < 9 ? 2 : 3));
         It[u] = ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3));
@@ -504,39 +523,44 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
       // the mask's cumulative sums and steps, read before the MFMAs so that their
       // latency hides behind them (the scheduler would otherwise sink the reads to
       // their use)
-      float csi[3];
-      f32x4 csj[3], dtj[3];
+      float csi[HPW][NT];
+      f32x4 csj[HPW][NT], dtj[HPW][NT];
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        csi[u] = sCS[16 * It[u] + li];
-        csj[u] = *(const f32x4*)(sCS + 16 * Jt[u] + 4 * lg);
-        dtj[u] = *(const f32x4*)(sDT + 16 * Jt[u] + 4 * lg);
-      }
+      for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          csi[hh][u] = sCS[hh][16 * It[u] + li];
+          csj[hh][u] = *(const f32x4*)(sCS[hh] + 16 * Jt[u] + 4 * lg);
+          dtj[hh][u] = *(const f32x4*)(sDT[hh] + 16 * Jt[u] + 4 * lg);
+        }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
+        for (int u = 0; u < NT; ++u) {
           const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt[u] + li) * LDB + 32 * kb + 8 * lg));
           const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDC + 32 * kb + 8 * lg));
           acc[u] = mfma(a, bb, acc[u]);
         }
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
+      for (int u = 0; u < NT; ++u) {
         // acc[r] = G[i][j], i = 16It + li, j = 16Jt + 4lg + r
         const int i = 16 * It[u] + li;
-        float m[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * Jt[u] + 4 * lg + r;
-          // computed for every lane and selected (the clamp keeps masked entries finite)
-          const float v = acc[u][r] * fast_exp2(fminf(csi[u] - csj[u][r], 0.0f)) * dtj[u][r];
-          m[r] = j <= i ? v : 0.0f;
+        for (int hh = 0; hh < HPW; ++hh) {
+          float m[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * Jt[u] + 4 * lg + r;
+            // computed for every lane and selected (the clamp keeps masked entries finite)
+            const float v = acc[u][r] * fast_exp2(fminf(csi[hh][u] - csj[hh][u][r], 0.0f)) * dtj[hh][u][r];
+            m[r] = j <= i ? v : 0.0f;
+          }
+          // columns in k order: j = 16Jt + 4lg + r sits at 16Jt + 8(lg/2) + kslot(4(lg%2) + r)
+          uint16_t* row = sM[hh] + i * LDM + 16 * Jt[u] + 8 * (lg >> 1) + 2 * (lg & 1);
+          *(uint32_t*)row = pack2(m[0], m[2]);
+          *(uint32_t*)(row + 4) = pack2(m[1], m[3]);
         }
-        // columns in k order: j = 16Jt + 4lg + r sits at 16Jt + 8(lg/2) + kslot(4(lg%2) + r)
-        uint16_t* row = sM + i * LDM + 16 * Jt[u] + 8 * (lg >> 1) + 2 * (lg & 1);
-        *(uint32_t*)row = pack2(m[0], m[2]);
-        *(uint32_t*)(row + 4) = pack2(m[1], m[3]);
       }
     }
 
@@ -547,14 +571,14 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
     // the row scales and the state update's weights, read before the MFMAs
     float ei[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) ei[it] = sE[16 * it + li];
+    for (int it = 0; it < 4; ++it) ei[it] = sE[hs][16 * it + li];
     f32x4 wj[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      wj[kb][0] = *(const f32x4*)(sW + 32 * kb + 8 * lg);
-      wj[kb][1] = *(const f32x4*)(sW + 32 * kb + 8 * lg + 4);
+      wj[kb][0] = *(const f32x4*)(sW[hs] + 32 * kb + 8 * lg);
+      wj[kb][1] = *(const f32x4*)(sW[hs] + 32 * kb + 8 * lg + 4);
     }
-    const float dec_last = sE[Q - 1];
+    const float dec_last = sE[hs][Q - 1];
     __builtin_amdgcn_sched_barrier(0);
     f32x4 yacc[4];
 #pragma unroll
@@ -580,7 +604,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 
     load_x(pf);
     // ---- S = exp(cs_last) S + B^T (w x). A operand: B^T rows n = 16nt + li, k = j
-    // (transposing loads of B); B operand: w_j x[j][16w + li] from the x^T fragments
+    // (transposing loads of B); B operand: w_j x[j][16wq + li] from the x^T fragments
     // (both in k order; sW holds w in k order).
     bf16x8 wxb[2];
 #pragma unroll
@@ -613,11 +637,11 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (kb == 1 && it < 2) continue;
-        const bf16x8 mb = as_bf16x8(lds128(sM + (16 * it + li) * LDM + 32 * kb + 8 * lg));
+        const bf16x8 mb = as_bf16x8(lds128(sM[hs] + (16 * it + li) * LDM + 32 * kb + 8 * lg));
         yacc[it] = mfma(as_bf16x8(xa[kb]), mb, yacc[it]);
       }
     }
-    // ---- epilogue: lane holds y[i = 16it + li][16w + 4lg + r]; y = (Y + D x) silu(z)
+    // ---- epilogue: lane holds y[i = 16it + li][16wq + 4lg + r]; y = (Y + D x) silu(z)
     {
       const __amdgpu_buffer_rsrc_t rY = rsrc((const char*)(k.y + (uint64_t)b * xz_bat + h * P) + (uint32_t)t0 * xz_row,
                                              (uint32_t)(L - t0) * xz_row - h * P * 2);
@@ -628,7 +652,7 @@ __global__ __launch_bounds__(256, 2) void ssd_chunk_kernel(SsdK k) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = fmaf(Dh, xs[r], yacc[it][r]) * (gate ? silu(zs[r]) : 1.0f);
-        *(u32x2*)(sY + (16 * it + li) * LDX + 16 * w + 4 * lg) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+        *(u32x2*)(sY[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
       }
       ry_prev = rY;
     }
@@ -676,7 +700,7 @@ namespace {
 // the load: the cost model counts rounds of items over one workgroup per unit,
 // plus one chunk of overhead per item.
 struct SsdPlan {
-  int nchains, seg_chunks, nseg, nq, grid;
+  int hpw, nchains, seg_chunks, nseg, nq, grid;
   size_t queue_bytes, ws_bytes;
 };
 
@@ -686,13 +710,20 @@ SsdPlan ssd_plan(const SSDArgs& a) {
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
     ncu = 256;
   SsdPlan p{};
-  const int64_t nchains = a.batch * a.H, nchunks = std::max<int64_t>((a.L + Q - 1) / Q, 1);
+  // One head per workgroup. Two (a chain is then a pair of neighbouring heads of one
+  // batch row that share a group of B and C) on request: measured at the Mamba-2 2.7B
+  // layer they are 5-10% slower, the second wave per SIMD adding LDS waits rather
+  // than hiding latency.
+  const int64_t hpg = a.H / a.G;
+  p.hpw = (knob(kKnobSsdHeadsPerWorkgroup) == 2 && a.H % 2 == 0 && hpg % 2 == 0) ? 2 : 1;
+  const int64_t nchains = a.batch * a.H / p.hpw, nchunks = std::max<int64_t>((a.L + Q - 1) / Q, 1);
   p.nchains = (int)nchains;
-  int64_t grid = nchains < 2 * (int64_t)ncu ? ncu : 2 * ncu;  // two per unit (the occupancy the
-                                                               // kernel is built for) with many chains
+  // Two workgroups per unit (the occupancy the one-head kernel is built for) with
+  // many chains; the two-head kernel fills a unit's LDS with one.
+  int64_t grid = (p.hpw == 1 && nchains >= 2 * (int64_t)ncu) ? 2 * ncu : ncu;
   int64_t best_seg = nchunks, best_ns = 1;
   auto queues = [&](int64_t g) { return std::max<int64_t>(1, std::min<int64_t>({8, nchains, g})); };
-  if (nchains < 2 * (int64_t)ncu) {
+  if (nchains < (p.hpw == 1 ? 2 : 1) * (int64_t)ncu) {
     // rounds of items in the fullest queue over its workgroups
     const int64_t nq = queues(grid), qch = (nchains + nq - 1) / nq, qwg = std::max<int64_t>(grid / nq, 1);
     auto cost = [&](int64_t sc, int64_t ns) {
@@ -724,7 +755,7 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   const int64_t qitems = best_ns * ((nchains + p.nq - 1) / p.nq);
   p.grid = (int)std::min<int64_t>(grid, (int64_t)p.nq * qitems);
   p.queue_bytes = ((size_t)(256 + p.nchains) * 4 + 255) / 256 * 256;
-  p.ws_bytes = p.queue_bytes + (p.nseg > 1 ? (size_t)p.nchains * P * NS * 4 : 0);
+  p.ws_bytes = p.queue_bytes + (p.nseg > 1 ? (size_t)(a.batch * a.H) * P * NS * 4 : 0);
   return p;
 }
 
@@ -753,7 +784,10 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   const int nwords = 256 + p.nchains;
   hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nwords + 255) / 256)), dim3(256), 0, s, k.queue,
                      nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
-  hipLaunchKernelGGL(ssd_chunk_kernel, dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+  if (p.hpw == 2)
+    hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);
+  else
+    hipLaunchKernelGGL(ssd_chunk_kernel<1>, dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
   return hipGetLastError();
 }
 

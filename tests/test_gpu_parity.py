@@ -524,3 +524,28 @@ def test_prompt_entry_points_replayed_from_a_hip_graph():
         for i, (o, e) in enumerate(zip(outs, eager)):
             assert torch.equal(o, e), (rep, i)
     check_all(s, (host(eager[0]), host(eager[1])), oracle.run_inputs(s), "ssd")
+
+
+HPW_CASES = [
+    # batch, seqlen, H, G, gate, h0, segment chunks (0: the plan's)
+    (2, 1000, 8, 1, True, True, 0),
+    (1, 777, 16, 8, True, False, 3),    # two heads per group: pairs never straddle groups
+    (2, 300, 6, 3, False, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", HPW_CASES, ids=lambda c: "b%d_L%d_H%d_G%d_g%d_h%d_seg%d" % c)
+def test_ssd_two_heads_per_workgroup_equals_one(case, tuning):
+    """The chunk kernel with two heads per workgroup (shared B, C and C B^T tiles) against
+    the same kernel with one head per workgroup: each head's arithmetic is the same, so the
+    results are bit-identical; both against the oracle."""
+    b, L, H, G, gate, h0, seg = case
+    say("ssd heads per workgroup", case)
+    if seg:
+        tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, seg)
+    inp = gen.make_ssd(b, L, H, 64, 128, G, act="bf16", seed=L + H + G, gate=gate, h0=h0)
+    one = run_ssd(inp)
+    tuning(bd.TUNE_SSD_HEADS_PER_WORKGROUP, 2)
+    two = run_ssd(inp)
+    assert np.array_equal(two[0], one[0]) and np.array_equal(two[1], one[1])
+    check_all(inp, two, oracle.run_inputs(inp), "ssd")
