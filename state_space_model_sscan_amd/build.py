@@ -15,7 +15,8 @@ SOURCES = ["api.cpp", "tokenloop.hip", "m1_fast.hip", "tl_m1_f32.hip", "tl_m1_bf
            "tl_ssd_bf16.hip", "m1f_f32_16.hip", "m1f_f32_32.hip", "m1f_f32_64.hip", "m1f_bf16_16.hip",
            "m1f_bf16_32.hip", "m1f_bf16_64.hip", "m1r_f32_16.hip", "m1r_f32_32.hip", "m1r_f32_64.hip",
            "m1r_bf16_16.hip", "m1r_bf16_32.hip", "m1r_bf16_64.hip", "ssd_chunk.hip", "mixer_ops.hip", "ssd_attention.hip",
-           "scratch.hip"]
+           "scratch.hip", "m1q_f32_16.hip", "m1q_f32_32.hip", "m1q_f32_64.hip", "m1q_bf16_16.hip", "m1q_bf16_32.hip",
+           "m1q_bf16_64.hip"]
 ARCH = os.environ.get("SSCAN_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU instructions are switched off for every device pass.

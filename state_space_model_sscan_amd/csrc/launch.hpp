@@ -48,6 +48,11 @@ Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t 
 Mamba1Plan tokenloop_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N);  // token-loop kernel
 hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const float* ws_h, const float* ws_sdt,
                           hipStream_t s);
+// Shapes the quad-lane kernel takes: state_dim 16, 32 or 64 and channels in whole
+// 16-byte pieces (es: bytes per activation).
+inline bool m1_quad_ok(int64_t N, int64_t Dc, int64_t es) {
+  return (N == 16 || N == 32 || N == 64) && Dc % (16 / es) == 0;
+}
 
 hipError_t launch_mamba1_fwd(const Mamba1Args& a, const Mamba1Plan& plan, void* ws, hipStream_t s);
 hipError_t launch_mamba1_step(const Mamba1Args& a, hipStream_t s);

@@ -1,7 +1,14 @@
 // m1_fast.hip -- host launch of the Mamba-1 prompt kernel (m1_fast_impl.hpp).
-#include "m1_row_impl.hpp"
+#include "m1_quad_impl.hpp"
 
 namespace sscan {
+
+extern template void launch_m1_quad_np<float, 16>(const M1F&, bool, bool, dim3, hipStream_t);
+extern template void launch_m1_quad_np<float, 32>(const M1F&, bool, bool, dim3, hipStream_t);
+extern template void launch_m1_quad_np<float, 64>(const M1F&, bool, bool, dim3, hipStream_t);
+extern template void launch_m1_quad_np<uint16_t, 16>(const M1F&, bool, bool, dim3, hipStream_t);
+extern template void launch_m1_quad_np<uint16_t, 32>(const M1F&, bool, bool, dim3, hipStream_t);
+extern template void launch_m1_quad_np<uint16_t, 64>(const M1F&, bool, bool, dim3, hipStream_t);
 
 extern template void launch_m1_np<float, 16>(const M1F&, int, bool, bool, dim3, hipStream_t);
 extern template void launch_m1_np<float, 32>(const M1F&, int, bool, bool, dim3, hipStream_t);
@@ -40,6 +47,19 @@ hipError_t launch_m1_fast(const Mamba1Args& a, const Mamba1Plan& plan, const flo
       if (np == 16) launch_m1_row_np<float, 16>(k, gate, st, grid, dyn, s);
       else if (np == 32) launch_m1_row_np<float, 32>(k, gate, st, grid, dyn, s);
       else launch_m1_row_np<float, 64>(k, gate, st, grid, dyn, s);
+    }
+    return hipGetLastError();
+  }
+  if (K == 4 && m1_quad_ok(a.N, a.Dc, a.bf16 ? 2 : 4)) {  // a quad per channel, 64 channels per 256-thread block
+    const dim3 grid((unsigned)(((a.Dc + 63) / 64) * plan.nslices * a.batch));
+    if (a.bf16) {
+      if (np == 16) launch_m1_quad_np<uint16_t, 16>(k, gate, st, grid, s);
+      else if (np == 32) launch_m1_quad_np<uint16_t, 32>(k, gate, st, grid, s);
+      else launch_m1_quad_np<uint16_t, 64>(k, gate, st, grid, s);
+    } else {
+      if (np == 16) launch_m1_quad_np<float, 16>(k, gate, st, grid, s);
+      else if (np == 32) launch_m1_quad_np<float, 32>(k, gate, st, grid, s);
+      else launch_m1_quad_np<float, 64>(k, gate, st, grid, s);
     }
     return hipGetLastError();
   }

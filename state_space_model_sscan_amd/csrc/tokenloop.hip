@@ -77,13 +77,15 @@ static hipError_t zero_length(const float* h0, float* h_out, int64_t nst, hipStr
   return hipGetLastError();
 }
 
-// Mamba-1 prompt plan. With state_dim 16, 32 or 64 and channels in groups of 4
-// the row-per-channel kernel (16 lanes per channel) runs: measured on MI355X it
-// beats four lanes per channel at the Mamba-130m width (1.5x, where four lanes
-// leave a quarter of the SIMDs empty) and at the Falcon-Mamba-7b width. Other
-// shapes take K = 1, 2 or 4 lanes per channel, the smallest K that puts two
-// waves on each of the 1024 SIMDs. Slices (two-pass carry) only when the grid
-// still has fewer than 512 waves on a long sequence.
+// Mamba-1 prompt plan. With state_dim 16, 32 or 64: the quad-lane kernel (4
+// lanes per channel) when its grid still puts two waves on every one of the 1024
+// SIMDs (it spends fewer VALU instructions per state update), else the
+// row-per-channel kernel (16 lanes per channel, channels in groups of 4), which
+// at the Mamba-130m width keeps three waves per SIMD where four lanes would leave
+// a quarter of the SIMDs empty. Other shapes take K = 1, 2 or 4 lanes per channel
+// of the general kernel, the smallest K that puts two waves on each SIMD. Slices
+// (two-pass carry) only when the grid still has fewer than 512 waves on a long
+// sequence.
 Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t G, int64_t es) {
   // a batch row (of x/dt/z/y, or of B/C) that the 32-bit buffer offsets of the
   // fast kernels cannot span: token-loop kernel
@@ -99,9 +101,11 @@ Mamba1Plan mamba1_plan(int64_t batch, int64_t L, int64_t Dc, int64_t N, int64_t 
   // the row-per-channel kernel (16 lanes) takes state_dim 16, 32 or 64 and
   // channels in whole groups of 4
   const bool row_ok = (N == 16 || N == 32 || N == 64) && Dc % 4 == 0;
+  const bool quad_ok = m1_quad_ok(N, Dc, es);
   int64_t K = N > 32 ? 2 : 1;  // 64 states in one lane would spill
   while (K < 4 && waves(K) < 2048) K *= 2;
-  if (row_ok) K = 16;
+  if (quad_ok && waves(4) >= 2048) K = 4;
+  else if (row_ok) K = 16;
   {  // tuning override: 1, 2, 4 or 16 lanes per channel
     const int64_t v = knob(kKnobM1Lanes);
     if ((v == 1 && N <= 32) || v == 2 || v == 4 || (v == 16 && row_ok)) K = v;

@@ -76,15 +76,19 @@ def test_mamba1_small(case):
     check_all(inp, run_mamba1(inp), oracle.run_inputs(inp), "mamba1", states=states)
 
 
-# The plan gives state_dim 16/32/64 (with channels in groups of 4) to the
-# row-per-channel kernel; these cases force the 1/2/4-lanes-per-channel kernel,
-# which the other shapes take, through its tuning override.
+# The plan gives state_dim 16/32/64 to the quad-lane kernel on wide shapes and to the
+# row-per-channel kernel on the others; these cases force the kernel through the
+# lanes-per-channel override: 4 selects the quad-lane kernel (state_dim 16/32/64,
+# channels in whole 16-byte pieces), 1 and 2 the general kernel.
 LANE_CASES = [
     # lanes, batch, seqlen, channels, N, act, gate, h0, states, bc_eps
     (1, 2, 300, 256, 16, "bf16", True, True, False, 1e-6),
     (2, 3, 129, 192, 32, "f32", True, False, True, 0.0),
     (4, 2, 1000, 128, 16, "f32", False, True, False, 0.0),
     (4, 1, 77, 64, 64, "bf16", True, True, True, 1e-5),
+    (4, 3, 300, 136, 16, "bf16", True, True, True, 1e-6),   # a part-filled block of 64 channels
+    (4, 1, 3000, 64, 32, "f32", True, True, False, 0.0),    # several slices
+    (4, 2, 257, 200, 64, "bf16", False, False, True, 0.0),  # ragged tile, per-token states
 ]
 
 
