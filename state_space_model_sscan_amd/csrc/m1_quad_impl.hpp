@@ -46,13 +46,6 @@ __device__ __forceinline__ float qb(float v) {
                                                     0xF, false));
 }
 
-template <typename T> __device__ __forceinline__ float to_f(T v);
-template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
-template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
-template <typename T> __device__ __forceinline__ T from_f(float v);
-template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float v) { return f32_to_bf16(v); }
-template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
-
 }  // namespace quad
 
 template <typename T, int NP, bool GATE, bool STATES>

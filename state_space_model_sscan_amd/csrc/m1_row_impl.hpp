@@ -132,19 +132,32 @@ struct RawVec {
   }
 };
 
+namespace quad {
+// activations as stored (bf16 bits or fp32) to fp32 and back (round to nearest even)
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float v) { return f32_to_bf16(v); }
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+}  // namespace quad
+
 template <typename T, int NP, bool GATE, bool STATES>
 __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
   constexpr int NPL = NP / 16;  // state entries per lane
   constexpr int NQ = NP / 4;    // B/C entries a thread stages (4 threads per token)
-  constexpr int TILE = 64;
+  constexpr int RT = 2;         // token rows a thread stages per tile
+  constexpr int TILE = 64 * RT;
   constexpr int TP = TILE + 4;  // LDS pitch (floats) of a state entry's row of tokens
-  constexpr int XP = 20;        // LDS pitch (floats) of a token's 16 channels
+  // LDS pitch (elements) of a token's 16 channels, kept as loaded: 40 bytes for
+  // bf16, so that the 16 token rows a wave reads at once fall on distinct banks
+  constexpr int XP = 20;
   constexpr uint32_t ES = sizeof(T);
   constexpr int WA = ES;           // dwords of 4 activations
   constexpr int WQ = NQ * ES / 4;  // dwords of a thread's B (or C) entries
   __shared__ __attribute__((aligned(16))) float sBC[2][NP][TP];  // [B, C][entry][token]
-  __shared__ __attribute__((aligned(16))) float sX[3][TILE][XP];  // [x, dt, z][token][channel]
-  __shared__ __attribute__((aligned(16))) float sY[TILE][XP];     // [token][channel]
+  __shared__ __attribute__((aligned(16))) T sX[3][TILE][XP];      // [x, dt, z][token][channel]
+  __shared__ __attribute__((aligned(16))) T sY[TILE][XP];         // [token][channel]
 
   const int tid = threadIdx.x;
   const int n = tid & 15;   // lane in the channel's row; token of a group
@@ -200,60 +213,83 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
   const float inv_n = 1.0f / (float)k.N;
   const bool bc_norm = k.bc_eps > 0.0f;
 
+  // a thread's pieces: token rows tr + 64 r of the tile (r < RT)
+  auto rowo = [&](uint32_t o, int r, uint32_t row) { return o == kOOB ? kOOB : o + (uint32_t)(64 * r) * row; };
   struct Raw {
-    RawVec<WA> x, d, z;
-    RawVec<WQ> bq, cq;
+    RawVec<WA> x[RT], d[RT], z[RT];
+    RawVec<WQ> bq[RT], cq[RT];
   };
   auto load_raw = [&](Raw& r, int t0) {
-    r.x.load(tile_rsrc(xb, t0, row_bytes), vx);
-    r.d.load(tile_rsrc(db, t0, row_bytes), vx);
-    if (GATE) r.z.load(tile_rsrc(zb, t0, row_bytes), vx);
-    r.bq.load(tile_rsrc(Bb, t0, bc_row), vb);
-    r.cq.load(tile_rsrc(Cb, t0, bc_row), vb);
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xb, t0, row_bytes), rd = tile_rsrc(db, t0, row_bytes);
+    const __amdgpu_buffer_rsrc_t rz = tile_rsrc(zb, t0, row_bytes);
+    const __amdgpu_buffer_rsrc_t rB = tile_rsrc(Bb, t0, bc_row), rC = tile_rsrc(Cb, t0, bc_row);
+#pragma unroll
+    for (int q = 0; q < RT; ++q) {
+      r.x[q].load(rx, rowo(vx, q, row_bytes));
+      r.d[q].load(rd, rowo(vx, q, row_bytes));
+      if (GATE) r.z[q].load(rz, rowo(vx, q, row_bytes));
+      r.bq[q].load(rB, rowo(vb, q, bc_row));
+      r.cq[q].load(rC, rowo(vb, q, bc_row));
+    }
+  };
+  // 4 activations as loaded into LDS (8 bytes of bf16 or 16 of fp32)
+  auto put4 = [&](T* dst, RawVec<WA>& v) {
+    if constexpr (ES == 2) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{v.w[0], v.w[1]};
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{v.w[0], v.w[1], v.w[2], v.w[3]};
+    }
   };
   auto stage = [&](Raw& r) {
-    float v[4];
-    r.x.template unpack<T>(v);
-    *reinterpret_cast<f32x4*>(&sX[0][tr][4 * tq]) = f32x4{v[0], v[1], v[2], v[3]};
-    r.d.template unpack<T>(v);
-    *reinterpret_cast<f32x4*>(&sX[1][tr][4 * tq]) = f32x4{v[0], v[1], v[2], v[3]};
-    if (GATE) {
-      r.z.template unpack<T>(v);
-      *reinterpret_cast<f32x4*>(&sX[2][tr][4 * tq]) = f32x4{v[0], v[1], v[2], v[3]};
-    }
-    float bv[NQ], cv[NQ];
-    r.bq.template unpack<T>(bv);
-    r.cq.template unpack<T>(cv);
-    float sb = 0.0f, sc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      sb = fmaf(bv[j], bv[j], sb);
-      sc = fmaf(cv[j], cv[j], sc);
-    }
-    // the norm's scale, computed without a branch (1 when there is no norm)
-    sb += dpp_f<0xB1>(sb);  // sum over the token's four threads
-    sc += dpp_f<0xB1>(sc);
-    sb += dpp_f<0x4E>(sb);
-    sc += dpp_f<0x4E>(sc);
-    const float ib = bc_norm ? __builtin_amdgcn_rsqf(fmaf(sb, inv_n, k.bc_eps)) : 1.0f;
-    const float ic = bc_norm ? __builtin_amdgcn_rsqf(fmaf(sc, inv_n, k.bc_eps)) : 1.0f;
+    for (int q = 0; q < RT; ++q) {
+      const int row = tr + 64 * q;
+      put4(&sX[0][row][4 * tq], r.x[q]);
+      put4(&sX[1][row][4 * tq], r.d[q]);
+      if (GATE) put4(&sX[2][row][4 * tq], r.z[q]);
+      float bv[NQ], cv[NQ];
+      r.bq[q].template unpack<T>(bv);
+      r.cq[q].template unpack<T>(cv);
+      if (bc_norm) {  // uniform: the weightless RMS norm of B and C over the state entries
+        float sb = 0.0f, sc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      sBC[0][tq * NQ + j][tr] = bv[j] * ib;
-      sBC[1][tq * NQ + j][tr] = cv[j] * ic;
+        for (int j = 0; j < NQ; ++j) {
+          sb = fmaf(bv[j], bv[j], sb);
+          sc = fmaf(cv[j], cv[j], sc);
+        }
+        sb += dpp_f<0xB1>(sb);  // sum over the token's four threads
+        sc += dpp_f<0xB1>(sc);
+        sb += dpp_f<0x4E>(sb);
+        sc += dpp_f<0x4E>(sc);
+        const float ib = __builtin_amdgcn_rsqf(fmaf(sb, inv_n, k.bc_eps));
+        const float ic = __builtin_amdgcn_rsqf(fmaf(sc, inv_n, k.bc_eps));
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          bv[j] *= ib;
+          cv[j] *= ic;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        sBC[0][tq * NQ + j][row] = bv[j];
+        sBC[1][tq * NQ + j][row] = cv[j];
+      }
     }
   };
-  // y of the tile from t0 (complete in sY) to memory: 4 channels of a token per thread.
+  // y of the tile from t0 (complete in sY, in the output dtype) to memory: 4 channels
+  // of a token row per thread and row.
   auto store_y = [&](int t0) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&sY[tr][4 * tq]);
     const __amdgpu_buffer_rsrc_t ry = tile_rsrc(yb, t0, row_bytes);
-    if constexpr (ES == 2) {
-      const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                       (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, ry, (int)vx, 0, 0);
-    } else {
-      const u32x4 w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-      __builtin_amdgcn_raw_buffer_store_b128(w, ry, (int)vx, 0, 0);
+#pragma unroll
+    for (int q = 0; q < RT; ++q) {
+      const T* src = &sY[tr + 64 * q][4 * tq];
+      if constexpr (ES == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2*>(src), ry, (int)rowo(vx, q, row_bytes), 0,
+                                              0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), ry, (int)rowo(vx, q, row_bytes),
+                                               0, 0);
+      }
     }
   };
 
@@ -269,8 +305,8 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
         b4[q4][i] = *reinterpret_cast<const f32x4*>(&sBC[0][n + 16 * i][16 * j + 4 * q4]);
         c4[q4][i] = *reinterpret_cast<const f32x4*>(&sBC[1][n + 16 * i][16 * j + 4 * q4]);
       }
-    const float xv = sX[0][tl][cl];
-    const float sp = softplus_fast(sX[1][tl][cl] + bias);
+    const float xv = quad::to_f<T>(sX[0][tl][cl]);
+    const float sp = softplus_fast(quad::to_f<T>(sX[1][tl][cl]) + bias);
     const float dtv = tg + n < t_end ? sp : 0.0f;  // a token past the end is a zero step
     const float dtx = dtv * xv;
     float p[16];
@@ -296,8 +332,8 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
       }
     });
     float yv = row_transpose_sum(p, n) + Dv * xv;
-    if (GATE) yv *= silu(sX[2][tl][cl]);
-    sY[tl][cl] = yv;
+    if (GATE) yv *= silu(quad::to_f<T>(sX[2][tl][cl]));
+    sY[tl][cl] = quad::from_f<T>(yv);
   };
 
   // Per tile: barrier (the previous tile's compute is done: LDS free, its y
@@ -312,7 +348,7 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
     load_raw(raw, t0 + TILE);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) compute_group(t0, j);
+    for (int j = 0; j < TILE / 16; ++j) compute_group(t0, j);
   }
   __syncthreads();
   if (t_end > t_begin) store_y(t_begin + ((t_end - t_begin - 1) / TILE) * TILE);
