@@ -26,12 +26,17 @@
 // neighbouring head_dim columns of one token row; y then leaves through LDS as
 // whole rows.
 //
+// G = C B^T of a chunk is the same for every head of a group, so ssd_cb_kernel
+// computes it once per (batch row, chunk, group) before the scan: the ten
+// lower-triangular 16x16 tiles, fp32, in the layout of the MFMA result (see
+// there). The scan's waves load the tiles they mask one chunk ahead.
+//
 // Per chunk, between two barriers:
-//   after barrier A (chunk staged in LDS: B, C and x row-major, C once more in the
-//   k order of the S C^T operand, cumulative decay):
+//   after barrier A (chunk staged in LDS: B and x row-major, C in the k order of
+//   the S C^T operand, cumulative decay):
 //     - x^T fragments and the epilogue's x values move from LDS to registers;
-//     - G^T = B C^T on MFMA (10 lower-triangular 16x16 tiles over the 4 waves),
-//       masked and scaled into M[i, j] = G[i, j] exp(cs_i - cs_j) dt_j (bf16, LDS);
+//     - the chunk's G tiles (10 over the 4 waves) are masked and scaled into
+//       M[i, j] = G[i, j] exp(cs_i - cs_j) dt_j (bf16, LDS);
 //     - Y^T = S_in C^T (A operand straight from the state accumulators), columns
 //       scaled by exp(cs_i);
 //     - S = exp(cs_last) S + B^T (w x), w_j = exp(cs_last - cs_j) dt_j, with the
@@ -75,13 +80,15 @@ constexpr int P = 64;        // head_dim
 constexpr int NS = 128;      // state_dim
 constexpr int LDB = NS + 24;  // row pitch (bf16) of sB: 76 dwords = 12 mod 64, so the 4-row
                               // windows of the transposing loads hit distinct banks
-constexpr int LDC = NS + 16;  // row pitch of sC and sCk: 72 dwords, where 16-byte reads of
+constexpr int LDC = NS + 16;  // row pitch of sCk: 72 dwords, where 16-byte reads of
                               // 16 rows (the MFMA operands) are conflict-free
+constexpr int kTiles = 10;    // lower-triangular 16x16 tiles of a chunk's C B^T
+constexpr int kTileFloats = 256;  // one tile: 64 lanes x 4 fp32
 constexpr int LDX = P + 8;   // row pitch of sX
 constexpr int LDM = Q + 8;   // row pitch of sM
 constexpr size_t kCkBytes = (size_t)Q * LDC * 2;
 // The wave that computes the chunk's steps and decays while staging: one of the
-// two waves whose third G tile is a repeat (waves 0 and 1 have three tiles).
+// two waves whose third G tile is a repeat (waves 0 and 1 mask three tiles).
 constexpr int kDecayWave = 3;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -100,12 +107,14 @@ struct SsdK {
   const uint16_t* C;
   const float* D;
   const uint16_t* z;
+  const float* cb;  // C B^T tiles from ssd_cb_kernel: [batch, nchunks, G][10 tiles][64 lanes][4]
   const float* h0;
   uint16_t* y;
   float* h_out;
   unsigned* queue;  // [16 q]: next item of queue q; [128]: a wait gave up; [256 + ch]: segments of chain ch done
   float* carry;     // [batch * H, P, NS]: the state a segment hands to the next one, per head
   int64_t L, H, G;
+  int nchunks;      // chunks of 64 tokens per batch row (ceil(L / 64))
   int heads_per_group;
   int nchains;      // batch * H / HPW (a chain is a run of HPW heads of one batch row)
   int seg_chunks;   // chunks per segment
@@ -114,6 +123,11 @@ struct SsdK {
                     // [q nchains / nq, (q + 1) nchains / nq): item i of a queue with n chains is
                     // segment i / n of its chain i % n
 };
+
+// Tile ti of a chunk's lower triangle -> (row block It, column block Jt), It >= Jt:
+// (0,0) (1,0) (2,0) (3,0) (1,1) (2,1) (3,1) (2,2) (3,2) (3,3)
+__device__ __forceinline__ int tile_j(int ti) { return ti < 4 ? 0 : (ti < 7 ? 1 : (ti < 9 ? 2 : 3)); }
+__device__ __forceinline__ int tile_i(int ti) { return ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3)); }
 
 // Position of token t of a chunk in k order (see the note on the transposing load):
 // within each group of 8, token 8g + t sits at 8g + (t even ? t/2 : 4 + t/2).
@@ -185,6 +199,7 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 template <int HPW>
 struct Prefetch {
   u32x4 b[4 / HPW], c[4 / HPW], x[2], z[2];
+  f32x4 g[HPW == 1 ? 3 : 2];  // the C B^T tiles this wave masks
   uint32_t dt;  // raw bf16 bits
 };
 
@@ -192,17 +207,16 @@ struct Prefetch {
 
 // HPW heads of one batch row per workgroup (1 or 2), four waves per head. With two
 // heads, B and C (shared by every head of a group) are staged once and each C B^T
-// tile is computed once, then masked with each head's decays; the two heads' waves
+// tile is loaded once, then masked with each head's decays; the two heads' waves
 // share the SIMDs, so one head's MFMA and memory latencies hide behind the other's
 // work.
 template <int HPW>
 __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(SsdK k) {
   constexpr int NW = 4 * HPW;      // waves
   constexpr int BCIT = 4 / HPW;    // rows of B (and of C) a thread stages
-  constexpr int NT = HPW == 1 ? 3 : 2;  // C B^T tiles a wave computes (some repeated)
+  constexpr int NT = HPW == 1 ? 3 : 2;  // C B^T tiles a wave masks (some repeated)
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * LDC];
-  // C again, each row in the k order of the Y^T = S C^T operand: positions
+  // C, each row in the k order of the Y^T = S C^T operand: positions
   // 32kb + 8lg + e hold states 32kb + 4lg + e (e < 4) and 32kb + 16 + 4lg + e - 4
   // (e >= 4), so that operand is one 16-byte read (the state accumulators fix
   // that order)
@@ -289,6 +303,16 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     for (int it = 0; it < BCIT; ++it)
       pf.c[it] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)(bc_lane + it * 16 * HPW * bc_row), 0, 0);
   };
+  // the target chunk's C B^T tiles that this wave masks (past the end: none)
+  auto load_g = [&](Prefetch<HPW>& pf) {
+    const float* blk = kargs()->cb + (((int64_t)tb * kargs()->nchunks + tt / Q) * G + tg) * (kTiles * kTileFloats);
+    const __amdgpu_buffer_rsrc_t rG = rsrc(blk, tt < L ? kTiles * kTileFloats * 4 : 0u);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int ti = w + NW * u < kTiles ? w + NW * u : w;
+      pf.g[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rG, (ti * 64 + l) * 16, 0, 0));
+    }
+  };
   auto load_x = [&](Prefetch<HPW>& pf) {
     const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
     // only the decay wave of a head uses dt: the other waves' resource is empty (no memory access)
@@ -345,7 +369,6 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     for (int it = 0; it < BCIT; ++it) {
       const int row = bc_r + 16 * HPW * it;
       *(u32x4*)(sB + row * LDB + bc_p * 8) = pf.b[it];
-      *(u32x4*)(sC + row * LDC + bc_p * 8) = pf.c[it];
       // states 8 bc_p + e: piece q = bc_p % 4 of the 32 states 32kb.. (kb = bc_p / 4)
       // goes to positions 32kb + 16 (q % 2) + 4 (q / 2) and 8 further on
       const int pk = 32 * (bc_p >> 2) + 16 * (bc_p & 1) + 4 * ((bc_p >> 1) & 1);
@@ -455,6 +478,7 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   Prefetch<HPW> pf;
   load_b(pf);
   load_c(pf);
+  load_g(pf);
   load_x(pf);
   load_z(pf);
   stage(pf);
@@ -505,24 +529,19 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       zkeep[it] = lds64(sZ[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
     }
 
-    // ---- G^T tiles -> M (lower triangle), each masked with every head's decays:
-    // wave w takes tiles w, w + NW, w + 2 NW. A wave with fewer tiles computes its
-    // first tile again, writing the same values again: a branch around a tile would
-    // split the phase into pieces that each wait for all of their LDS reads.
+    // ---- G tiles -> M (lower triangle), each masked with every head's decays:
+    // wave w takes tiles w, w + NW, w + 2 NW. A wave with fewer tiles masks its
+    // first tile again, writing the same values again (no branch in the phase).
     {
       f32x4 acc[NT];
       int Jt[NT], It[NT];
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
-        const int ti = w + NW * u < 10 ? w + NW * u : w;
-        // ti -> (Jt, It), It >= Jt: (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
-        Jt[u] = ti < 4 ? 0 : (ti < 7 ? 1 : (ti < 9 ? 2 : 3));
-        It[u] = ti < 4 ? ti : (ti < 7 ? ti - 3 : (ti < 9 ? ti - 5 : 3));
-        acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int ti = w + NW * u < kTiles ? w + NW * u : w;
+        Jt[u] = tile_j(ti);
+        It[u] = tile_i(ti);
+        acc[u] = pf.g[u];  // loaded during the previous chunk
       }
-      // the mask's cumulative sums and steps, read before the MFMAs so that their
-      // latency hides behind them (the scheduler would otherwise sink the reads to
-      // their use)
       float csi[HPW][NT];
       f32x4 csj[HPW][NT], dtj[HPW][NT];
 #pragma unroll
@@ -532,15 +551,6 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
           csi[hh][u] = sCS[hh][16 * It[u] + li];
           csj[hh][u] = *(const f32x4*)(sCS[hh] + 16 * Jt[u] + 4 * lg);
           dtj[hh][u] = *(const f32x4*)(sDT[hh] + 16 * Jt[u] + 4 * lg);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          const bf16x8 a = as_bf16x8(lds128(sB + (16 * Jt[u] + li) * LDB + 32 * kb + 8 * lg));
-          const bf16x8 bb = as_bf16x8(lds128(sC + (16 * It[u] + li) * LDC + 32 * kb + 8 * lg));
-          acc[u] = mfma(a, bb, acc[u]);
         }
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
@@ -565,6 +575,7 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     }
 
     load_c(pf);
+    load_g(pf);
     // ---- Y^T = S_in C^T, columns scaled by exp(cs_i). A operand: the state,
     // k = n in {32kb + 4lg + r} U {32kb + 16 + 4lg + r} (the accumulator layout);
     // B operand: C[i][n] for the same n, 16 bytes of row i of sCk.
@@ -629,7 +640,7 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       }
     }
 
-    __syncthreads();  // ---- barrier B: M complete; no wave reads sB, sC, sX or the decays again
+    __syncthreads();  // ---- barrier B: M complete; no wave reads sB, sCk, sX or the decays again
 
     // ---- Y^T += X^T M^T (M[i][j] = 0 for j > i: skip the upper blocks)
 #pragma unroll
@@ -682,6 +693,41 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   store_y();  // the last chunk's y
 }
 
+// G = C B^T of every chunk of 64 tokens and every group, once for all the heads
+// of the group (the scan's masked "hidden attention" inside a chunk, "Mamba-2",
+// section "The hidden attention", before the per-head decays): the ten
+// lower-triangular 16x16 tiles in the layout of the MFMA result, so that a lane of
+// the scan reads its four values of a tile as one 16-byte piece:
+//   cb[blk][ti][l][r] = sum_n C[t0 + 16 It + l % 16][n] B[t0 + 16 Jt + 4 (l / 16) + r][n],
+// blk = (b nchunks + c) G + g, t0 = 64 c, (It, Jt) = the tile's blocks. Rows past
+// the sequence end read zeros. One workgroup of 4 waves per block; wave w takes
+// tiles w, w + 4, w + 8.
+__global__ __launch_bounds__(256) void ssd_cb_kernel(const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
+                                                     float* __restrict__ cb, int L, int G, int nchunks, int64_t nblk) {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = threadIdx.x & 63, li = l & 15,
+            lg = l >> 4;
+  const uint32_t row = (uint32_t)(G * NS * 2);
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int g = (int)(blk % G), c = (int)((blk / G) % nchunks);
+    const int64_t b = blk / ((int64_t)G * nchunks);
+    const int t0 = c * Q;
+    const uint32_t bytes = (uint32_t)(L - t0) * row - (uint32_t)g * NS * 2;
+    const int64_t base = (b * L + t0) * (int64_t)G * NS + (int64_t)g * NS;
+    const __amdgpu_buffer_rsrc_t rB = rsrc(B + base, bytes), rC = rsrc(C + base, bytes);
+    for (int ti = w; ti < kTiles; ti += 4) {
+      const int It = tile_i(ti), Jt = tile_j(ti);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)((16 * Jt + li) * row + (32 * kb + 8 * lg) * 2), 0, 0);
+        const u32x4 bb = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)((16 * It + li) * row + (32 * kb + 8 * lg) * 2), 0, 0);
+        acc = mfma(as_bf16x8(a), as_bf16x8(bb), acc);
+      }
+      *(f32x4*)(cb + (blk * kTiles + ti) * kTileFloats + 4 * l) = acc;
+    }
+  }
+}
+
 // Zeroes the queue counters, the give-up word and the per-chain flags (a kernel, not a memset, so
 // that the call can be captured in a graph). give_up != 0 raises the give-up word instead, so that
 // every hand-off wait ends at once (the test of what a wait that gives up does to the outputs).
@@ -701,7 +747,7 @@ namespace {
 // plus one chunk of overhead per item.
 struct SsdPlan {
   int hpw, nchains, seg_chunks, nseg, nq, grid;
-  size_t queue_bytes, ws_bytes;
+  size_t queue_bytes, carry_bytes, cb_bytes, ws_bytes;
 };
 
 SsdPlan ssd_plan(const SSDArgs& a) {
@@ -755,7 +801,9 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   const int64_t qitems = best_ns * ((nchains + p.nq - 1) / p.nq);
   p.grid = (int)std::min<int64_t>(grid, (int64_t)p.nq * qitems);
   p.queue_bytes = ((size_t)(256 + p.nchains) * 4 + 255) / 256 * 256;
-  p.ws_bytes = p.queue_bytes + (p.nseg > 1 ? (size_t)(a.batch * a.H) * P * NS * 4 : 0);
+  p.carry_bytes = p.nseg > 1 ? (size_t)(a.batch * a.H) * P * NS * 4 : 0;
+  p.cb_bytes = (size_t)a.batch * (size_t)((a.L + Q - 1) / Q) * (size_t)a.G * kTiles * kTileFloats * 4;
+  p.ws_bytes = p.queue_bytes + p.carry_bytes + p.cb_bytes;
   return p;
 }
 
@@ -779,11 +827,18 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   k.h0 = a.h0; k.y = (uint16_t*)a.y; k.h_out = a.h_out;
   k.queue = (unsigned*)ws;
   k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
+  float* cb = (float*)((char*)ws + p.queue_bytes + p.carry_bytes);
+  k.cb = cb;
   k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
+  k.nchunks = (int)((a.L + Q - 1) / Q);
   k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
   const int nwords = 256 + p.nchains;
   hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nwords + 255) / 256)), dim3(256), 0, s, k.queue,
                      nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
+  const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
+  if (nblk > 0)
+    hipLaunchKernelGGL(ssd_cb_kernel, dim3((unsigned)std::min<int64_t>(nblk, 1 << 20)), dim3(256), 0, s,
+                       (const uint16_t*)a.B, (const uint16_t*)a.C, cb, (int)a.L, (int)a.G, k.nchunks, nblk);
   if (p.hpw == 2)
     hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);
   else
