@@ -587,6 +587,28 @@ def bench_ssd_states(steps, warmup, torch, bd, gen):
                      wall, ev, nbytes, tokens_per_s=b * L / (wall * 1e-3))
 
 
+def bench_ssd_f32(steps, warmup, torch, bd, gen):
+    """sscan_ssd_fwd with fp32 activations at the Mamba-2 2.7B layer shape, one batch row
+    (8192 tokens x 80 heads x 64, state 128): the path for activations the MFMA chunk kernel
+    does not take (the fp32 token loop, 16 lanes per head_dim column)."""
+    inp = gen.make_workload(4, batch=1, act="f32")
+    base = upload(inp, torch)
+    b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
+    y = torch.empty_like(base["x"])
+    h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def fn(_):
+        bd.sscan_ssd_fwd(base["x"], base["dt_raw"], base["dt_bias"], base["A_log"], base["B"], base["C"], base["D"],
+                         base["z"], base["state_input"], y=y, state_output=h, workspace=ws, chunk=inp.chunk)
+
+    wall, ev = time_calls(fn, [None], steps, warmup, torch)
+    return hbm_entry("mamba2-2.7b layer, fp32 activations, 1 x 8192 tokens x 80 heads x 64, state 128 (token loop)",
+                     wall, ev, ssd_bytes(inp), tokens_per_s=b * L / (wall * 1e-3),
+                     updates_per_s=b * L * H * P * N / (ev["mean"] * 1e-3))
+
+
 def bench_attention(steps, warmup, torch, bd, gen, L=2048):
     """The hidden attention map of the first L tokens of one batch row of the Mamba-2 2.7B
     workload's distributions (80 heads, one group, state 128): alpha [1, L, L, 80] fp32,
@@ -686,6 +708,8 @@ def main():
         extra["ssd_attention_map"] = bench_attention(max(5, args.steps // 10), 2, torch, bd, gen)
         log("bench: SSD with per-token states")
         extra["ssd_per_token_states"] = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
+        log("bench: SSD with fp32 activations")
+        extra["ssd_fp32"] = bench_ssd_f32(max(3, args.steps // 10), 1, torch, bd, gen)
 
     cfg = gen.WORKLOADS[MAIN]
     roof = dict(main_d["roofline"])

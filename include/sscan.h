@@ -164,8 +164,8 @@ sscan_status sscan_ssd_fwd(const sscan_ssd_desc* desc, const void* x, const void
 /* sscan_ssd_fwd for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * arguments without the workspace, and the same kernels and results. What the
- * workspace would hold (the chunk path's work queues, give-up word and state
- * hand-offs, or the token loop's slice carries) lives in the library's static
+ * workspace would hold (the chunk path's work queues, give-up word, state
+ * hand-offs and C.B^T tiles, or the token loop's slice carries) lives in the library's static
  * device scratch of SSCAN_NOALLOC_SCRATCH_BYTES, which every GPU the library runs
  * on holds from the first call until the process ends. A problem that needs more
  * returns SSCAN_ERR_UNSUPPORTED before any launch (sscan_ssd_workspace_size

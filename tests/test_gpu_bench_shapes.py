@@ -1,7 +1,7 @@
-"""GPU parity of the steps next to the scan, the Mamba-2 decode step and the hidden
-attention map at the shapes the benchmark times (the Mamba-2 2.7B layer: batch 4,
-8192 tokens, 80 heads x 64, state 128, xBC width 5376), in the same launch
-configuration. The conv, the norm and the decode step are compared whole. The
+"""GPU parity of the steps next to the scan, the Mamba-2 decode step, the SSD scan with
+fp32 activations and the hidden attention map at the shapes the benchmark times (the
+Mamba-2 2.7B layer: batch 4, 8192 tokens, 80 heads x 64, state 128, xBC width 5376), in
+the same launch configuration. The conv, the norm and the decode step are compared whole. The
 attention map (1.3 GB of fp32 at 2048 tokens) is compared on windows: an entry
 alpha[t, s] depends only on tokens s..t, so the oracle's map of the subsequence
 [s1, t2) holds alpha[t, s] for s1 <= s <= t < t2."""
@@ -13,7 +13,7 @@ import oracle
 from state_space_model_sscan_amd import binding as bd
 from state_space_model_sscan_amd import inputs as gen
 
-from _gpu import check, check_all, dev, host, par, say
+from _gpu import check, check_all, dev, host, par, run_ssd, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +55,16 @@ def test_gated_norm_at_the_2p7b_shape():
     torch.cuda.synchronize()
     ref = oracle.gated_rmsnorm(host(y), host(z), host(wt), 1e-5)
     check(host(out), ref, "bf16", "norm out", path="stream")
+
+
+@pytest.mark.timeout(600)
+def test_ssd_fp32_at_the_2p7b_shape():
+    """fp32 activations at the 2.7B layer shape, one batch row (the token-loop path the
+    benchmark times), every element of y and of the final state."""
+    inp = gen.make_workload(4, batch=1, act="f32")
+    say("ssd fp32 at", (1, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim))
+    got = run_ssd(inp)
+    check_all(inp, got, oracle.run_inputs(inp), "ssd")
 
 
 def test_ssd_decode_step_at_the_2p7b_shape():
