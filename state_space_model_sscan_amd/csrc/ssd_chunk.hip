@@ -769,8 +769,9 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   int64_t grid = (p.hpw == 1 && nchains >= 2 * (int64_t)ncu) ? 2 * ncu : ncu;
   int64_t best_seg = nchunks, best_ns = 1;
   auto queues = [&](int64_t g) { return std::max<int64_t>(1, std::min<int64_t>({8, nchains, g})); };
-  if (nchains < (p.hpw == 1 ? 2 : 1) * (int64_t)ncu) {
-    // rounds of items in the fullest queue over its workgroups
+  {
+    // rounds of items in the fullest queue over its workgroups (with many more chains
+    // than workgroups, whole chains win: cutting them only adds hand-offs)
     const int64_t nq = queues(grid), qch = (nchains + nq - 1) / nq, qwg = std::max<int64_t>(grid / nq, 1);
     auto cost = [&](int64_t sc, int64_t ns) {
       const int64_t rounds = (ns * qch + qwg - 1) / qwg;
