@@ -523,12 +523,19 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
         sNC[tid] = 1.0f / sqrtf(sc / (float)k.N + k.bc_eps);
       }
       __syncthreads();
+      // the normed B and C in place, once per tile (the per-token loop then needs no
+      // scaling; B * ib is formed first either way, so the rounding is the same)
+      for (int e = tid; e < TILE * NP; e += 256) {
+        const int t = e / NP, n = e % NP;
+        sB[t][n] *= sNB[t];
+        if (!PASS1) sC[t][n] *= sNC[t];
+      }
+      __syncthreads();
     }
     for (int i = 0; i < nt; ++i) {
       const float xv = sX[i][cl];
       const float dtv = sDT[i][cl];
       const float dtx = dtv * xv;
-      const float ib = k.bc_eps > 0.0f ? sNB[i] : 1.0f;
       const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
       float bv[NQ];
       step_ld<NP>(&sB[i][0], q, bv);
@@ -536,16 +543,15 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
         sdt += dtv;
 #pragma unroll
         for (int e = 0; e < NQ; ++e)
-          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * (bv[e] * ib));
+          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
       } else {
         float cv[NQ];
         step_ld<NP>(&sC[i][0], q, cv);
-        const float ic = k.bc_eps > 0.0f ? sNC[i] : 1.0f;
         float acc = 0.0f;
 #pragma unroll
         for (int e = 0; e < NQ; ++e) {
-          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * (bv[e] * ib));
-          acc = fmaf(cv[e] * ic, h[e], acc);
+          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
+          acc = fmaf(cv[e], h[e], acc);
         }
         acc = step_sum<K>(acc);
         const int64_t idx = (b * k.L + t0 + i) * k.Dc + cc;
