@@ -62,4 +62,36 @@ __device__ __forceinline__ int64_t xcd_local_order(int64_t lin, int64_t n) {
 // silu(z) = z / (1 + e^-z); z -> -inf gives -0, z -> +inf gives z.
 __device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 
+// DPP helpers for the 16-lane rows of a wave (gfx950).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// One exchange stage of the row transpose-reduce: tokens lo (class 0 keeps) and
+// hi (class 1 keeps); the partner lane (CTRL) is in the other class.
+template <int CTRL>
+__device__ __forceinline__ float tr_stage(float lo, float hi, bool cls) {
+  const float keep = cls ? hi : lo;
+  const float send = cls ? lo : hi;
+  return keep + dpp_f<CTRL>(send);
+}
+
+// p[t] holds this lane's term for token t of a 16-token group; returns, in lane n
+// of each row, the sum of p[n] over the 16 lanes of the row. Stage partners:
+// n^8 (row_ror:8), n^7 (row_half_mirror), n^2 and n^1 (quad_perm); the vectors
+// 8, 7, 2, 1 span all 16 lanes, and the classes (bits 3, 2, 1, 0 of n) make the
+// token kept at the end token n.
+__device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int n) {
+  const bool c3 = n & 8, c2 = n & 4, c1 = n & 2, c0 = n & 1;
+  float q[8], r[4], u[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = tr_stage<0x128>(p[i], p[i + 8], c3);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = tr_stage<0x141>(q[i], q[i + 4], c2);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) u[i] = tr_stage<0x4E>(r[i], r[i + 2], c1);
+  return tr_stage<0xB1>(u[0], u[1], c0);
+}
+
 }  // namespace sscan

@@ -532,47 +532,66 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
       }
       __syncthreads();
     }
-    for (int i = 0; i < nt; ++i) {
-      const float xv = sX[i][cl];
-      const float dtv = sDT[i][cl];
-      const float dtx = dtv * xv;
-      const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
-      float bv[NQ];
-      step_ld<NP>(&sB[i][0], q, bv);
-      if (PASS1) {
+    if (PASS1) {
+      for (int i = 0; i < nt; ++i) {
+        const float dtv = sDT[i][cl];
+        const float dtx = dtv * sX[i][cl];
+        const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
+        float bv[NQ];
+        step_ld<NP>(&sB[i][0], q, bv);
         sdt += dtv;
 #pragma unroll
-        for (int e = 0; e < NQ; ++e)
-          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
-      } else {
-        float cv[NQ];
-        step_ld<NP>(&sC[i][0], q, cv);
-        float acc = 0.0f;
+        for (int e = 0; e < NQ; ++e) h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
+      }
+    } else {
+      // 16 tokens at a time: each lane keeps its partial read-out of every token,
+      // then a transpose-reduce over the channel's 16 lanes (one DPP row) leaves
+      // token i0 + q's sum in lane q, which finishes and stores that token's y
+      for (int i0 = 0; i0 < nt; i0 += 16) {
+        float p[16];
 #pragma unroll
-        for (int e = 0; e < NQ; ++e) {
-          h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
-          acc = fmaf(cv[e], h[e], acc);
-        }
-        acc = step_sum<K>(acc);
-        const int64_t idx = (b * k.L + t0 + i) * k.Dc + cc;
-        if (STATES && active) {
-          if (full) {  // non-temporal: the per-token states are not read again here
-            typedef float f32x4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-            for (int c4 = 0; c4 < NQ / 4; ++c4)
-              __builtin_nontemporal_store(f32x4_t{h[4 * c4], h[4 * c4 + 1], h[4 * c4 + 2], h[4 * c4 + 3]},
-                                          (f32x4_t*)(k.states + idx * NP + 64 * c4 + 4 * q));
-          } else {
+        for (int j = 0; j < 16; ++j) {
+          const int i = i0 + j;
+          p[j] = 0.0f;
+          if (i < nt) {
+            const float dtv = sDT[i][cl];
+            const float dtx = dtv * sX[i][cl];
+            const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
+            float bv[NQ], cv[NQ];
+            step_ld<NP>(&sB[i][0], q, bv);
+            step_ld<NP>(&sC[i][0], q, cv);
+            float acc = 0.0f;
 #pragma unroll
             for (int e = 0; e < NQ; ++e) {
-              const int n = step_entry<NP>(q, e);
-              if (n < k.N) k.states[idx * k.N + n] = h[e];
+              h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
+              acc = fmaf(cv[e], h[e], acc);
+            }
+            p[j] = acc;
+            if (STATES && active) {
+              const int64_t idx = (b * k.L + t0 + i) * k.Dc + cc;
+              if (full) {  // non-temporal: the per-token states are not read again here
+                typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+                for (int c4 = 0; c4 < NQ / 4; ++c4)
+                  __builtin_nontemporal_store(f32x4_t{h[4 * c4], h[4 * c4 + 1], h[4 * c4 + 2], h[4 * c4 + 3]},
+                                              (f32x4_t*)(k.states + idx * NP + 64 * c4 + 4 * q));
+              } else {
+#pragma unroll
+                for (int e = 0; e < NQ; ++e) {
+                  const int n = step_entry<NP>(q, e);
+                  if (n < k.N) k.states[idx * k.N + n] = h[e];
+                }
+              }
             }
           }
         }
-        float yv = acc + Dv * xv;
-        if (GATE) yv *= silu(sZ[i][cl]);
-        if (active && q == 0) Act<T>::st(yp + idx, yv);
+        const float tot = row_transpose_sum(p, q);
+        const int i = i0 + q;
+        if (i < nt && active) {
+          float yv = tot + Dv * sX[i][cl];
+          if (GATE) yv *= silu(sZ[i][cl]);
+          Act<T>::st(yp + (b * k.L + t0 + i) * k.Dc + cc, yv);
+        }
       }
     }
   }
