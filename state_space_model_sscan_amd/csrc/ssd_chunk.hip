@@ -700,11 +700,17 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
 // the scan reads its four values of a tile as one 16-byte piece:
 //   cb[blk][ti][l][r] = sum_n C[t0 + 16 It + l % 16][n] B[t0 + 16 Jt + 4 (l / 16) + r][n],
 // blk = (b nchunks + c) G + g, t0 = 64 c, (It, Jt) = the tile's blocks. Rows past
-// the sequence end read zeros. One workgroup of 4 waves per block; wave w takes
-// tiles w, w + 4, w + 8.
-__global__ __launch_bounds__(256) void ssd_cb_kernel(const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
-                                                     float* __restrict__ cb, int L, int G, int nchunks, int64_t nblk) {
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = threadIdx.x & 63, li = l & 15,
+// the sequence end read zeros. One workgroup of 10 waves per block, one tile each.
+// It also clears the scan's work queues, give-up word and chain flags (q, nq words;
+// give_up != 0 raises the give-up word instead, the test of what a wait that gives
+// up does): a kernel rather than a memset, so that the call can be captured in a
+// graph, and this one rather than a kernel of its own, to save a launch.
+__global__ __launch_bounds__(640) void ssd_cb_kernel(const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
+                                                     float* __restrict__ cb, int L, int G, int nchunks, int64_t nblk,
+                                                     unsigned* __restrict__ q, int nq, unsigned give_up) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nq; i += gridDim.x * blockDim.x)
+    q[i] = i == 128 ? give_up : 0u;
+  const int ti = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = threadIdx.x & 63, li = l & 15,
             lg = l >> 4;
   const uint32_t row = (uint32_t)(G * NS * 2);
   for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
@@ -714,7 +720,7 @@ __global__ __launch_bounds__(256) void ssd_cb_kernel(const uint16_t* __restrict_
     const uint32_t bytes = (uint32_t)(L - t0) * row - (uint32_t)g * NS * 2;
     const int64_t base = (b * L + t0) * (int64_t)G * NS + (int64_t)g * NS;
     const __amdgpu_buffer_rsrc_t rB = rsrc(B + base, bytes), rC = rsrc(C + base, bytes);
-    for (int ti = w; ti < kTiles; ti += 4) {
+    {
       const int It = tile_i(ti), Jt = tile_j(ti);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -726,14 +732,6 @@ __global__ __launch_bounds__(256) void ssd_cb_kernel(const uint16_t* __restrict_
       *(f32x4*)(cb + (blk * kTiles + ti) * kTileFloats + 4 * l) = acc;
     }
   }
-}
-
-// Zeroes the queue counters, the give-up word and the per-chain flags (a kernel, not a memset, so
-// that the call can be captured in a graph). give_up != 0 raises the give-up word instead, so that
-// every hand-off wait ends at once (the test of what a wait that gives up does to the outputs).
-__global__ void ssd_queue_reset(unsigned* q, int n, unsigned give_up) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    q[i] = i == 128 ? give_up : 0u;
 }
 
 namespace {
@@ -834,12 +832,11 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   k.nchunks = (int)((a.L + Q - 1) / Q);
   k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
   const int nwords = 256 + p.nchains;
-  hipLaunchKernelGGL(ssd_queue_reset, dim3((unsigned)std::min(64, (nwords + 255) / 256)), dim3(256), 0, s, k.queue,
-                     nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
   const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
-  if (nblk > 0)
-    hipLaunchKernelGGL(ssd_cb_kernel, dim3((unsigned)std::min<int64_t>(nblk, 1 << 20)), dim3(256), 0, s,
-                       (const uint16_t*)a.B, (const uint16_t*)a.C, cb, (int)a.L, (int)a.G, k.nchunks, nblk);
+  // (at least one workgroup: it also clears the queues)
+  hipLaunchKernelGGL(ssd_cb_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(nblk, 1 << 20))), dim3(640),
+                     0, s, (const uint16_t*)a.B, (const uint16_t*)a.C, cb, (int)a.L, (int)a.G, k.nchunks, nblk, k.queue,
+                     nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
   if (p.hpw == 2)
     hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);
   else
