@@ -197,6 +197,11 @@ SSD_CASES = [
     (2, 300, 4, 32, 128, 2, "f32", True, True, True),    # token loop, 16 lanes a channel: groups, slices, states
     (1, 150, 2, 64, 100, 1, "bf16", True, True, True),   # 100 of a padded 128, slices, states
     (1, 1100, 2, 128, 64, 1, "bf16", True, True, False), # head_dim 128: the token loop
+    # head_dim and state_dim 128 on the token loop (fp32, and bf16 with states and
+    # groups), with slices; head_dim 160
+    (1, 600, 2, 128, 128, 1, "f32", True, True, False),
+    (1, 500, 2, 128, 128, 2, "bf16", True, True, True),
+    (1, 300, 2, 160, 64, 1, "f32", True, False, False),
 ]
 
 
