@@ -94,4 +94,59 @@ __device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int n) 
   return tr_stage<0xB1>(u[0], u[1], c0);
 }
 
+// The same sum with the two stages over lane bits 3 and 2 done without selects.
+// Their classes are whole DPP banks (lanes 4k..4k+3 of a row), so one output is
+// two bank-masked DPP adds into the same register: the first writes the banks of
+// class 0 (its kept token plus the partner's copy of it), the second those of
+// class 1; a lane outside a mask keeps what it holds. row_ror:r gives lane l the
+// value of lane (l - r) mod 16, so the partner n^8 is row_ror:8 for both classes,
+// and n^4 is row_ror:12 for class 0 (banks 0, 2: lane n + 4) and row_ror:4 for
+// class 1 (banks 1, 3: lane n - 4). The masks gate only the writes: a lane still
+// reads its partner in the other bank. The compiler has no form for a masked float
+// add, hence the asm; `s_nop 1` gives the two wait states a DPP read needs after a
+// VALU write of its source, so nothing depends on what the compiler scheduled
+// before a block. EXEC must be full (every lane of the row takes part). The stages
+// over bits 1 and 0 are the select form above. Per 16 tokens: 33 VALU instructions
+// against 45.
+__device__ __forceinline__ float row_transpose_sum_banked(const float (&p)[16], int n) {
+  float q[8], r[4], u[2];
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %4, %20, %20 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %5, %21, %21 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %6, %22, %22 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %7, %23, %23 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]), "=&v"(q[7])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(p[8]),
+        "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:4 row_mask:0xf bank_mask:0xa"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
+  const bool c1 = n & 2, c0 = n & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) u[i] = tr_stage<0x4E>(r[i], r[i + 2], c1);
+  return tr_stage<0xB1>(u[0], u[1], c0);
+}
+
 }  // namespace sscan

@@ -24,10 +24,10 @@
 //    of token s from lane s of its row by DPP row_newbcast, which the compiler
 //    folds into the multiplies that consume them.
 //  * Each lane keeps its partial read-out C_n h_n for the 16 tokens of a group; a
-//    transpose-reduce over the row (four DPP exchange stages: lane n with n^8,
-//    n^7, n^2, n^1) leaves the full sum for token n in lane n, which adds D*x,
-//    applies the gate and writes y to LDS; the block stores the tile's y as
-//    8/16-byte pieces.
+//    transpose-reduce over the row (four DPP exchange stages: lane n with n^8 and
+//    n^4 as bank-masked DPP adds, then n^2 and n^1 with selects) leaves the full
+//    sum for token n in lane n, which adds D*x, applies the gate and writes y to
+//    LDS; the block stores the tile's y as 8/16-byte pieces.
 //  * Every buffer resource is based at the tile's first token row and ends at
 //    the slice's last token, so rows past the end read zeros and drop their
 //    stores in hardware, and per-lane offsets stay fixed over the whole scan.
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
         }
       }
     });
-    float yv = row_transpose_sum(p, n) + Dv * xv;
+    float yv = row_transpose_sum_banked(p, n) + Dv * xv;
     if (GATE) yv *= silu(quad::to_f<T>(sX[2][tl][cl]));
     sY[tl][cl] = quad::from_f<T>(yv);
   };
