@@ -105,12 +105,14 @@ __device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int n) 
 // reads its partner in the other bank. The compiler has no form for a masked float
 // add, hence the asm; `s_nop 1` gives the two wait states a DPP read needs after a
 // VALU write of its source, so nothing depends on what the compiler scheduled
-// before a block. EXEC must be full (every lane of the row takes part). The stages
+// before a block. The blocks have no effect beyond their outputs (not volatile,
+// so the compiler may schedule them among other work). EXEC must be full (every
+// lane of the row takes part). The stages
 // over bits 1 and 0 are the select form above. Per 16 tokens: 33 VALU instructions
 // against 45.
 __device__ __forceinline__ float row_transpose_sum_banked(const float (&p)[16], int n) {
   float q[8], r[4], u[2];
-  asm volatile(
+  asm(
       "s_nop 1\n\t"
       "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
       "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
@@ -131,7 +133,7 @@ __device__ __forceinline__ float row_transpose_sum_banked(const float (&p)[16], 
       : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]), "=&v"(q[7])
       : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(p[8]),
         "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
-  asm volatile(
+  asm(
       "s_nop 1\n\t"
       "v_add_f32_dpp %0, %4, %4 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
       "v_add_f32_dpp %0, %8, %8 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"

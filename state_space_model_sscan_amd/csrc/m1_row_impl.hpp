@@ -12,7 +12,7 @@
 // channel give fewer waves than the chip has SIMDs. This kernel gives every
 // channel a whole 16-lane row of a wave, lane n holding state entries n, n+16, ..,
 // which quadruples the waves (three per SIMD for a batch of 8 at width 1536).
-// A 256-thread block owns 16 channels and walks the sequence in 64-token tiles:
+// A 256-thread block owns 16 channels and walks the sequence in 128-token tiles:
 //  * Each tile's x, dt_raw, z, B and C are loaded cooperatively, a thread reading
 //    4 neighbouring channels (or state entries) of one token in a single 8- or
 //    16-byte load, converted to fp32 and written to LDS: x/dt/z as [token][channel],
@@ -34,6 +34,7 @@
 // The host uses this kernel when state_dim is 16, 32 or 64 and channels are a
 // multiple of 4 (so a thread's 4 channels are all inside the row or all past it).
 #pragma once
+#include <type_traits>
 #include <utility>
 
 #include "m1_fast_impl.hpp"
@@ -262,8 +263,10 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
     }
   };
 
-  // Group j (tokens t0+16j .. t0+16j+15) of the tile in LDS.
-  auto compute_group = [&](int t0, int j) {
+  // Group j (tokens t0+16j .. t0+16j+15) of the tile in LDS. TAIL: the tile may
+  // run past the slice's end (only the last tile does), so its steps are masked.
+  auto compute_group = [&](int t0, int j, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     const int tg = t0 + 16 * j;
     const int tl = 16 * j + n;  // this lane's token in the tile
     f32x4 b4[4][NPL], c4[4][NPL];  // B and C of the group's 16 tokens, this lane's entries
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
       }
     const float xv = quad::to_f<T>(sX[0][tl][cl]);
     const float sp = softplus_fast(quad::to_f<T>(sX[1][tl][cl]) + bias);
-    const float dtv = tg + n < t_end ? sp : 0.0f;  // a token past the end is a zero step
+    const float dtv = (!TAIL || tg + n < t_end) ? sp : 0.0f;  // a token past the end is a zero step
     const float dtx = dtv * xv;
     float p[16];
     static_for<16>([&](auto S) {
@@ -316,8 +319,13 @@ __global__ __launch_bounds__(256) void m1_row_kernel(M1F k) {
     if (t0 > t_begin) store_y(t0 - TILE);
     load_raw(raw, t0 + TILE);
     __syncthreads();
+    if (t0 + TILE <= t_end) {  // uniform: every token of the tile is in the slice
 #pragma unroll
-    for (int j = 0; j < TILE / 16; ++j) compute_group(t0, j);
+      for (int j = 0; j < TILE / 16; ++j) compute_group(t0, j, std::false_type{});
+    } else {
+#pragma unroll
+      for (int j = 0; j < TILE / 16; ++j) compute_group(t0, j, std::true_type{});
+    }
   }
   __syncthreads();
   if (t_end > t_begin) store_y(t_begin + ((t_end - t_begin - 1) / TILE) * TILE);
