@@ -5,10 +5,13 @@
 A step is one sscan_mamba1_fwd over the Mamba-130m layer workload (batch 8,
 seq 2048, d_inner 1536, state_dim 16, bf16 activations, fp32 state, fused
 silu(z) gate). Inputs are resident in HBM when timing starts; three copies of
-them rotate so no step finds its inputs in the 256 MiB Infinity Cache. K steps
-are timed between two device synchronizations; each call is also bracketed by
-HIP events on the stream the kernels are launched on (mean, median and minimum
-are reported). The Falcon-Mamba-7b-width Mamba-1 workload and the Mamba-2 2.7B
+them rotate so no step finds its inputs in the 256 MiB Infinity Cache. Before
+the W warmup steps half a second of VALU work (zeta over a buffer; no step of the
+workload) brings the GPU from its idle clock to its loaded one. K steps are then
+timed between two device synchronizations, with one pair of HIP events on the
+stream the kernels are launched on around them (the kernel time per launch is
+their time / K); a second pass of K calls, each between its own events, gives
+the median and minimum of single launches. The Falcon-Mamba-7b-width Mamba-1 workload and the Mamba-2 2.7B
 SSD workload get blocks of their own with the same roofline and CPU-baseline
 fields; beside them the decode steps, the conv1d + silu and gated RMS norm
 around the Mamba-2 scan, the hidden attention map and the SSD with per-token
@@ -46,6 +49,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
 MFMA_FLOPS_PER_MOP = 512         # SQ_INSTS_VALU_MFMA_MOPS_* counts units of 512 FLOPs
+DEVICE_WARMUP_S = 0.5         # seconds of VALU work before each timed region (device_warmup)
 METRIC = "scan tokens/s & % HBM roofline (Mamba-1); SSD tokens/s & % MFMA peak"
 MAIN = 1
 BLOCKS = (3, 4)                  # the other throughput workloads, with blocks of their own
@@ -146,24 +150,56 @@ def scan_call(inp, bd, torch, base):
     return fn
 
 
+def device_warmup(torch, seconds=None):
+    """Brings the GPU to its loaded clock before a timed region: Hurwitz zeta over a
+    64 MB buffer (a long VALU loop per element, about 0.75 ms per launch, so that a
+    kernel trace of the bench stays small) for `seconds`. It is no step of any
+    workload. After seconds of host-only work (the CPU baseline, input generation)
+    the GPU idles at a low clock: measured cold, the Mamba-130m layer's first tens
+    of calls ran 15% slower than after half a second of VALU work (a bf16 GEMM
+    warms it less: under MFMA load the clock settles lower)."""
+    seconds = DEVICE_WARMUP_S if seconds is None else seconds
+    if seconds <= 0:
+        return
+    x = torch.rand(1 << 24, device="cuda") + 1.5
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        torch.special.zeta(x, 2.0)
+        torch.cuda.synchronize()
+    del x
+
+
 def time_calls(fn, sets, steps, warmup, torch):
-    """`warmup` untimed calls, then `steps` timed calls between two synchronizations,
-    each also bracketed by HIP events on the current stream (the one the library
-    launches on). Returns (wall ms per step, event ms statistics)."""
+    """The device warm-up, `warmup` untimed calls, then `steps` timed calls between two
+    synchronizations, bracketed by one pair of HIP events on the current stream (the
+    one the library launches on), so nothing is queued between the calls. Then, after
+    the timed region, the same number of calls with an event pair around each, for
+    the spread of single launches. Returns (wall ms per step, event ms statistics:
+    `mean` = the timed region's event time / steps, the per-launch GPU time including
+    the gaps between launches; `median`, `min`, `per_call_mean` from the second pass)."""
+    device_warmup(torch)
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    region = e0.elapsed_time(e1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         evs[i][0].record(stream)
         fn(sets[i % len(sets)])
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     ms = np.array([a.elapsed_time(b) for a, b in evs])
-    return wall, dict(mean=float(ms.mean()), median=float(np.median(ms)), min=float(ms.min()), n=int(ms.size))
+    return wall, dict(mean=float(region), median=float(np.median(ms)), min=float(ms.min()),
+                      per_call_mean=float(ms.mean()), n=int(ms.size))
 
 
 # ---------------------------------------------------------------- hardware counters (rocprofv3 children)
@@ -427,6 +463,7 @@ def bench_step(torch, bd, gen, calls=512):
             bd.sscan_step(state, xs[t], dts[t], base["dt_bias"], base["A_log"], Bs[t], Cs[t], base["D"], zs[t],
                           y=ys[t], state_output=state)
 
+    device_warmup(torch)
     run(8)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -542,6 +579,7 @@ def bench_ssd_step(torch, bd, gen, nstates=32, calls=64):
             run()
     finally:
         bd.set_pointer_checks(prev)
+    device_warmup(torch)
     gr.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -735,6 +773,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu.get(MAIN),
         "kernel_ms": main_d["kernel_ms"],
+        "device_warmup_s": DEVICE_WARMUP_S,
         "counters": main_d.get("counters"),
         "host": host_info(),
         "workloads": blocks,

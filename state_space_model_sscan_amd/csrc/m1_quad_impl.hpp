@@ -187,12 +187,14 @@ __global__ __launch_bounds__(256) void m1_quad_kernel(M1F k) {
                                              (int)(vx == kOOB ? kOOB : vx + it * RPI * row_bytes), 0, 0);
   };
 
-  // Group j (tokens t0 + 4j .. t0 + 4j + 3) of the tile in LDS.
-  auto compute_group = [&](int t0, int j) {
+  // Group j (tokens t0 + 4j .. t0 + 4j + 3) of the tile in LDS. TAIL: the tile
+  // may run past the slice's end (only the last tile does), so its steps are masked.
+  auto compute_group = [&](int t0, int j, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     const int tl = 4 * j + q;  // this lane's token in the tile
     const float xv = to_f<T>(sA[0][tl][cl]);
     const float sp = softplus_fast(to_f<T>(sA[1][tl][cl]) + bias);
-    const float dtv = t0 + tl < t_end ? sp : 0.0f;  // a token past the end is a zero step
+    const float dtv = (!TAIL || t0 + tl < t_end) ? sp : 0.0f;  // a token past the end is a zero step
     const float dtx = dtv * xv;
     float p[4];
     static_for<4>([&](auto S) {
@@ -242,7 +244,12 @@ __global__ __launch_bounds__(256) void m1_quad_kernel(M1F k) {
     if (t0 > t_begin) store_y(t0 - TILE);
     load_raw(raw, t0 + TILE);
     __syncthreads();
-    for (int j = 0; j < TILE / 4; ++j) compute_group(t0, j);
+    if (t0 + TILE <= t_end) {  // uniform: every token of the tile is in the slice
+#pragma unroll 2
+      for (int j = 0; j < TILE / 4; ++j) compute_group(t0, j, std::false_type{});
+    } else {
+      for (int j = 0; j < TILE / 4; ++j) compute_group(t0, j, std::true_type{});
+    }
   }
   __syncthreads();
   if (t_end > t_begin) store_y(t_begin + ((t_end - t_begin - 1) / TILE) * TILE);
