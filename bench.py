@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
+F32_MFMA_PEAK_TFLOPS = 157.3     # dense fp32 MFMA, published
 MFMA_FLOPS_PER_MOP = 512         # SQ_INSTS_VALU_MFMA_MOPS_* counts units of 512 FLOPs
 DEVICE_WARMUP_S = 0.5         # seconds of VALU work before each timed region (device_warmup)
 METRIC = "scan tokens/s & % HBM roofline (Mamba-1); SSD tokens/s & % MFMA peak"
@@ -627,24 +628,38 @@ def bench_ssd_states(steps, warmup, torch, bd, gen):
 
 def bench_ssd_f32(steps, warmup, torch, bd, gen):
     """sscan_ssd_fwd with fp32 activations at the Mamba-2 2.7B layer shape, one batch row
-    (8192 tokens x 80 heads x 64, state 128): the path for activations the MFMA chunk kernel
-    does not take (the fp32 token loop, 16 lanes per head_dim column)."""
+    (8192 tokens x 80 heads x 64, state 128): the fp32 MFMA chunk kernel, and beside it
+    the same call sent to the fp32 token loop (16 lanes per head_dim column) by the
+    tuning knob, the path fp32 activations of other shapes take."""
     inp = gen.make_workload(4, batch=1, act="f32")
     base = upload(inp, torch)
     b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
     y = torch.empty_like(base["x"])
     h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
-    ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
-    def fn(_):
-        bd.sscan_ssd_fwd(base["x"], base["dt_raw"], base["dt_bias"], base["A_log"], base["B"], base["C"], base["D"],
-                         base["z"], base["state_input"], y=y, state_output=h, workspace=ws, chunk=inp.chunk)
+    def run(token_loop):
+        prev = bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1 if token_loop else 0)
+        try:
+            ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
+            ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
-    wall, ev = time_calls(fn, [None], steps, warmup, torch)
-    return hbm_entry("mamba2-2.7b layer, fp32 activations, 1 x 8192 tokens x 80 heads x 64, state 128 (token loop)",
-                     wall, ev, ssd_bytes(inp), tokens_per_s=b * L / (wall * 1e-3),
-                     updates_per_s=b * L * H * P * N / (ev["mean"] * 1e-3))
+            def fn(_):
+                bd.sscan_ssd_fwd(base["x"], base["dt_raw"], base["dt_bias"], base["A_log"], base["B"], base["C"],
+                                 base["D"], base["z"], base["state_input"], y=y, state_output=h, workspace=ws,
+                                 chunk=inp.chunk)
+
+            return time_calls(fn, [None], steps, warmup, torch)
+        finally:
+            bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, prev)
+
+    wall, ev = run(False)
+    lwall, lev = run(True)
+    return hbm_entry("mamba2-2.7b layer, fp32 activations, 1 x 8192 tokens x 80 heads x 64, state 128 "
+                     "(fp32 MFMA chunk kernel)", wall, ev, ssd_bytes(inp), tokens_per_s=b * L / (wall * 1e-3),
+                     updates_per_s=b * L * H * P * N / (ev["mean"] * 1e-3),
+                     mfma_flops_q64=ssd_flops(inp, 64),
+                     mfma_frac_fp32_q64=ssd_flops(inp, 64) / (ev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS,
+                     token_loop=dict(ms_per_step=lwall, kernel_ms=lev, tokens_per_s=b * L / (lwall * 1e-3)))
 
 
 def bench_attention(steps, warmup, torch, bd, gen, L=2048):

@@ -131,7 +131,8 @@ sscan_status sscan_step(const sscan_mamba1_desc* desc, const float* state_input,
 size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
 
 /* Byte offset, in the workspace of an sscan_ssd_fwd call that takes the MFMA
- * chunk path (act bf16, head_dim 64, state_dim 128, states NULL), of a 32-bit
+ * chunk path (head_dim 64, state_dim 128, states NULL; act bf16, or f32 unless
+ * SSCAN_TUNE_SSD_F32_TOKEN_LOOP is set), of a 32-bit
  * word that is 0 after the call unless a state hand-off between two segments of
  * a head's sequence gave up waiting (see sscan_ssd_fwd). */
 #define SSCAN_SSD_GIVEUP_WORD_OFFSET 512
@@ -148,6 +149,9 @@ size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
  *   states        [batch, seqlen, nheads, head_dim, state_dim] f32 (out) or NULL
  * The state is stored value side (head_dim) first and state_dim innermost: entry
  * [b, h, p, n] is the pages' [b, h, key n, value p]. state_dim in 1..128.
+ * head_dim 64 with state_dim 128 and no per-token states takes the MFMA chunk
+ * path: bf16 MFMA for bf16 activations, fp32 MFMA (fp32 products and sums) for
+ * fp32 ones; other shapes take the token loop (fp32 arithmetic).
  * The MFMA chunk path cuts a head's sequence into segments that different
  * workgroups scan, each handing its final state to the next through the
  * workspace. The kernel's own scheduling guarantees every hand-off wait ends;
@@ -267,9 +271,11 @@ typedef enum {
   SSCAN_TUNE_SSD_WORKGROUPS = 3,    /* workgroups of the SSD chunk path */
   SSCAN_TUNE_SSD_GIVE_UP = 4,       /* nonzero: every state hand-off wait of the SSD chunk path gives
                                        up at once (for testing what a wait that gives up does) */
-  SSCAN_TUNE_SSD_HEADS_PER_WORKGROUP = 5  /* 2: two neighbouring heads of a group share a workgroup of
+  SSCAN_TUNE_SSD_HEADS_PER_WORKGROUP = 5, /* 2: two neighbouring heads of a group share a workgroup of
                                        the SSD chunk path, with B, C and C.B^T staged once (by
-                                       default one head per workgroup; same results) */
+                                       default one head per workgroup; same results; bf16 only) */
+  SSCAN_TUNE_SSD_F32_TOKEN_LOOP = 6 /* nonzero: fp32 activations of sscan_ssd_fwd take the token loop
+                                       instead of the fp32 MFMA chunk path (head_dim 64, state_dim 128) */
 } sscan_tune_knob;
 int64_t sscan_set_tuning(int knob, int64_t value);
 

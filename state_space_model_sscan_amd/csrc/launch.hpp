@@ -14,7 +14,8 @@ enum Knob {
   kKnobSsdWorkgroups = 3,    // workgroups of the SSD chunk kernel
   kKnobSsdGiveUp = 4,        // nonzero: every state hand-off wait of the chunk kernel gives up at once
   kKnobSsdHeadsPerWorkgroup = 5,  // 2: two heads per workgroup of the chunk kernel where they share a group
-  kKnobCount = 6
+  kKnobSsdF32TokenLoop = 6,  // nonzero: fp32 SSD activations take the token loop, not the fp32 chunk kernel
+  kKnobCount = 7
 };
 int64_t knob(int which);
 
@@ -84,7 +85,7 @@ hipError_t launch_ssd_step(const SSDArgs& a, hipStream_t s);
 constexpr size_t kScratchBytes = size_t(16) << 20;
 hipError_t scratch_ptr(void** out);
 
-// MFMA chunk SSD (ssd_chunk.hip): bf16, head_dim 64, state_dim 128, no per-token states.
+// MFMA chunk SSD (ssd_chunk.hip): bf16 or fp32, head_dim 64, state_dim 128, no per-token states.
 bool ssd_chunk_supported(const SSDArgs& a);
 size_t ssd_chunk_ws(const SSDArgs& a);
 hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s);

@@ -98,18 +98,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-struct SsdK {
-  const uint16_t* x;
-  const uint16_t* dt;
+// E: the activations' element type (bf16 bits for ssd_chunk_kernel, float for
+// ssd_chunk_f32_kernel)
+template <typename E>
+struct SsdKT {
+  const E* x;
+  const E* dt;
   const float* dt_bias;
   const float* A_log;
-  const uint16_t* B;
-  const uint16_t* C;
+  const E* B;
+  const E* C;
   const float* D;
-  const uint16_t* z;
+  const E* z;
   const float* cb;  // C B^T tiles from ssd_cb_kernel: [batch, nchunks, G][10 tiles][64 lanes][4]
   const float* h0;
-  uint16_t* y;
+  E* y;
   float* h_out;
   unsigned* queue;  // [16 q]: next item of queue q; [128]: a wait gave up; [256 + ch]: segments of chain ch done
   float* carry;     // [batch * H, P, NS]: the state a segment hands to the next one, per head
@@ -123,6 +126,8 @@ struct SsdK {
                     // [q nchains / nq, (q + 1) nchains / nq): item i of a queue with n chains is
                     // segment i / n of its chain i % n
 };
+typedef SsdKT<uint16_t> SsdK;
+typedef SsdKT<float> SsdKF;
 
 // Tile ti of a chunk's lower triangle -> (row block It, column block Jt), It >= Jt:
 // (0,0) (1,0) (2,0) (3,0) (1,1) (2,1) (3,1) (2,2) (3,2) (3,3)
@@ -134,6 +139,7 @@ __device__ __forceinline__ int tile_i(int ti) { return ti < 4 ? ti : (ti < 7 ? t
 __device__ __forceinline__ int kslot(int t) { return (t & ~7) | ((t & 1) << 2) | ((t & 7) >> 1); }
 
 typedef __attribute__((address_space(4))) const SsdK KArgs;
+typedef __attribute__((address_space(4))) const SsdKF KArgsF;
 // The kernel's arguments, read again from the argument segment: used where a
 // value is needed rarely, so that it does not hold a scalar register.
 __device__ __forceinline__ KArgs* kargs() {
@@ -142,6 +148,7 @@ __device__ __forceinline__ KArgs* kargs() {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (KArgs*)(((uint64_t)hi << 32) | lo);
 }
+__device__ __forceinline__ KArgsF* kargs_f() { return (KArgsF*)kargs(); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -734,6 +741,443 @@ __global__ __launch_bounds__(640) void ssd_cb_kernel(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- fp32 activations
+//
+// ssd_chunk_f32_kernel: the chunked restatement, work items, segments and state
+// hand-offs of ssd_chunk_kernel (one head per workgroup), for fp32 activations on
+// fp32 MFMA (v_mfma_f32_16x16x4_f32: fp32 products and sums, so the chunked form
+// carries fp32 rounding only). Operand layouts:
+//   A[16 x 4]: lane l holds A[l % 16][l / 16]; B[4 x 16]: lane l holds
+//   B[l / 16][l % 16]; D[16 x 16]: lane l holds D[4 (l / 16) + r][l % 16].
+// With one float per lane and operand, each phase picks its own assignment of
+// the contraction index k to the lane groups lg (any works if A and B agree):
+//   Y^T = S_in C^T: k = lg <-> state n = 16 nt + 4 lg + r, so the A operand is the
+//     state accumulator value hacc[nt][r] itself, and the B operand for r = 0..3
+//     is one 16-byte read of row i of C (sCf, row-major);
+//   S^T = exp(cs_last) S^T + B^T (w x) and Y^T += X^T M^T: k = lg <-> token
+//     j = 16 jb + 4 lg + kk (kk = 0..3): the B^T operand (sBt, B transposed at
+//     staging) and the M operand (sMf, row-major) are 16-byte reads for kk = 0..3,
+//     and x[j][p] for the 16 (jb, kk) is read once per chunk and serves both;
+//     Y^T += X^T M^T takes only the blocks jb <= it (M is lower triangular).
+// The state is kept as S^T tiles in the accumulators (rows n, columns p), which
+// puts S[p = 16 wq + li][n = 16 nt + 4 lg + r] in lane l, register r of tile nt:
+// the layout of ssd_chunk_kernel, so the state moves in and out alike.
+// LDS: B^T, C, x, z, y and M of a chunk in fp32 (146 KB, one workgroup per
+// compute unit), row pitches 8 dwords past a multiple of 64, where 16-byte reads
+// of 16 rows at once are conflict-free.
+constexpr int LBT = Q + 8;   // row pitch (fp32) of sBt: B^T [state][token]
+constexpr int LCF = NS + 8;  // row pitch of sCf: C [token][state]
+constexpr int LXF = P + 8;   // row pitch of sXf, sZf, sYf: [token][head_dim]
+constexpr int LMF = Q + 8;   // row pitch of sMf: M [token i][token j]
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 ld_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// One chunk's staged global loads of one thread (coalesced: 32 lanes cover a
+// 512-byte row of B or C, 16 lanes a 256-byte row of x or z).
+struct PrefetchF {
+  f32x4 b[2][4];     // B rows 32 it + 4 (tid / 32) + u, states 4 (tid % 32) .. + 3
+  f32x4 c[8];        // C rows 8 it + tid / 32, states 4 (tid % 32) .. + 3
+  f32x4 x[4], z[4];  // x / z rows 16 it + tid / 16, columns 4 (tid % 16) .. + 3
+  f32x4 g[3];        // the C B^T tiles this wave masks
+  float dt;
+};
+
+__global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
+  constexpr int NW = 4, NT = 3;
+  __shared__ __attribute__((aligned(16))) float sBt[NS * LBT];
+  __shared__ __attribute__((aligned(16))) float sCf[Q * LCF];
+  __shared__ __attribute__((aligned(16))) float sXf[Q * LXF];
+  __shared__ __attribute__((aligned(16))) float sZf[Q * LXF];
+  __shared__ __attribute__((aligned(16))) float sYf[Q * LXF];
+  __shared__ __attribute__((aligned(16))) float sMf[Q * LMF];
+  __shared__ __attribute__((aligned(16))) float sCS[Q], sDT[Q], sW[Q], sE[Q];
+  __shared__ int sTicket[3];
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), wq = w, l = tid & 63, li = l & 15,
+            lg = l >> 4;
+  const int L = (int)k.L, H = (int)k.H, G = (int)k.G;
+  const bool gate = k.z != nullptr;
+
+  // the work queues, as in ssd_chunk_kernel
+  auto qindex = [&]() { return __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)kargs_f()->nq)); };
+  auto qcounter = [&]() { return kargs_f()->queue + 16 * qindex(); };
+  auto qfirst = [&]() {
+    return __builtin_amdgcn_readfirstlane((int)((unsigned)(qindex() * kargs_f()->nchains) / (unsigned)kargs_f()->nq));
+  };
+  auto qchains = [&]() {
+    const unsigned q = (unsigned)qindex(), n = (unsigned)kargs_f()->nchains, nq = (unsigned)kargs_f()->nq;
+    return __builtin_amdgcn_readfirstlane((int)((q + 1) * n / nq - q * n / nq));
+  };
+  auto qitems = [&]() { return kargs_f()->nseg * qchains(); };
+
+  if (tid == 0) sTicket[0] = (int)atomicAdd(qcounter(), 1u);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(sTicket[0]);
+  if (cur >= qitems()) return;
+  int nxt = -1;
+
+  // row bytes and elements per batch row
+  const uint32_t bc_row = (uint32_t)(G * NS * 4), xz_row = (uint32_t)(H * P * 4), dt_row = (uint32_t)(H * 4);
+  const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * H;
+  const int nb = tid & 31, jq = tid >> 5;  // staging of B and C: 16-byte piece, row
+  const int xp = tid & 15, xr = tid >> 4;  // staging of x, z and y: 16-byte piece, row
+
+  int tb = 0, th = 0, tg = 0, tt = 0;  // target of the loads in flight (as in ssd_chunk_kernel)
+  auto tgt_rsrc = [&](const float* base, uint32_t bat, uint32_t col, uint32_t rowb, bool on = true) {
+    const int left = on ? L - tt : 0;
+    return rsrc((const char*)(base + (uint64_t)tb * bat + col) + (uint32_t)tt * rowb,
+                left > 0 ? (uint32_t)left * rowb - col * 4 : 0u);
+  };
+  auto load_b = [&](PrefetchF& pf) {
+    const __amdgpu_buffer_rsrc_t rB = tgt_rsrc(k.B, bc_bat, (uint32_t)tg * NS, bc_row);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pf.b[it][u] = ld_f32x4(rB, (uint32_t)(32 * it + 4 * jq + u) * bc_row + nb * 16);
+  };
+  auto load_c = [&](PrefetchF& pf) {
+    const __amdgpu_buffer_rsrc_t rC = tgt_rsrc(k.C, bc_bat, (uint32_t)tg * NS, bc_row);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) pf.c[it] = ld_f32x4(rC, (uint32_t)(8 * it + jq) * bc_row + nb * 16);
+  };
+  auto load_g = [&](PrefetchF& pf) {
+    const float* blk =
+        kargs_f()->cb + (((int64_t)tb * kargs_f()->nchunks + tt / Q) * G + tg) * (kTiles * kTileFloats);
+    const __amdgpu_buffer_rsrc_t rG = rsrc(blk, tt < L ? kTiles * kTileFloats * 4 : 0u);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int ti = w + NW * u < kTiles ? w + NW * u : w;
+      pf.g[u] = ld_f32x4(rG, (uint32_t)(ti * 64 + l) * 16);
+    }
+  };
+  auto load_x = [&](PrefetchF& pf) {
+    const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
+    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, wq == kDecayWave);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) pf.x[it] = ld_f32x4(rX, (uint32_t)(16 * it + xr) * xz_row + xp * 16);
+    pf.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (int)(l * dt_row), 0, 0));
+  };
+  auto load_z = [&](PrefetchF& pf) {
+    const __amdgpu_buffer_rsrc_t rZ = tgt_rsrc(gate ? k.z : k.x, xz_bat, (uint32_t)th * P, xz_row);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) pf.z[it] = ld_f32x4(rZ, (uint32_t)(16 * it + xr) * xz_row + xp * 16);
+  };
+  __amdgpu_buffer_rsrc_t ry_prev = rsrc(k.y, 0);
+  auto store_y = [&]() {
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(sYf + (16 * it + xr) * LXF + 4 * xp), ry_prev,
+                                             (int)((uint32_t)(16 * it + xr) * xz_row + xp * 16), 0, 2);
+  };
+
+  int b = 0, h = 0, g = 0, c = 0, c_end = 0, seg = 0;
+  float A2 = 0.f, bias = 0.f, Dh = 0.f;
+  auto set_item = [&](int it) {
+    const KArgsF* kk = kargs_f();
+    const int nch = qchains();
+    seg = it / nch;
+    const int ch = qfirst() + it % nch;
+    b = ch / H;
+    h = ch % H;
+    g = h / kk->heads_per_group;
+    c = seg * kk->seg_chunks;
+    c_end = min(c + kk->seg_chunks, max((L + Q - 1) / Q, 1));
+    A2 = -expf(kk->A_log[h]) * kLog2e;
+    bias = kk->dt_bias[h];
+    Dh = kk->D[h];
+  };
+
+  // Chunk at token tt from the prefetch registers into LDS (B transposed); wave
+  // kDecayWave adds the steps, their inclusive cumulative sum (exp2 domain), the
+  // row scales exp(cs) and the state update's weights w_j = exp(cs_last - cs_j) dt_j.
+  auto stage = [&](PrefetchF& pf) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(f32x4*)(sBt + (4 * nb + e) * LBT + 32 * it + 4 * jq) =
+            f32x4{pf.b[it][0][e], pf.b[it][1][e], pf.b[it][2][e], pf.b[it][3][e]};
+#pragma unroll
+    for (int it = 0; it < 8; ++it) *(f32x4*)(sCf + (8 * it + jq) * LCF + 4 * nb) = pf.c[it];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      *(f32x4*)(sXf + (16 * it + xr) * LXF + 4 * xp) = pf.x[it];
+      *(f32x4*)(sZf + (16 * it + xr) * LXF + 4 * xp) = pf.z[it];
+    }
+    if (wq == kDecayWave) {
+      const int nt_valid = max(0, min(Q, L - tt));
+      const float dtv = l < nt_valid ? softplus(pf.dt + bias) : 0.0f;
+      const float cs = wave_inclusive_sum(dtv * A2);
+      const float cs_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
+      sDT[l] = dtv;
+      sCS[l] = cs;
+      sE[l] = fast_exp2(cs);
+      sW[l] = fast_exp2(cs_last - cs) * dtv;
+    }
+  };
+
+  f32x4 hacc[8];
+  const int64_t s_lane = (int64_t)(16 * wq + li) * NS + 4 * lg;
+  // the entering state, as in ssd_chunk_kernel (the same flags, give-up word and carry)
+  auto state_in = [&]() {
+    const int64_t ch = (int64_t)b * H + h;
+    if (seg > 0) {
+      if (tid == 0) {
+        unsigned* flag = kargs_f()->queue + 256 + ch;
+        bool ready = false, quit = false;
+        for (int n = 0; n < (1 << 20) && !ready && !quit; ++n) {
+          ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg;
+          quit = !ready && __hip_atomic_load(kargs_f()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+          if (!ready && !quit) __builtin_amdgcn_s_sleep(2);
+        }
+        if (!ready) __hip_atomic_store(kargs_f()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sTicket[2] = ready ? 0 : 1;
+      }
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(sTicket[2]) != 0) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{NAN, NAN, NAN, NAN};
+      } else {
+        const __amdgpu_buffer_rsrc_t rS = rsrc(kargs_f()->carry + ch * (P * NS), P * NS * 4);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          hacc[nt] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
+      }
+    } else if (kargs_f()->h0) {
+      const float* src = kargs_f()->h0 + ch * (P * NS) + s_lane;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
+  };
+  auto state_out = [&]() {
+    const int64_t ch = (int64_t)b * H + h;
+    if (seg + 1 < kargs_f()->nseg) {
+      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs_f()->carry + ch * (P * NS), P * NS * 4);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hacc[nt]), rS, (int)((s_lane + 16 * nt) * 4), 0,
+                                               kDeviceCoherent);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(kargs_f()->queue + 256 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      float* dst = kargs_f()->h_out + ch * (P * NS) + s_lane;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
+    }
+  };
+
+  set_item(cur);
+  tb = b; th = h; tg = g; tt = c * Q;
+  PrefetchF pf;
+  load_b(pf);
+  load_c(pf);
+  load_g(pf);
+  load_x(pf);
+  load_z(pf);
+  stage(pf);
+  state_in();
+  if (tid == 0) sTicket[1] = (int)atomicAdd(qcounter(), 1u);
+  __syncthreads();
+  {
+    const int t = __builtin_amdgcn_readfirstlane(sTicket[1]);
+    nxt = t < qitems() ? t : -1;
+  }
+
+  for (;;) {
+    const int t0 = c * Q;
+    const bool last = c + 1 == c_end;
+    // ---- after barrier A: chunk c is in LDS; loads go to the next chunk
+    int ticket = 0;
+    if (!last) {
+      tt = t0 + Q;
+    } else if (nxt >= 0) {
+      const int qn = qchains(), ns = nxt / qn, nch = qfirst() + nxt % qn;
+      tb = nch / H;
+      th = nch % H;
+      tg = th / kargs_f()->heads_per_group;
+      tt = ns * kargs_f()->seg_chunks * Q;
+      if (tid == 0) ticket = (int)atomicAdd(qcounter(), 1u);
+    } else {
+      tt = L;
+    }
+    store_y();
+    load_b(pf);
+    load_z(pf);
+
+    // x[j = 16 jb + 4 lg + kk][p = 16 wq + li] (operand of the state update and of
+    // X^T M^T), and the epilogue's x and z (4 columns of row 16 it + li)
+    float xv[4][4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) xv[jb][kk] = sXf[(16 * jb + 4 * lg + kk) * LXF + 16 * wq + li];
+    f32x4 xe[4], ze[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      xe[it] = *(const f32x4*)(sXf + (16 * it + li) * LXF + 16 * wq + 4 * lg);
+      ze[it] = *(const f32x4*)(sZf + (16 * it + li) * LXF + 16 * wq + 4 * lg);
+    }
+
+    // ---- G tiles -> M[i][j] = G[i][j] exp(cs_i - cs_j) dt_j (j <= i), fp32, row-major;
+    // wave w takes tiles w, w + 4, w + 8 (a wave with two masks its first again)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int ti = w + NW * u < kTiles ? w + NW * u : w;
+      const int It = tile_i(ti), Jt = tile_j(ti);
+      const int i = 16 * It + li;
+      const float csi = sCS[i];
+      const f32x4 csj = *(const f32x4*)(sCS + 16 * Jt + 4 * lg);
+      const f32x4 dtj = *(const f32x4*)(sDT + 16 * Jt + 4 * lg);
+      f32x4 m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * Jt + 4 * lg + r;
+        const float v = pf.g[u][r] * fast_exp2(fminf(csi - csj[r], 0.0f)) * dtj[r];
+        m[r] = j <= i ? v : 0.0f;
+      }
+      *(f32x4*)(sMf + i * LMF + 16 * Jt + 4 * lg) = m;
+    }
+
+    load_c(pf);
+    load_g(pf);
+    float ei[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) ei[it] = sE[16 * it + li];
+    f32x4 wv[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) wv[jb] = *(const f32x4*)(sW + 16 * jb + 4 * lg);
+    const float dec_last = sE[Q - 1];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- Y^T = S_in C^T, columns scaled by exp(cs_i)
+    f32x4 yacc[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) yacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const f32x4 cv = *(const f32x4*)(sCf + (16 * it + li) * LCF + 16 * nt + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[it] = mfma_f32(hacc[nt][r], cv[r], yacc[it]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yacc[it][r] *= ei[it];
+    }
+
+    load_x(pf);
+    // ---- S^T = exp(cs_last) S^T + B^T (w x)
+    float wx[4][4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) wx[jb][kk] = wv[jb][kk] * xv[jb][kk];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hacc[nt][r] *= dec_last;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const f32x4 bv = *(const f32x4*)(sBt + (16 * nt + li) * LBT + 16 * jb + 4 * lg);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) hacc[nt] = mfma_f32(bv[kk], wx[jb][kk], hacc[nt]);
+      }
+    }
+
+    __syncthreads();  // ---- barrier B: M complete; no wave reads sBt, sCf, sXf, sZf or the decays again
+
+    // ---- Y^T += X^T M^T over the blocks jb <= it
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (jb > it) continue;
+        const f32x4 mv = *(const f32x4*)(sMf + (16 * it + li) * LMF + 16 * jb + 4 * lg);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) yacc[it] = mfma_f32(xv[jb][kk], mv[kk], yacc[it]);
+      }
+    }
+    // ---- epilogue: lane holds y[i = 16 it + li][16 wq + 4 lg + r]; y = (Y + D x) silu(z)
+    {
+      const __amdgpu_buffer_rsrc_t rY = rsrc((const char*)(k.y + (uint64_t)b * xz_bat + h * P) + (uint32_t)t0 * xz_row,
+                                             (uint32_t)(L - t0) * xz_row - h * P * 4);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = fmaf(Dh, xe[it][r], yacc[it][r]) * (gate ? silu(ze[it][r]) : 1.0f);
+        *(f32x4*)(sYf + (16 * it + li) * LXF + 16 * wq + 4 * lg) = v;
+      }
+      ry_prev = rY;
+    }
+    const bool finished = last && nxt < 0;
+    if (last) {
+      state_out();
+      if (!finished) {
+        if (tid == 0) sTicket[1] = ticket;
+        set_item(nxt);
+        state_in();
+        __syncthreads();
+        const int t = __builtin_amdgcn_readfirstlane(sTicket[1]);
+        nxt = t < qitems() ? t : -1;
+      }
+    } else {
+      ++c;
+    }
+    stage(pf);
+    __syncthreads();  // ---- barrier A of the next chunk
+    if (finished) break;
+  }
+  store_y();
+}
+
+// ssd_cb_kernel for fp32 B and C on fp32 MFMA, in the same tile layout:
+//   cb[blk][ti][l][r] = sum_n C[t0 + 16 It + l % 16][n] B[t0 + 16 Jt + 4 (l / 16) + r][n],
+// computed as the transposed tile (A operand from rows of B, B operand from rows
+// of C; k = lane group <-> n = 16 nb + 4 lg + kk). Also clears the work queues.
+__global__ __launch_bounds__(640) void ssd_cb_f32_kernel(const float* __restrict__ B, const float* __restrict__ C,
+                                                         float* __restrict__ cb, int L, int G, int nchunks, int64_t nblk,
+                                                         unsigned* __restrict__ q, int nq, unsigned give_up) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nq; i += gridDim.x * blockDim.x)
+    q[i] = i == 128 ? give_up : 0u;
+  const int ti = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = threadIdx.x & 63, li = l & 15,
+            lg = l >> 4;
+  const uint32_t row = (uint32_t)(G * NS * 4);
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int g = (int)(blk % G), c = (int)((blk / G) % nchunks);
+    const int64_t b = blk / ((int64_t)G * nchunks);
+    const int t0 = c * Q;
+    const uint32_t bytes = (uint32_t)(L - t0) * row - (uint32_t)g * NS * 4;
+    const int64_t base = (b * L + t0) * (int64_t)G * NS + (int64_t)g * NS;
+    const __amdgpu_buffer_rsrc_t rB = rsrc(B + base, bytes), rC = rsrc(C + base, bytes);
+    const int It = tile_i(ti), Jt = tile_j(ti);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const f32x4 a = ld_f32x4(rB, (uint32_t)(16 * Jt + li) * row + (16 * nb + 4 * lg) * 4);
+      const f32x4 cc = ld_f32x4(rC, (uint32_t)(16 * It + li) * row + (16 * nb + 4 * lg) * 4);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(a[kk], cc[kk], acc);
+    }
+    *(f32x4*)(cb + (blk * kTiles + ti) * kTileFloats + 4 * l) = acc;
+  }
+}
+
 namespace {
 
 // How the chains are cut into segments and how many workgroups take them. A
@@ -749,6 +1193,7 @@ struct SsdPlan {
 };
 
 SsdPlan ssd_plan(const SSDArgs& a) {
+  const bool f32 = !a.bf16;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
@@ -759,12 +1204,13 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   // layer they are 5-10% slower, the second wave per SIMD adding LDS waits rather
   // than hiding latency.
   const int64_t hpg = a.H / a.G;
-  p.hpw = (knob(kKnobSsdHeadsPerWorkgroup) == 2 && a.H % 2 == 0 && hpg % 2 == 0) ? 2 : 1;
+  // (fp32 activations: one head per workgroup, the only form of that kernel)
+  p.hpw = (!f32 && knob(kKnobSsdHeadsPerWorkgroup) == 2 && a.H % 2 == 0 && hpg % 2 == 0) ? 2 : 1;
   const int64_t nchains = a.batch * a.H / p.hpw, nchunks = std::max<int64_t>((a.L + Q - 1) / Q, 1);
   p.nchains = (int)nchains;
   // Two workgroups per unit (the occupancy the one-head kernel is built for) with
-  // many chains; the two-head kernel fills a unit's LDS with one.
-  int64_t grid = (p.hpw == 1 && nchains >= 2 * (int64_t)ncu) ? 2 * ncu : ncu;
+  // many chains; the two-head kernel and the fp32 kernel fill a unit's LDS with one.
+  int64_t grid = (!f32 && p.hpw == 1 && nchains >= 2 * (int64_t)ncu) ? 2 * ncu : ncu;
   int64_t best_seg = nchunks, best_ns = 1;
   auto queues = [&](int64_t g) { return std::max<int64_t>(1, std::min<int64_t>({8, nchains, g})); };
   {
@@ -810,16 +1256,40 @@ SsdPlan ssd_plan(const SSDArgs& a) {
 
 bool ssd_chunk_supported(const SSDArgs& a) {
   // buffer offsets are 32-bit: each batch row of x / z / y / B / C must stay below 2^31 bytes
-  const int64_t row_x = a.L * a.H * P * 2, row_bc = a.L * a.G * NS * 2;
-  return a.bf16 && a.P == P && a.N == NS && a.states == nullptr && a.batch * a.H <= (1 << 24) &&
-         row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
+  const int64_t es = a.bf16 ? 2 : 4;
+  const int64_t row_x = a.L * a.H * P * es, row_bc = a.L * a.G * NS * es;
+  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.P == P && a.N == NS && a.states == nullptr &&
+         a.batch * a.H <= (1 << 24) && row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
 }
 
 size_t ssd_chunk_ws(const SSDArgs& a) { return a.batch == 0 ? 0 : ssd_plan(a).ws_bytes; }
 
+// fp32 activations: ssd_cb_f32_kernel and ssd_chunk_f32_kernel on the same plan
+hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, void* ws, hipStream_t s) {
+  SsdKF k{};
+  k.x = (const float*)a.x; k.dt = (const float*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
+  k.B = (const float*)a.B; k.C = (const float*)a.C; k.D = a.D; k.z = (const float*)a.z;
+  k.h0 = a.h0; k.y = (float*)a.y; k.h_out = a.h_out;
+  k.queue = (unsigned*)ws;
+  k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
+  float* cb = (float*)((char*)ws + p.queue_bytes + p.carry_bytes);
+  k.cb = cb;
+  k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
+  k.nchunks = (int)((a.L + Q - 1) / Q);
+  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
+  const int nwords = 256 + p.nchains;
+  const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
+  hipLaunchKernelGGL(ssd_cb_f32_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(nblk, 1 << 20))),
+                     dim3(640), 0, s, (const float*)a.B, (const float*)a.C, cb, (int)a.L, (int)a.G, k.nchunks, nblk,
+                     k.queue, nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
+  hipLaunchKernelGGL(ssd_chunk_f32_kernel, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+  return hipGetLastError();
+}
+
 hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const SsdPlan p = ssd_plan(a);
+  if (!a.bf16) return launch_ssd_chunk_f32(a, p, ws, s);
   SsdK k{};
   k.x = (const uint16_t*)a.x; k.dt = (const uint16_t*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const uint16_t*)a.B; k.C = (const uint16_t*)a.C; k.D = a.D; k.z = (const uint16_t*)a.z;

@@ -33,6 +33,8 @@
 // writing y, the optional per-token states and, for the last slice, the final
 // state. Both passes restate the recurrence exactly; only rounding differs.
 #pragma once
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
       __syncthreads();
     }
     if (PASS1) {
-      for (int i = 0; i < nt; ++i) {
+      auto pass1_step = [&](int i) {
         const float dtv = sDT[i][cl];
         const float dtx = dtv * sX[i][cl];
         const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
@@ -542,18 +544,30 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
         sdt += dtv;
 #pragma unroll
         for (int e = 0; e < NQ; ++e) h[e] = fmaf(SSD ? dec0 : fast_exp2(dtv * A2[SSD ? 0 : e]), h[e], dtx * bv[e]);
+      };
+      // four tokens per iteration with no test between them (the LDS reads of the
+      // four overlap), then the rest one by one
+      int i = 0;
+      for (; i + 4 <= nt; i += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pass1_step(i + j);
       }
+      for (; i < nt; ++i) pass1_step(i);
     } else {
       // 16 tokens at a time: each lane keeps its partial read-out of every token,
       // then a transpose-reduce over the channel's 16 lanes (one DPP row) leaves
-      // token i0 + q's sum in lane q, which finishes and stores that token's y
-      for (int i0 = 0; i0 < nt; i0 += 16) {
+      // token i0 + q's sum in lane q, which finishes and stores that token's y.
+      // A whole group runs without a test per token: with one, every token's state
+      // update is a branch of its own and the compiler copies the state between
+      // registers at each join (8 moves per token at 8 entries per lane).
+      auto group = [&](int i0, auto tail) {
+        constexpr bool TL = decltype(tail)::value;
         float p[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int i = i0 + j;
           p[j] = 0.0f;
-          if (i < nt) {
+          if (!TL || i < nt) {
             const float dtv = sDT[i][cl];
             const float dtx = dtv * sX[i][cl];
             const float dec0 = SSD ? fast_exp2(dtv * A2[0]) : 0.0f;
@@ -592,6 +606,12 @@ __global__ __launch_bounds__(256) void tokenloop_group_kernel(TLK k) {
           if (GATE) yv *= silu(sZ[i][cl]);
           Act<T>::st(yp + (b * k.L + t0 + i) * k.Dc + cc, yv);
         }
+      };
+      for (int i0 = 0; i0 < nt; i0 += 16) {
+        // (with per-token states the tested form stays: untested, the compiler keeps
+        // all 16 tokens' states live for their stores, 322 registers against 90)
+        if (!STATES && i0 + 16 <= nt) group(i0, std::false_type{});
+        else group(i0, std::true_type{});
       }
     }
   }

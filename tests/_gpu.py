@@ -63,9 +63,11 @@ def run_mamba1(inp, want_states=None, state_input=None):
     return host(y), host(h), host(st)
 
 
-def ssd_chunk_path(inp, want_states):
-    """Whether sscan_ssd_fwd takes the MFMA chunk path for these inputs."""
-    return inp.act == "bf16" and inp.head_dim == 64 and inp.state_dim == 128 and not want_states
+def ssd_chunk_path(inp, want_states, token_loop=False):
+    """Whether sscan_ssd_fwd takes the MFMA chunk path for these inputs (bf16 MFMA for
+    bf16 activations, fp32 MFMA for fp32 ones; token_loop: fp32 sent to the token loop)."""
+    return (inp.head_dim == 64 and inp.state_dim == 128 and not want_states
+            and (inp.act == "bf16" or not token_loop))
 
 
 def giveup_word(workspace):
@@ -74,18 +76,24 @@ def giveup_word(workspace):
     return int(workspace[o:o + 4].cpu().numpy().view(np.uint32)[0])
 
 
-def run_ssd(inp, want_states=None, chunk=0, expect_giveup=False):
+def run_ssd(inp, want_states=None, chunk=0, expect_giveup=False, token_loop=False):
     """sscan_ssd_fwd on the inputs; on the chunk path, the give-up word must read 0
-    (or, with expect_giveup, must be raised)."""
+    (or, with expect_giveup, must be raised). token_loop: fp32 activations take the
+    token loop (the knob is set for the call and cleared after it)."""
     ws = inp.want_states if want_states is None else want_states
     a = inp.act
     x, B = dev(inp.x, a), dev(inp.B, a)
-    need = bd.sscan_ssd_workspace_size(bd.ssd_desc(x, B, chunk))
-    work = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    y, h, st = bd.sscan_ssd_fwd(x, dev(inp.dt_raw, a), par(inp.dt_bias), par(inp.A_log), B, dev(inp.C, a),
-                                par(inp.D), dev(inp.z, a), par(inp.h0), want_states=ws, chunk=chunk, workspace=work)
-    torch.cuda.synchronize()
-    if ssd_chunk_path(inp, ws) and inp.batch > 0:
+    prev = bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1 if token_loop else 0)
+    try:
+        need = bd.sscan_ssd_workspace_size(bd.ssd_desc(x, B, chunk))
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        y, h, st = bd.sscan_ssd_fwd(x, dev(inp.dt_raw, a), par(inp.dt_bias), par(inp.A_log), B, dev(inp.C, a),
+                                    par(inp.D), dev(inp.z, a), par(inp.h0), want_states=ws, chunk=chunk,
+                                    workspace=work)
+        torch.cuda.synchronize()
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, prev)
+    if ssd_chunk_path(inp, ws, token_loop) and inp.batch > 0:
         word = giveup_word(work)
         assert (word != 0) == expect_giveup, "give-up word %d" % word
     return host(y), host(h), host(st)

@@ -59,8 +59,8 @@ def test_gated_norm_at_the_2p7b_shape():
 
 @pytest.mark.timeout(600)
 def test_ssd_fp32_at_the_2p7b_shape():
-    """fp32 activations at the 2.7B layer shape, one batch row (the token-loop path the
-    benchmark times), every element of y and of the final state."""
+    """fp32 activations at the 2.7B layer shape, one batch row (the fp32 MFMA chunk path
+    the benchmark times), every element of y and of the final state."""
     inp = gen.make_workload(4, batch=1, act="f32")
     say("ssd fp32 at", (1, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim))
     got = run_ssd(inp)

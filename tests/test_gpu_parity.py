@@ -202,6 +202,14 @@ SSD_CASES = [
     (1, 600, 2, 128, 128, 1, "f32", True, True, False),
     (1, 500, 2, 128, 128, 2, "bf16", True, True, True),
     (1, 300, 2, 160, 64, 1, "f32", True, False, False),
+    # fp32 activations on the fp32 MFMA chunk kernel: one token, chunk edges, ragged
+    # tails, groups, long sequences (segments)
+    (1, 1, 2, 64, 128, 1, "f32", True, True, False),
+    (2, 63, 3, 64, 128, 1, "f32", False, True, False),
+    (1, 64, 2, 64, 128, 1, "f32", True, False, False),
+    (2, 257, 4, 64, 128, 2, "f32", True, True, False),
+    (1, 1000, 4, 64, 128, 4, "f32", True, False, False),
+    (1, 2100, 2, 64, 128, 1, "f32", True, True, False),
 ]
 
 
@@ -241,6 +249,43 @@ def test_ssd_forced_segments(case, tuning):
     bd.set_tuning(bd.TUNE_SSD_WORKGROUPS, 0)
     yw, hw, _ = run_ssd(inp)
     assert np.array_equal(got[0], yw) and np.array_equal(got[1], hw)
+
+
+F32_SEGMENT_CASES = [
+    # chunks per segment, workgroups, batch, seqlen, H, G, gate, h0
+    (1, 3, 2, 300, 3, 1, True, True),
+    (3, 64, 3, 700, 4, 2, True, True),
+]
+
+
+@pytest.mark.parametrize("case", F32_SEGMENT_CASES, ids=lambda c: "seg%d_wg%d_b%d_L%d_H%d_G%d_g%d_h%d" % c)
+def test_ssd_f32_forced_segments(case, tuning):
+    """The fp32 chunk kernel's hand-offs: forced one- and three-chunk segments on small
+    grids, against the oracle and bit-identical to the library's own cut."""
+    sc, wg, b, L, H, G, gate, h0 = case
+    say("ssd f32 forced segments", case)
+    tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, sc)
+    tuning(bd.TUNE_SSD_WORKGROUPS, wg)
+    inp = gen.make_ssd(b, L, H, 64, 128, G, act="f32", seed=L + 7 * sc + wg, gate=gate, h0=h0)
+    got = run_ssd(inp)
+    check_all(inp, got, oracle.run_inputs(inp), "ssd")
+    bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 0)
+    bd.set_tuning(bd.TUNE_SSD_WORKGROUPS, 0)
+    yw, hw, _ = run_ssd(inp)
+    assert np.array_equal(got[0], yw) and np.array_equal(got[1], hw)
+
+
+def test_ssd_f32_chunk_kernel_agrees_with_token_loop():
+    """fp32 activations: the fp32 MFMA chunk kernel and the token loop restate the same
+    recurrence in fp32, so both meet the oracle and each other at the fp32 bound."""
+    inp = gen.make_ssd(2, 900, 4, 64, 128, 2, act="f32", seed=321, gate=True, h0=True)
+    ref = oracle.run_inputs(inp)
+    chunk = run_ssd(inp)
+    loop = run_ssd(inp, token_loop=True)
+    check_all(inp, chunk, ref, "ssd")
+    check_all(inp, loop, ref, "mamba1")
+    check(chunk[0], loop[0], "f32", "y (chunk vs token loop)")
+    check(chunk[1], loop[1], "f32", "state (chunk vs token loop)")
 
 
 def test_ssd_handoff_give_up_poisons_dependent_outputs(tuning):
