@@ -1,8 +1,8 @@
 """sscan_ssd_fwd_noalloc (the SSD prompt scan on the library's static device scratch)
 against sscan_ssd_fwd with a caller's workspace, through the C ABI: the same kernels
 and plan, so the results must be bit-identical. Two calls in a row, the second on a
-smaller problem, for the MFMA chunk path (with state hand-offs between segments in
-the scratch) and for the token-loop path (slice carries in the scratch); a problem
+smaller problem, for the MFMA chunk paths, bf16 and fp32 (with state hand-offs between
+segments in the scratch), and for the token-loop path (slice carries in the scratch); a problem
 that needs more scratch than there is is refused before any launch."""
 import numpy as np
 import pytest
@@ -57,14 +57,34 @@ def test_noalloc_chunk_path_two_calls(seg):
         bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 0)
 
 
+@pytest.mark.parametrize("seg", [0, 2])
+def test_noalloc_f32_chunk_path_two_calls(seg):
+    """fp32, head_dim 64, state_dim 128: the fp32 chunk kernel's queues, C B^T tiles and
+    (with segments of two chunks) state hand-offs in the static scratch."""
+    try:
+        bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, seg)
+        big = gen.make_ssd(2, 900, 6, 64, 128, 2, act="f32", seed=191, gate=True, h0=True)
+        small = gen.make_ssd(1, 200, 2, 64, 128, 1, act="f32", seed=192, gate=False, h0=False)
+        for inp in (big, small):
+            say("noalloc f32 chunk path", inp.x.shape, "segment chunks", seg)
+            _both(inp)
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 0)
+
+
 def test_noalloc_token_loop_path_two_calls():
-    """fp32 (the token loop), long enough to be cut into slices whose carries live in the
-    scratch; the second call is smaller, and a third asks for per-token states."""
+    """fp32 on the token loop (the knob sends head_dim 64 / state_dim 128 there), long
+    enough to be cut into slices whose carries live in the scratch; the second call is
+    smaller, and a third asks for per-token states."""
     big = gen.make_ssd(1, 3000, 2, 64, 128, act="f32", seed=93, gate=True, h0=True)
     small = gen.make_ssd(1, 700, 1, 32, 64, act="f32", seed=94, gate=True, h0=False)
-    for inp in (big, small):
-        say("noalloc token loop", inp.x.shape)
-        _both(inp)
+    try:
+        bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1)
+        for inp in (big, small):
+            say("noalloc token loop", inp.x.shape)
+            _both(inp)
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0)
     _both(gen.make_ssd(1, 100, 2, 64, 128, act="bf16", seed=95, gate=True, h0=True), want_states=True)
 
 
