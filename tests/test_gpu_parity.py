@@ -288,12 +288,13 @@ def test_ssd_f32_chunk_kernel_agrees_with_token_loop():
     check(chunk[1], loop[1], "f32", "state (chunk vs token loop)")
 
 
-def test_ssd_handoff_give_up_poisons_dependent_outputs(tuning):
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_ssd_handoff_give_up_poisons_dependent_outputs(tuning, act):
     """A state hand-off wait that gives up (forced from the host: the give-up word is raised
     before the kernel starts, so every wait ends at once) must not leave wrong numbers
     behind: the first segment of every head is exact, everything after it is NaN, and the
-    word reads back nonzero. No wait blocks and no kernel faults."""
-    inp = gen.make_ssd(2, 700, 4, 64, 128, act="bf16", seed=83, gate=True, h0=True)
+    word reads back nonzero. No wait blocks and no kernel faults. Both chunk kernels."""
+    inp = gen.make_ssd(2, 700, 4, 64, 128, act=act, seed=83, gate=True, h0=True)
     tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 2)      # segments of 128 tokens
     good_y, good_h, _ = run_ssd(inp)
     tuning(bd.TUNE_SSD_GIVE_UP, 1)
