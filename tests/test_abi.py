@@ -253,6 +253,9 @@ def test_tuning_knobs_are_validated_and_restored():
     assert L.sscan_set_tuning(bd.TUNE_M1_LANES, -2) == -1
     assert bd.set_tuning(bd.TUNE_M1_LANES, 4) == 0
     assert bd.set_tuning(bd.TUNE_M1_LANES, 0) == 4   # the previous value comes back
+    assert bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1) == 0
+    assert bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0) == 1
+    assert L.sscan_set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP + 1, 1) == -1   # one past the last knob
     with pytest.raises(ValueError):
         bd.set_tuning(42, 1)
 
@@ -288,6 +291,17 @@ def test_launch_plans_are_stable_and_follow_the_knobs():
     finally:
         bd.set_tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 0)
     assert L.sscan_ssd_workspace_size(ctypes.byref(s)) == s0
+    # fp32 activations take the fp32 chunk kernel (its plan: the larger workspace here)
+    # unless the knob sends them to the token loop
+    f = sdesc(batch=1, seqlen=256, nheads=400, act=0)
+    f0 = L.sscan_ssd_workspace_size(ctypes.byref(f))
+    bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1)
+    try:
+        ft = L.sscan_ssd_workspace_size(ctypes.byref(f))
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0)
+    assert ft < f0   # (400 heads need no slices on the token loop: no workspace at all)
+    assert L.sscan_ssd_workspace_size(ctypes.byref(f)) == f0
 
 
 def _cpu(*shape, dtype=None):
