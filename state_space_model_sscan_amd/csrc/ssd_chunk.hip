@@ -1,4 +1,5 @@
-// ssd_chunk.hip -- the Mamba-2 SSD prompt scan on MFMA for gfx950 (bf16 in, fp32 state).
+// ssd_chunk.hip -- the Mamba-2 SSD prompt scan on MFMA for gfx950 (bf16 or fp32 in, fp32 state;
+// the fp32 kernel is described at ssd_chunk_f32_kernel below).
 //
 // What it computes ("Mamba-2", nnterp encyclopedia, sections "The mixer's
 // values", "The hidden attention", "The state" and "The block, in order"):
@@ -763,6 +764,11 @@ __global__ __launch_bounds__(640) void ssd_cb_kernel(const uint16_t* __restrict_
 // The state is kept as S^T tiles in the accumulators (rows n, columns p), which
 // puts S[p = 16 wq + li][n = 16 nt + 4 lg + r] in lane l, register r of tile nt:
 // the layout of ssd_chunk_kernel, so the state moves in and out alike.
+// Per chunk: after barrier A (chunk staged), the x operands; the mask of the C B^T
+// tiles into M; Y^T = S_in C^T; the state update; barrier B (M complete); the
+// gate and D x from this chunk's z and x; Y^T += X^T M^T; y into LDS; the switch
+// of item after an item's last chunk; barrier C (every wave has read x and z);
+// the next chunk staged from its prefetch registers; barrier A.
 // LDS: B^T, C, x, z, y and M of a chunk in fp32 (146 KB, one workgroup per
 // compute unit), row pitches 8 dwords past a multiple of 64, where 16-byte reads
 // of 16 rows at once are conflict-free.
