@@ -162,20 +162,23 @@ def test_workload4_ssd_full_size():
     check_all(inp, got, oracle.run_inputs(inp), "ssd")
 
 
-def test_ssd_long_memory():
-    """8192 tokens on the chunk kernel with decays near the slowest the Mamba-2 page reports on
-    real weights (|A| from 4e-4 to 1e-2): the state sums thousands of tokens, the case where
-    the bf16 operands of w*x and of the state as C reads it would accumulate error."""
-    inp = gen.make_ssd(1, 8192, 8, 64, 128, act="bf16", seed=81, gate=True, h0=True)
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_ssd_long_memory(act):
+    """8192 tokens on the chunk kernels with decays near the slowest the Mamba-2 page reports
+    on real weights (|A| from 4e-4 to 1e-2): the state sums thousands of tokens, the case
+    where the bf16 operands of w*x and of the state as C reads it would accumulate error
+    (and, for fp32 activations, where the fp32 chunk kernel's sums run longest)."""
+    inp = gen.make_ssd(1, 8192, 8, 64, 128, act=act, seed=81, gate=True, h0=True)
     inp.A_log = np.log(np.geomspace(4e-4, 1e-2, 8)).astype(np.float32)
     say("ssd long memory: A", -np.exp(inp.A_log.astype(np.float64)))
     got = run_ssd(inp)
     check_all(inp, got, oracle.run_inputs(inp), "ssd")
 
 
-def test_ssd_codestral_heads_and_groups():
-    """Codestral's layout on the chunk kernel: 128 heads in 8 groups of B and C."""
-    inp = gen.make_ssd(1, 1000, 128, 64, 128, 8, act="bf16", seed=82, gate=True, h0=True)
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_ssd_codestral_heads_and_groups(act):
+    """Codestral's layout on the chunk kernels: 128 heads in 8 groups of B and C."""
+    inp = gen.make_ssd(1, 1000, 128, 64, 128, 8, act=act, seed=82, gate=True, h0=True)
     check_all(inp, run_ssd(inp), oracle.run_inputs(inp), "ssd")
 
 
@@ -460,7 +463,7 @@ def test_wide_decay_rates(act):
     """A from -4e-4 to -36316, the span the Mamba-2 page reports on real weights."""
     inp = gen.make_mamba1(2, 600, 128, 16, act=act, seed=25, gate=True, h0=True, A_log_mode="wide")
     check_all(inp, run_mamba1(inp), oracle.run_inputs(inp), "mamba1")
-    s = gen.make_ssd(2, 600, 4, 64, 128, act="bf16", seed=26, A_log_mode="wide")
+    s = gen.make_ssd(2, 600, 4, 64, 128, act=act, seed=26, A_log_mode="wide")
     check_all(s, run_ssd(s), oracle.run_inputs(s), "ssd")
 
 
