@@ -769,10 +769,17 @@ __global__ __launch_bounds__(640) void ssd_cb_kernel(const uint16_t* __restrict_
 // gate and D x from this chunk's z and x; Y^T += X^T M^T; y into LDS; the switch
 // of item after an item's last chunk; barrier C (every wave has read x and z);
 // the next chunk staged from its prefetch registers; barrier A.
-// LDS: B^T, C, x, z, y and M of a chunk in fp32 (146 KB, one workgroup per
-// compute unit), row pitches 8 dwords past a multiple of 64, where 16-byte reads
-// of 16 rows at once are conflict-free.
-constexpr int LBT = Q + 8;   // row pitch (fp32) of sBt: B^T [state][token]
+// LDS: B^T, C, x, z, y and M of a chunk in fp32 (142 KB, one workgroup per
+// compute unit); row pitches 8 dwords past a multiple of 64, where 16-byte reads
+// of 16 rows at once are conflict-free, except B^T, whose 16-byte blocks are
+// swizzled (bt_at) so that its transposing writes are conflict-free too.
+constexpr int LBT = Q;       // row pitch (fp32) of sBt: B^T [state][token], 16-byte blocks swizzled
+// sBt row n holds its 16 blocks of 4 tokens with block b at position b ^ bt_swz(n): the
+// 16 lanes of a transposing staging write (rows 4 nb + e) and of an operand read (rows
+// 16 nt + li) then all land on distinct banks (unswizzled, rows 4 apart at any pitch
+// that keeps 16-byte alignment share banks: up to 16-way conflicts on the writes)
+__device__ __forceinline__ int bt_swz(int n) { return ((n & 15) + (n >> 4)) & 15; }
+__device__ __forceinline__ int bt_at(int n, int j) { return n * LBT + 4 * ((j >> 2) ^ bt_swz(n)); }
 constexpr int LCF = NS + 8;  // row pitch of sCf: C [token][state]
 constexpr int LXF = P + 8;   // row pitch of sXf, sZf, sYf: [token][head_dim]
 constexpr int LMF = Q + 8;   // row pitch of sMf: M [token i][token j]
@@ -907,7 +914,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        *(f32x4*)(sBt + (4 * nb + e) * LBT + 32 * it + 4 * jq) =
+        *(f32x4*)(sBt + bt_at(4 * nb + e, 32 * it + 4 * jq)) =
             f32x4{pf.b[it][0][e], pf.b[it][1][e], pf.b[it][2][e], pf.b[it][3][e]};
 #pragma unroll
     for (int it = 0; it < 8; ++it) *(f32x4*)(sCf + (8 * it + jq) * LCF + 4 * nb) = pf.c[it];
@@ -1098,8 +1105,8 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
       }
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
-        const f32x4 b0 = *(const f32x4*)(sBt + (16 * nt + li) * LBT + 16 * jb + 4 * lg);
-        const f32x4 b1 = *(const f32x4*)(sBt + (16 * nt + 16 + li) * LBT + 16 * jb + 4 * lg);
+        const f32x4 b0 = *(const f32x4*)(sBt + bt_at(16 * nt + li, 16 * jb + 4 * lg));
+        const f32x4 b1 = *(const f32x4*)(sBt + bt_at(16 * nt + 16 + li, 16 * jb + 4 * lg));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           hacc[nt] = mfma_f32(b0[kk], wx[jb][kk], hacc[nt]);
