@@ -630,7 +630,9 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
     """sscan_ssd_fwd with fp32 activations at the Mamba-2 2.7B layer shape, one batch row
     (8192 tokens x 80 heads x 64, state 128): the fp32 MFMA chunk kernel, and beside it
     the same call sent to the fp32 token loop (16 lanes per head_dim column) by the
-    tuning knob, the path fp32 activations of other shapes take."""
+    tuning knob, the path fp32 activations of other shapes take. One batch row has 80
+    chains for 256 compute units; `full_batch` times the layer's whole batch of 4 (320
+    chains) on the chunk kernel."""
     inp = gen.make_workload(4, batch=1, act="f32")
     base = upload(inp, torch)
     b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
@@ -654,12 +656,34 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
 
     wall, ev = run(False)
     lwall, lev = run(True)
+    del base, y, h
+    torch.cuda.empty_cache()
+    # the whole batch of the layer (4 rows: 320 chains, enough to fill the chip)
+    full = gen.make_workload(4, act="f32")
+    fb = upload(full, torch)
+    fy = torch.empty_like(fb["x"])
+    fh = torch.empty((full.batch, H, P, N), dtype=torch.float32, device="cuda")
+    fws = torch.empty(max(bd.sscan_ssd_workspace_size(bd.ssd_desc(fb["x"], fb["B"], full.chunk)), 1),
+                      dtype=torch.uint8, device="cuda")
+
+    def ffn(_):
+        bd.sscan_ssd_fwd(fb["x"], fb["dt_raw"], fb["dt_bias"], fb["A_log"], fb["B"], fb["C"], fb["D"], fb["z"],
+                         fb["state_input"], y=fy, state_output=fh, workspace=fws, chunk=full.chunk)
+
+    fwall, fev = time_calls(ffn, [None], max(3, steps // 2), warmup, torch)
+    del fb, fy, fh, fws
+    torch.cuda.empty_cache()
+    fq = ssd_flops(full, 64)
     return hbm_entry("mamba2-2.7b layer, fp32 activations, 1 x 8192 tokens x 80 heads x 64, state 128 "
                      "(fp32 MFMA chunk kernel)", wall, ev, ssd_bytes(inp), tokens_per_s=b * L / (wall * 1e-3),
                      updates_per_s=b * L * H * P * N / (ev["mean"] * 1e-3),
                      mfma_flops_q64=ssd_flops(inp, 64),
                      mfma_frac_fp32_q64=ssd_flops(inp, 64) / (ev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS,
-                     token_loop=dict(ms_per_step=lwall, kernel_ms=lev, tokens_per_s=b * L / (lwall * 1e-3)))
+                     token_loop=dict(ms_per_step=lwall, kernel_ms=lev, tokens_per_s=b * L / (lwall * 1e-3)),
+                     full_batch=dict(workload="4 x 8192 tokens x 80 heads x 64, state 128, fp32", ms_per_step=fwall,
+                                     kernel_ms=fev, tokens_per_s=full.batch * L / (fwall * 1e-3),
+                                     hbm_frac=ssd_bytes(full) / (fev["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                     mfma_frac_fp32_q64=fq / (fev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS))
 
 
 def bench_attention(steps, warmup, torch, bd, gen, L=2048):

@@ -67,6 +67,14 @@ def test_ssd_fp32_at_the_2p7b_shape():
     check_all(inp, got, oracle.run_inputs(inp), "ssd")
 
 
+def test_ssd_fp32_four_rows_at_the_2p7b_width():
+    """fp32 activations on all four batch rows at the 2.7B width (320 chains, the plan the
+    benchmark's full-batch fp32 figure runs), 2048 tokens, every element."""
+    inp = gen.make_ssd(4, 2048, 80, 64, 128, act="f32", seed=2704, gate=True, h0=True)
+    say("ssd fp32 four rows", (4, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim))
+    check_all(inp, run_ssd(inp), oracle.run_inputs(inp), "ssd")
+
+
 def test_ssd_decode_step_at_the_2p7b_shape():
     """Two one-token steps at batch 4 x 80 heads x 64 x 128, the state updated in place,
     against the oracle's scan of the same two tokens from the same state."""
