@@ -1287,11 +1287,15 @@ SsdPlan ssd_plan(const SSDArgs& a) {
 }  // namespace
 
 bool ssd_chunk_supported(const SSDArgs& a) {
-  // buffer offsets are 32-bit: each batch row of x / z / y / B / C must stay below 2^31 bytes
+  // buffer offsets are 32-bit: each batch row of x / z / y / B / C must stay below 2^31 bytes.
+  // A sequence of length 0 goes to the token loop, which only passes the state through:
+  // the chunk kernels size their resources as (L - t0) rows less the head's or group's
+  // column offset, which needs at least one token row.
   const int64_t es = a.bf16 ? 2 : 4;
   const int64_t row_x = a.L * a.H * P * es, row_bc = a.L * a.G * NS * es;
-  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.P == P && a.N == NS && a.states == nullptr &&
-         a.batch * a.H <= (1 << 24) && row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
+  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.L > 0 && a.P == P && a.N == NS &&
+         a.states == nullptr && a.batch * a.H <= (1 << 24) && row_x < (int64_t(1) << 31) &&
+         row_bc < (int64_t(1) << 31);
 }
 
 size_t ssd_chunk_ws(const SSDArgs& a) { return a.batch == 0 ? 0 : ssd_plan(a).ws_bytes; }

@@ -301,6 +301,9 @@ def test_launch_plans_are_stable_and_follow_the_knobs():
     finally:
         bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0)
     assert ft < f0   # (400 heads need no slices on the token loop: no workspace at all)
+    # a sequence of length 0 takes no chunk-path workspace: the call only passes the state through
+    assert L.sscan_ssd_workspace_size(ctypes.byref(sdesc(seqlen=0))) == 0
+    assert L.sscan_ssd_workspace_size(ctypes.byref(sdesc(seqlen=0, act=0))) == 0
     assert L.sscan_ssd_workspace_size(ctypes.byref(f)) == f0
 
 

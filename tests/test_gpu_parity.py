@@ -476,6 +476,20 @@ def test_zero_length_sequence_passes_state_through():
     assert not hg.any()
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_ssd_zero_length_sequence_passes_state_through(act):
+    """seqlen 0 at the chunk kernels' shape (head_dim 64, state_dim 128): the state passes
+    through unchanged (zeros without an entering state) and y is empty."""
+    for h0 in (True, False):
+        inp = gen.make_ssd(2, 0, 3, 64, 128, act=act, seed=29, gate=True, h0=h0)
+        y, hg, _ = run_ssd(inp)
+        assert y.size == 0
+        if h0:
+            assert np.array_equal(hg, inp.h0.astype(np.float64))
+        else:
+            assert not hg.any()
+
+
 def test_host_tensors_are_refused():
     inp = gen.make_mamba1(1, 4, 64, 16, act="f32", seed=28)
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32))
