@@ -198,6 +198,84 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
   return x;
 }
 
+// The entering state of the current item: the caller's (or zeros) for a first
+// segment, else the one the previous segment left in carry, once its chain's
+// flag says so. The producer of that segment holds an item dequeued earlier
+// than this one, so it is running and never waits on this workgroup: the wait
+// ends. Its bound (2^20 polls, about a second) only guarantees that the kernel
+// terminates; a wait that gives up raises queue[128], which ends every other
+// wait, and starts its item from a NaN state: every output that depends on a
+// hand-off that did not happen (the rest of that chain's y and its final
+// state) comes out NaN rather than silently wrong.
+// carry and the flags move through device-coherent loads and stores (the sc1
+// cache policy, as device-scope atomics use), which need no cache write-back
+// or invalidation (either would flush the L2 that the other workgroups share);
+// carry moves in 16-byte pieces, so the write-through goes out in whole
+// 64-byte segments.
+// (Both chunk kernels: the fields used here sit at the same offsets in SsdK and SsdKF.)
+// hacc: this wave's state slice, S[p = 16 wq + li][n = 16 nt + 4 lg + r] in lane l,
+// register r of tile nt; flag_ix: the chain's flag; state_ix: the head's state; s_lane:
+// the lane's offset in a [P, NS] state; ticket: a word of workgroup memory.
+__device__ __forceinline__ void chain_state_in(f32x4 (&hacc)[8], int tid, int seg, int64_t flag_ix, int64_t state_ix,
+                                               int64_t s_lane, int& ticket) {
+  if (seg > 0) {
+    if (tid == 0) {
+      unsigned* flag = kargs()->queue + 256 + flag_ix;
+      bool ready = false, quit = false;
+      for (int n = 0; n < (1 << 20) && !ready && !quit; ++n) {
+        ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg;
+        quit = !ready && __hip_atomic_load(kargs()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        if (!ready && !quit) __builtin_amdgcn_s_sleep(2);
+      }
+      if (!ready) __hip_atomic_store(kargs()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ticket = ready ? 0 : 1;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(ticket) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{NAN, NAN, NAN, NAN};
+    } else {
+      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + state_ix * (P * NS), P * NS * 4);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        hacc[nt] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
+    }
+  } else if (kargs()->h0) {
+    const float* src = kargs()->h0 + state_ix * (P * NS) + s_lane;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // The loads complete here: otherwise every chunk would wait for them (and
+  // for the chunk loads queued behind them) before it first reads the state.
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
+}
+
+// The leaving state: to the caller after the last segment, else to carry and
+// then the chain's flag. Every thread waits until its stores are complete
+// (visible to the device) before the barrier; thread 0 raises the flag after it.
+__device__ __forceinline__ void chain_state_out(const f32x4 (&hacc)[8], int tid, int seg, int64_t flag_ix,
+                                                int64_t state_ix, int64_t s_lane) {
+  if (seg + 1 < kargs()->nseg) {
+    const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + state_ix * (P * NS), P * NS * 4);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hacc[nt]), rS, (int)((s_lane + 16 * nt) * 4), 0,
+                                             kDeviceCoherent);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(kargs()->queue + 256 + flag_ix, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    float* dst = kargs()->h_out + state_ix * (P * NS) + s_lane;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
+  }
+}
+
 // One chunk's staged global loads of one thread, in flight during the previous
 // chunk. Coalesced: 16 lanes cover a 256-byte row of B or C (an instruction, 4
 // rows), 8 lanes a 128-byte row of x (8 rows), so each load touches a few cache
@@ -403,79 +481,12 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   // state slice: hacc[nt][r] = S[p = 16wq + li][n = 16nt + 4lg + r] of head h; stored as [b, h, p, n]
   f32x4 hacc[8];
   const int64_t s_lane = (int64_t)(16 * wq + li) * NS + 4 * lg;
-  // The entering state of the current item: the caller's (or zeros) for a first
-  // segment, else the one the previous segment left in carry, once its chain's
-  // flag says so. The producer of that segment holds an item dequeued earlier
-  // than this one, so it is running and never waits on this workgroup: the wait
-  // ends. Its bound (2^20 polls, about a second) only guarantees that the kernel
-  // terminates; a wait that gives up raises queue[128], which ends every other
-  // wait, and starts its item from a NaN state: every output that depends on a
-  // hand-off that did not happen (the rest of that chain's y and its final
-  // state) comes out NaN rather than silently wrong.
-  // carry and the flags move through device-coherent loads and stores (the sc1
-  // cache policy, as device-scope atomics use), which need no cache write-back
-  // or invalidation (either would flush the L2 that the other workgroups share);
-  // carry moves in 16-byte pieces, so the write-through goes out in whole
-  // 64-byte segments.
+  // the entering state of the current item and the leaving one (chain_state_in / _out)
   auto state_in = [&]() {
-    const int64_t ch = (int64_t)b * hpc + hc;  // the chain: its flag
-    const int64_t hh = (int64_t)b * H + h;     // this wave's head: its state
-    if (seg > 0) {
-      if (tid == 0) {
-        unsigned* flag = kargs()->queue + 256 + ch;
-        bool ready = false, quit = false;
-        for (int n = 0; n < (1 << 20) && !ready && !quit; ++n) {
-          ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg;
-          quit = !ready && __hip_atomic_load(kargs()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-          if (!ready && !quit) __builtin_amdgcn_s_sleep(2);
-        }
-        if (!ready) __hip_atomic_store(kargs()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sTicket[2] = ready ? 0 : 1;
-      }
-      __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(sTicket[2]) != 0) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{NAN, NAN, NAN, NAN};
-      } else {
-        const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + hh * (P * NS), P * NS * 4);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          hacc[nt] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
-      }
-    } else if (kargs()->h0) {
-      const float* src = kargs()->h0 + hh * (P * NS) + s_lane;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // The loads complete here: otherwise every chunk would wait for them (and
-    // for the chunk loads queued behind them) before it first reads the state.
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
+    chain_state_in(hacc, tid, seg, (int64_t)b * hpc + hc, (int64_t)b * H + h, s_lane, sTicket[2]);
   };
-  // The leaving state: to the caller after the last segment, else to carry and
-  // then the chain's flag. Every thread waits until its stores are complete
-  // (visible to the device) before the barrier; thread 0 raises the flag after it.
   auto state_out = [&]() {
-    const int64_t ch = (int64_t)b * hpc + hc;
-    const int64_t hh = (int64_t)b * H + h;
-    if (seg + 1 < kargs()->nseg) {
-      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + hh * (P * NS), P * NS * 4);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hacc[nt]), rS, (int)((s_lane + 16 * nt) * 4), 0,
-                                               kDeviceCoherent);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
-      __syncthreads();
-      if (tid == 0) __hip_atomic_store(kargs()->queue + 256 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      float* dst = kargs()->h_out + hh * (P * NS) + s_lane;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
-    }
+    chain_state_out(hacc, tid, seg, (int64_t)b * hpc + hc, (int64_t)b * H + h, s_lane);
   };
 
   // the tiles of M above the diagonal block row stay zero
@@ -937,59 +948,13 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
 
   f32x4 hacc[8];
   const int64_t s_lane = (int64_t)(16 * wq + li) * NS + 4 * lg;
-  // the entering state, as in ssd_chunk_kernel (the same flags, give-up word and carry)
+  // the entering and leaving state, as in ssd_chunk_kernel (chain_state_in / _out: the
+  // same flags, give-up word and carry; a chain is one head)
   auto state_in = [&]() {
-    const int64_t ch = (int64_t)b * H + h;
-    if (seg > 0) {
-      if (tid == 0) {
-        unsigned* flag = kargs_f()->queue + 256 + ch;
-        bool ready = false, quit = false;
-        for (int n = 0; n < (1 << 20) && !ready && !quit; ++n) {
-          ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)seg;
-          quit = !ready && __hip_atomic_load(kargs_f()->queue + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-          if (!ready && !quit) __builtin_amdgcn_s_sleep(2);
-        }
-        if (!ready) __hip_atomic_store(kargs_f()->queue + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sTicket[2] = ready ? 0 : 1;
-      }
-      __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(sTicket[2]) != 0) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{NAN, NAN, NAN, NAN};
-      } else {
-        const __amdgpu_buffer_rsrc_t rS = rsrc(kargs_f()->carry + ch * (P * NS), P * NS * 4);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          hacc[nt] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS, (int)((s_lane + 16 * nt) * 4), 0, kDeviceCoherent));
-      }
-    } else if (kargs_f()->h0) {
-      const float* src = kargs_f()->h0 + ch * (P * NS) + s_lane;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
+    chain_state_in(hacc, tid, seg, (int64_t)b * H + h, (int64_t)b * H + h, s_lane, sTicket[2]);
   };
   auto state_out = [&]() {
-    const int64_t ch = (int64_t)b * H + h;
-    if (seg + 1 < kargs_f()->nseg) {
-      const __amdgpu_buffer_rsrc_t rS = rsrc(kargs_f()->carry + ch * (P * NS), P * NS * 4);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hacc[nt]), rS, (int)((s_lane + 16 * nt) * 4), 0,
-                                               kDeviceCoherent);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
-      __syncthreads();
-      if (tid == 0) __hip_atomic_store(kargs_f()->queue + 256 + ch, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      float* dst = kargs_f()->h_out + ch * (P * NS) + s_lane;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
-    }
+    chain_state_out(hacc, tid, seg, (int64_t)b * H + h, (int64_t)b * H + h, s_lane);
   };
 
   set_item(cur);
