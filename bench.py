@@ -686,6 +686,16 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
                                      mfma_frac_fp32_q64=fq / (fev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS))
 
 
+def bench_ssd_wide_heads(steps, warmup, torch, bd, gen):
+    """The Mamba-2 2.7B layer's SSD (bf16, 4 x 8192 tokens, state 128) with its 5120
+    channels as 40 heads of 128 columns instead of 80 of 64: the same bytes, on the bf16
+    chunk kernel, which takes each head as two 64-column heads sharing its step and decay."""
+    inp = gen.make_workload(4, nheads=40, head_dim=128)
+    d, _ = bench_workload(4, steps, warmup, torch, bd, gen, inp)
+    d["workload"] = "mamba2-2.7b layer as 40 heads x 128 columns, state 128, bf16 (4 x 8192 tokens)"
+    return d
+
+
 def bench_attention(steps, warmup, torch, bd, gen, L=2048):
     """The hidden attention map of the first L tokens of one batch row of the Mamba-2 2.7B
     workload's distributions (80 heads, one group, state 128): alpha [1, L, L, 80] fp32,
@@ -787,6 +797,8 @@ def main():
         extra["ssd_per_token_states"] = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
         log("bench: SSD with fp32 activations")
         extra["ssd_fp32"] = bench_ssd_f32(max(3, args.steps // 10), 1, torch, bd, gen)
+        log("bench: SSD with head_dim 128")
+        extra["ssd_head_dim_128"] = bench_ssd_wide_heads(max(5, args.steps // 4), 3, torch, bd, gen)
 
     cfg = gen.WORKLOADS[MAIN]
     roof = dict(main_d["roofline"])

@@ -117,6 +117,9 @@ struct SsdKT {
   float* h_out;
   unsigned* queue;  // [16 q]: next item of queue q; [128]: a wait gave up; [256 + ch]: segments of chain ch done
   float* carry;     // [batch * H, P, NS]: the state a segment hands to the next one, per head
+  // H counts heads of P = 64 columns: a caller's head of 64 * 2^hshift columns is
+  // 2^hshift of them, which share that head's step, decay and D (dt_raw has H >> hshift
+  // columns; dt_bias, A_log and D H >> hshift entries)
   int64_t L, H, G;
   int nchunks;      // chunks of 64 tokens per batch row (ceil(L / 64))
   int heads_per_group;
@@ -126,6 +129,7 @@ struct SsdKT {
   int nq;           // work queues; workgroup i serves queue i % nq, which holds chains
                     // [q nchains / nq, (q + 1) nchains / nq): item i of a queue with n chains is
                     // segment i / n of its chain i % n
+  int hshift;       // log2(caller's head_dim / 64)
 };
 typedef SsdKT<uint16_t> SsdK;
 typedef SsdKT<float> SsdKF;
@@ -356,9 +360,11 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   if (cur >= qitems()) return;  // the whole workgroup
   int nxt = -1;
 
-  const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2), dt_row = (uint32_t)(H * 2);
+  // (dt_raw has one column per caller's head: H >> hshift)
+  const int Hd = H >> k.hshift;
+  const uint32_t bc_row = (uint32_t)(G * NS * 2), xz_row = (uint32_t)(H * P * 2), dt_row = (uint32_t)(Hd * 2);
   // elements per batch row
-  const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * H;
+  const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * Hd;
   const int bc_r = tid >> 4, bc_p = tid & 15;         // staging row (+ 16 HPW it) and piece of B, C
   const int x_r = 16 * wq + (l >> 3), x_p = l & 7;    // staging row (+ 8 it) and piece of x
   const uint32_t bc_lane = (uint32_t)(bc_r * bc_row + bc_p * 16);
@@ -402,7 +408,8 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   auto load_x = [&](Prefetch<HPW>& pf) {
     const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
     // only the decay wave of a head uses dt: the other waves' resource is empty (no memory access)
-    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, wq == kDecayWave);
+    const __amdgpu_buffer_rsrc_t rD =
+        tgt_rsrc(k.dt, dt_bat, (uint32_t)(th >> kargs()->hshift), dt_row, wq == kDecayWave);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
       pf.x[it] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(x_lane + it * 8 * xz_row), 0, 0);
@@ -442,9 +449,10 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     g = h / kk->heads_per_group;  // the host guarantees the chain's heads share a group
     c = seg * kk->seg_chunks;
     c_end = min(c + kk->seg_chunks, max((L + Q - 1) / Q, 1));  // seqlen 0: one empty chunk
-    A2 = -expf(kk->A_log[h]) * kLog2e;  // decay per unit step, exp2 domain
-    bias = kk->dt_bias[h];
-    Dh = kk->D[h];
+    const int hp = h >> kk->hshift;  // the caller's head
+    A2 = -expf(kk->A_log[hp]) * kLog2e;  // decay per unit step, exp2 domain
+    bias = kk->dt_bias[hp];
+    Dh = kk->D[hp];
   };
 
   // Chunk at token tt from the prefetch registers into LDS; wave kDecayWave of each
@@ -847,8 +855,9 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
   int nxt = -1;
 
   // row bytes and elements per batch row
-  const uint32_t bc_row = (uint32_t)(G * NS * 4), xz_row = (uint32_t)(H * P * 4), dt_row = (uint32_t)(H * 4);
-  const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * H;
+  const int Hd = H >> k.hshift;  // dt_raw columns (the caller's heads)
+  const uint32_t bc_row = (uint32_t)(G * NS * 4), xz_row = (uint32_t)(H * P * 4), dt_row = (uint32_t)(Hd * 4);
+  const uint32_t bc_bat = (uint32_t)L * (G * NS), xz_bat = (uint32_t)L * (H * P), dt_bat = (uint32_t)L * Hd;
   const int nb = tid & 31, jq = tid >> 5;  // staging of B and C: 16-byte piece, row
   const int xp = tid & 15, xr = tid >> 4;  // staging of x, z and y: 16-byte piece, row
 
@@ -882,7 +891,8 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
   };
   auto load_x = [&](PrefetchF& pf) {
     const __amdgpu_buffer_rsrc_t rX = tgt_rsrc(k.x, xz_bat, (uint32_t)th * P, xz_row);
-    const __amdgpu_buffer_rsrc_t rD = tgt_rsrc(k.dt, dt_bat, (uint32_t)th, dt_row, wq == kDecayWave);
+    const __amdgpu_buffer_rsrc_t rD =
+        tgt_rsrc(k.dt, dt_bat, (uint32_t)(th >> kargs_f()->hshift), dt_row, wq == kDecayWave);
 #pragma unroll
     for (int it = 0; it < 4; ++it) pf.x[it] = ld_f32x4(rX, (uint32_t)(16 * it + xr) * xz_row + xp * 16);
     pf.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (int)(l * dt_row), 0, 0));
@@ -912,9 +922,10 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     g = h / kk->heads_per_group;
     c = seg * kk->seg_chunks;
     c_end = min(c + kk->seg_chunks, max((L + Q - 1) / Q, 1));
-    A2 = -expf(kk->A_log[h]) * kLog2e;
-    bias = kk->dt_bias[h];
-    Dh = kk->D[h];
+    const int hp = h >> kk->hshift;  // the caller's head
+    A2 = -expf(kk->A_log[hp]) * kLog2e;
+    bias = kk->dt_bias[hp];
+    Dh = kk->D[hp];
   };
 
   // Chunk at token tt from the prefetch registers into LDS (B transposed); wave
@@ -1177,6 +1188,23 @@ __global__ __launch_bounds__(640) void ssd_cb_f32_kernel(const float* __restrict
 
 namespace {
 
+// log2(head_dim / 64): a head of 64 * 2^k columns is 2^k heads of 64 columns that
+// share its step, decay and D (its columns are independent given those); -1 for
+// any other head_dim
+int head_shift(int64_t P_) {
+  for (int k = 0; k < 16; ++k)
+    if (P_ == (int64_t)P << k) return k;
+  return -1;
+}
+
+// The problem seen as heads of P = 64 columns (x, y and the states keep their layout)
+SSDArgs by_64_columns(const SSDArgs& a) {
+  SSDArgs v = a;
+  v.H = a.H << head_shift(a.P);
+  v.P = P;
+  return v;
+}
+
 // How the chains are cut into segments and how many workgroups take them. A
 // chain (one head of one batch row) is sequential; with fewer chains than
 // compute units some units idle whatever is done, and with a few more (say 1.25
@@ -1189,6 +1217,7 @@ struct SsdPlan {
   size_t queue_bytes, carry_bytes, cb_bytes, ws_bytes;
 };
 
+// (a: the problem in heads of 64 columns)
 SsdPlan ssd_plan(const SSDArgs& a) {
   const bool f32 = !a.bf16;
   int dev = 0, ncu = 0;
@@ -1256,17 +1285,20 @@ bool ssd_chunk_supported(const SSDArgs& a) {
   // A sequence of length 0 goes to the token loop, which only passes the state through:
   // the chunk kernels size their resources as (L - t0) rows less the head's or group's
   // column offset, which needs at least one token row.
+  // head_dim 64 * 2^k: each head is 2^k heads of 64 columns (by_64_columns).
   const int64_t es = a.bf16 ? 2 : 4;
-  const int64_t row_x = a.L * a.H * P * es, row_bc = a.L * a.G * NS * es;
-  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.L > 0 && a.P == P && a.N == NS &&
-         a.states == nullptr && a.batch * a.H <= (1 << 24) && row_x < (int64_t(1) << 31) &&
-         row_bc < (int64_t(1) << 31);
+  const int hsh = head_shift(a.P);
+  const int64_t row_x = a.L * a.H * a.P * es, row_bc = a.L * a.G * NS * es;
+  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.L > 0 && hsh >= 0 && a.N == NS &&
+         a.states == nullptr && a.H <= (1 << 24) && (a.batch * a.H << hsh) <= (1 << 24) &&
+         row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
 }
 
-size_t ssd_chunk_ws(const SSDArgs& a) { return a.batch == 0 ? 0 : ssd_plan(a).ws_bytes; }
+size_t ssd_chunk_ws(const SSDArgs& a) { return a.batch == 0 ? 0 : ssd_plan(by_64_columns(a)).ws_bytes; }
 
 // fp32 activations: ssd_cb_f32_kernel and ssd_chunk_f32_kernel on the same plan
-hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, void* ws, hipStream_t s) {
+// (a: the problem in heads of 64 columns; hshift: log2 of the caller's head_dim / 64)
+hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s) {
   SsdKF k{};
   k.x = (const float*)a.x; k.dt = (const float*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const float*)a.B; k.C = (const float*)a.C; k.D = a.D; k.z = (const float*)a.z;
@@ -1278,6 +1310,7 @@ hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, void* ws, hi
   k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
   k.nchunks = (int)((a.L + Q - 1) / Q);
   k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
+  k.hshift = hshift;
   const int nwords = 256 + p.nchains;
   const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
   hipLaunchKernelGGL(ssd_cb_f32_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(nblk, 1 << 20))),
@@ -1287,10 +1320,12 @@ hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, void* ws, hi
   return hipGetLastError();
 }
 
-hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
-  if (a.batch == 0) return hipSuccess;
+hipError_t launch_ssd_chunk(const SSDArgs& a_caller, void* ws, hipStream_t s) {
+  if (a_caller.batch == 0) return hipSuccess;
+  const SSDArgs a = by_64_columns(a_caller);
+  const int hshift = head_shift(a_caller.P);
   const SsdPlan p = ssd_plan(a);
-  if (!a.bf16) return launch_ssd_chunk_f32(a, p, ws, s);
+  if (!a.bf16) return launch_ssd_chunk_f32(a, p, hshift, ws, s);
   SsdK k{};
   k.x = (const uint16_t*)a.x; k.dt = (const uint16_t*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const uint16_t*)a.B; k.C = (const uint16_t*)a.C; k.D = a.D; k.z = (const uint16_t*)a.z;
@@ -1302,6 +1337,7 @@ hipError_t launch_ssd_chunk(const SSDArgs& a, void* ws, hipStream_t s) {
   k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
   k.nchunks = (int)((a.L + Q - 1) / Q);
   k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
+  k.hshift = hshift;
   const int nwords = 256 + p.nchains;
   const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
   // (at least one workgroup: it also clears the queues)

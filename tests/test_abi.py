@@ -305,6 +305,12 @@ def test_launch_plans_are_stable_and_follow_the_knobs():
     assert L.sscan_ssd_workspace_size(ctypes.byref(sdesc(seqlen=0))) == 0
     assert L.sscan_ssd_workspace_size(ctypes.byref(sdesc(seqlen=0, act=0))) == 0
     assert L.sscan_ssd_workspace_size(ctypes.byref(f)) == f0
+    # a head of 128 or 256 columns is planned as 2 or 4 heads of 64 columns
+    for act in (1, 0):
+        for P, m in ((128, 2), (256, 4)):
+            wide = sdesc(batch=2, seqlen=3000, nheads=40, head_dim=P, act=act)
+            narrow = sdesc(batch=2, seqlen=3000, nheads=40 * m, head_dim=64, act=act)
+            assert L.sscan_ssd_workspace_size(ctypes.byref(wide)) == L.sscan_ssd_workspace_size(ctypes.byref(narrow))
 
 
 def _cpu(*shape, dtype=None):

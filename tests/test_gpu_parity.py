@@ -2,6 +2,8 @@
 the same seeded inputs. Every case, the five workloads at full size included,
 compares every output element; bf16 results are held to the relative L2 budget
 and to the element-wise bound of tests/_gpu.py."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -199,12 +201,20 @@ SSD_CASES = [
     (1, 2100, 2, 64, 128, 1, "bf16", True, True, False),
     (2, 300, 4, 32, 128, 2, "f32", True, True, True),    # token loop, 16 lanes a channel: groups, slices, states
     (1, 150, 2, 64, 100, 1, "bf16", True, True, True),   # 100 of a padded 128, slices, states
-    (1, 1100, 2, 128, 64, 1, "bf16", True, True, False), # head_dim 128: the token loop
-    # head_dim and state_dim 128 on the token loop (fp32, and bf16 with states and
-    # groups), with slices; head_dim 160
-    (1, 600, 2, 128, 128, 1, "f32", True, True, False),
+    (1, 1100, 2, 128, 64, 1, "bf16", True, True, False), # head_dim 128, state_dim 64: the token loop
+    # head_dim and state_dim 128: bf16 with states and groups on the token loop, with
+    # slices; head_dim 160 (not 64 times a power of two) and 96 on the token loop
     (1, 500, 2, 128, 128, 2, "bf16", True, True, True),
     (1, 300, 2, 160, 64, 1, "f32", True, False, False),
+    (1, 400, 3, 96, 128, 1, "bf16", True, True, False),
+    # head_dim 128 and 256 on the chunk kernels (each head as 64-column heads that
+    # share its step, decay and D): chunk edges, ragged tails, groups
+    (1, 600, 2, 128, 128, 1, "f32", True, True, False),
+    (2, 700, 3, 128, 128, 1, "bf16", True, True, False),
+    (1, 129, 4, 128, 128, 2, "bf16", False, False, False),
+    (2, 300, 4, 128, 128, 4, "f32", True, False, False),
+    (1, 1500, 2, 256, 128, 2, "bf16", True, True, False),
+    (1, 65, 2, 256, 128, 1, "f32", True, True, False),
     # fp32 activations on the fp32 MFMA chunk kernel: one token, chunk edges, ragged
     # tails, groups, long sequences (segments)
     (1, 1, 2, 64, 128, 1, "f32", True, True, False),
@@ -276,6 +286,48 @@ def test_ssd_f32_forced_segments(case, tuning):
     bd.set_tuning(bd.TUNE_SSD_WORKGROUPS, 0)
     yw, hw, _ = run_ssd(inp)
     assert np.array_equal(got[0], yw) and np.array_equal(got[1], hw)
+
+
+def _as_64_column_heads(inp):
+    """The same problem with each head of 64 m columns written as m heads of 64 columns,
+    each with its head's step, decay and D: x, z, y and the states keep their bytes."""
+    m = inp.head_dim // 64
+    rep = lambda a: None if a is None else np.ascontiguousarray(np.repeat(a, m, axis=-1))
+    b, L, H = inp.batch, inp.seqlen, inp.nheads
+    cols = lambda a: None if a is None else np.ascontiguousarray(a.reshape(b, L, H * m, 64))
+    return dataclasses.replace(
+        inp, nheads=H * m, head_dim=64, x=cols(inp.x), z=cols(inp.z), dt_raw=rep(inp.dt_raw),
+        dt_bias=rep(inp.dt_bias), A_log=rep(inp.A_log), D=rep(inp.D),
+        h0=None if inp.h0 is None else np.ascontiguousarray(inp.h0.reshape(b, H * m, 64, inp.state_dim)))
+
+
+HEAD_DIM_CASES = [
+    # head_dim, batch, seqlen, H, G, act, gate, h0, segment chunks (0: the plan's)
+    (128, 2, 700, 3, 1, "bf16", True, True, 0),
+    (128, 1, 1000, 4, 2, "bf16", True, False, 3),
+    (256, 1, 500, 2, 1, "bf16", False, True, 1),
+    (128, 2, 300, 4, 2, "f32", True, True, 0),
+    (256, 1, 600, 2, 2, "f32", True, True, 2),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_DIM_CASES, ids=lambda c: "P%d_b%d_L%d_H%d_G%d_%s_g%d_h%d_seg%d" % c)
+def test_ssd_wide_heads_equal_their_64_column_heads(case, tuning):
+    """The chunk kernels take a head of 64 m columns as m heads of 64 columns that share
+    its step, decay and D. Written out that way by the caller (dt_raw, dt_bias, A_log and
+    D repeated per column block), the same call must give bit-identical y and state;
+    both against the oracle."""
+    P, b, L, H, G, act, gate, h0, seg = case
+    say("ssd wide heads", case)
+    if seg:
+        tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, seg)
+    inp = gen.make_ssd(b, L, H, P, 128, G, act=act, seed=P + L + H, gate=gate, h0=h0)
+    assert ssd_chunk_path(inp, False)
+    wide = run_ssd(inp)
+    narrow = run_ssd(_as_64_column_heads(inp))
+    assert np.array_equal(wide[0].reshape(-1), narrow[0].reshape(-1))
+    assert np.array_equal(wide[1].reshape(-1), narrow[1].reshape(-1))
+    check_all(inp, wide, oracle.run_inputs(inp), "ssd")
 
 
 def test_ssd_f32_chunk_kernel_agrees_with_token_loop():
