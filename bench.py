@@ -686,13 +686,15 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
                                      mfma_frac_fp32_q64=fq / (fev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS))
 
 
-def bench_ssd_wide_heads(steps, warmup, torch, bd, gen):
-    """The Mamba-2 2.7B layer's SSD (bf16, 4 x 8192 tokens, state 128) with its 5120
-    channels as 40 heads of 128 columns instead of 80 of 64: the same bytes, on the bf16
-    chunk kernel, which takes each head as two 64-column heads sharing its step and decay."""
-    inp = gen.make_workload(4, nheads=40, head_dim=128)
+def bench_ssd_shape(steps, warmup, torch, bd, gen, label, **overrides):
+    """The Mamba-2 2.7B layer's SSD (bf16, 4 x 8192 tokens) at another head or state
+    shape on the bf16 chunk kernel: 40 heads of 128 columns (the same channels; each head
+    runs as two 64-column heads sharing its step and decay), or state_dim 64 (B, C and
+    the states zero-padded to 128 in the workspace, so the kernel does the work of 128;
+    the padding and un-padding kernels are in the call's time)."""
+    inp = gen.make_workload(4, **overrides)
     d, _ = bench_workload(4, steps, warmup, torch, bd, gen, inp)
-    d["workload"] = "mamba2-2.7b layer as 40 heads x 128 columns, state 128, bf16 (4 x 8192 tokens)"
+    d["workload"] = label
     return d
 
 
@@ -797,8 +799,13 @@ def main():
         extra["ssd_per_token_states"] = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
         log("bench: SSD with fp32 activations")
         extra["ssd_fp32"] = bench_ssd_f32(max(3, args.steps // 10), 1, torch, bd, gen)
-        log("bench: SSD with head_dim 128")
-        extra["ssd_head_dim_128"] = bench_ssd_wide_heads(max(5, args.steps // 4), 3, torch, bd, gen)
+        log("bench: SSD with head_dim 128, with state_dim 64")
+        extra["ssd_head_dim_128"] = bench_ssd_shape(
+            max(5, args.steps // 4), 3, torch, bd, gen,
+            "mamba2-2.7b layer as 40 heads x 128 columns, state 128, bf16 (4 x 8192 tokens)", nheads=40, head_dim=128)
+        extra["ssd_state_dim_64"] = bench_ssd_shape(
+            max(5, args.steps // 4), 3, torch, bd, gen,
+            "mamba2-2.7b layer with state_dim 64, bf16 (4 x 8192 tokens x 80 heads x 64)", state_dim=64)
 
     cfg = gen.WORKLOADS[MAIN]
     roof = dict(main_d["roofline"])

@@ -131,8 +131,8 @@ sscan_status sscan_step(const sscan_mamba1_desc* desc, const float* state_input,
 size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
 
 /* Byte offset, in the workspace of an sscan_ssd_fwd call that takes the MFMA
- * chunk path (head_dim 64, 128, 256, ..., state_dim 128, states NULL; act bf16,
- * or f32 unless SSCAN_TUNE_SSD_F32_TOKEN_LOOP is set), of a 32-bit
+ * chunk path (head_dim 64, 128, 256, ..., state_dim 64..128, states NULL; act
+ * bf16, or f32 unless SSCAN_TUNE_SSD_F32_TOKEN_LOOP is set), of a 32-bit
  * word that is 0 after the call unless a state hand-off between two segments of
  * a head's sequence gave up waiting (see sscan_ssd_fwd). */
 #define SSCAN_SSD_GIVEUP_WORD_OFFSET 512
@@ -149,12 +149,14 @@ size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
  *   states        [batch, seqlen, nheads, head_dim, state_dim] f32 (out) or NULL
  * The state is stored value side (head_dim) first and state_dim innermost: entry
  * [b, h, p, n] is the pages' [b, h, key n, value p]. state_dim in 1..128.
- * head_dim 64 times a power of two (64, 128, 256, ...) with state_dim 128 and no
- * per-token states takes the MFMA chunk path: bf16 MFMA for bf16 activations, fp32
- * MFMA (fp32 products and sums) for fp32 ones. A head of 64 m columns runs as m
+ * head_dim 64 times a power of two (64, 128, 256, ...) with state_dim 64..128 and
+ * no per-token states takes the MFMA chunk path: bf16 MFMA for bf16 activations,
+ * fp32 MFMA (fp32 products and sums) for fp32 ones. A head of 64 m columns runs as m
  * heads of 64 columns that share its step, decay and D (its columns are
  * independent given those), so its results are those of that split, bit for bit.
- * Other shapes take the token loop (fp32 arithmetic).
+ * state_dim below 128 runs on B, C and states padded with zero states in the
+ * workspace (the padded entries stay exactly zero), with the results of that
+ * padding, bit for bit. Other shapes take the token loop (fp32 arithmetic).
  * The MFMA chunk path cuts a head's sequence into segments that different
  * workgroups scan, each handing its final state to the next through the
  * workspace. The kernel's own scheduling guarantees every hand-off wait ends;

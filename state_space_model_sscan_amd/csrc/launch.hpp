@@ -85,7 +85,7 @@ hipError_t launch_ssd_step(const SSDArgs& a, hipStream_t s);
 constexpr size_t kScratchBytes = size_t(16) << 20;
 hipError_t scratch_ptr(void** out);
 
-// MFMA chunk SSD (ssd_chunk.hip): bf16 or fp32, head_dim 64 times a power of two, state_dim 128,
+// MFMA chunk SSD (ssd_chunk.hip): bf16 or fp32, head_dim 64 times a power of two, state_dim 64..128,
 // no per-token states.
 bool ssd_chunk_supported(const SSDArgs& a);
 size_t ssd_chunk_ws(const SSDArgs& a);

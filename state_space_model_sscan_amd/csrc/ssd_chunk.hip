@@ -1186,6 +1186,26 @@ __global__ __launch_bounds__(640) void ssd_cb_f32_kernel(const float* __restrict
   }
 }
 
+// state_dim 64..127 on the chunk kernels: rows of nin entries (B, C, the entering
+// state) copied into rows of NS with zeros after them, and the leaving state's rows
+// cut back to nout entries. With B, C and the entering state zero in states
+// nin..NS-1, those state columns stay exactly zero (each update scales zero and adds
+// a zero product) and add exact zeros to every C.B^T and C.S sum, so states 0..nin-1
+// and y are the unpadded problem's. One workgroup of NS threads per row.
+template <typename T>
+__global__ __launch_bounds__(NS) void pad_state_rows_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                            int64_t rows, int nin) {
+  const int j = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) dst[r * NS + j] = j < nin ? src[r * nin + j] : T(0);
+}
+
+__global__ __launch_bounds__(NS) void unpad_state_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                              int64_t rows, int nout) {
+  const int j = threadIdx.x;
+  if (j >= nout) return;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) dst[r * nout + j] = src[r * NS + j];
+}
+
 namespace {
 
 // log2(head_dim / 64): a head of 64 * 2^k columns is 2^k heads of 64 columns that
@@ -1215,6 +1235,7 @@ SSDArgs by_64_columns(const SSDArgs& a) {
 struct SsdPlan {
   int hpw, nchains, seg_chunks, nseg, nq, grid;
   size_t queue_bytes, carry_bytes, cb_bytes, ws_bytes;
+  size_t pad_bc_bytes, pad_state_bytes;  // state_dim < NS: each padded B, C and state copy
 };
 
 // (a: the problem in heads of 64 columns)
@@ -1274,7 +1295,12 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   p.queue_bytes = ((size_t)(256 + p.nchains) * 4 + 255) / 256 * 256;
   p.carry_bytes = p.nseg > 1 ? (size_t)(a.batch * a.H) * P * NS * 4 : 0;
   p.cb_bytes = (size_t)a.batch * (size_t)((a.L + Q - 1) / Q) * (size_t)a.G * kTiles * kTileFloats * 4;
-  p.ws_bytes = p.queue_bytes + p.carry_bytes + p.cb_bytes;
+  // state_dim below NS: B and C padded to NS states, and the entering and leaving
+  // states as [batch, H, P, NS] (after the C B^T tiles, 256-byte aligned)
+  const size_t es = f32 ? 4 : 2;
+  p.pad_bc_bytes = a.N < NS ? ((size_t)(a.batch * a.L * a.G) * NS * es + 255) / 256 * 256 : 0;
+  p.pad_state_bytes = a.N < NS ? (size_t)(a.batch * a.H) * P * NS * 4 : 0;
+  p.ws_bytes = p.queue_bytes + p.carry_bytes + p.cb_bytes + 2 * p.pad_bc_bytes + 2 * p.pad_state_bytes;
   return p;
 }
 
@@ -1289,7 +1315,8 @@ bool ssd_chunk_supported(const SSDArgs& a) {
   const int64_t es = a.bf16 ? 2 : 4;
   const int hsh = head_shift(a.P);
   const int64_t row_x = a.L * a.H * a.P * es, row_bc = a.L * a.G * NS * es;
-  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.L > 0 && hsh >= 0 && a.N == NS &&
+  // state_dim 64..NS: below NS, zero-padded in the workspace (pad_state_rows_kernel).
+  return (a.bf16 || knob(kKnobSsdF32TokenLoop) == 0) && a.L > 0 && hsh >= 0 && a.N >= 64 && a.N <= NS &&
          a.states == nullptr && a.H <= (1 << 24) && (a.batch * a.H << hsh) <= (1 << 24) &&
          row_x < (int64_t(1) << 31) && row_bc < (int64_t(1) << 31);
 }
@@ -1320,12 +1347,8 @@ hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, int hshift, 
   return hipGetLastError();
 }
 
-hipError_t launch_ssd_chunk(const SSDArgs& a_caller, void* ws, hipStream_t s) {
-  if (a_caller.batch == 0) return hipSuccess;
-  const SSDArgs a = by_64_columns(a_caller);
-  const int hshift = head_shift(a_caller.P);
-  const SsdPlan p = ssd_plan(a);
-  if (!a.bf16) return launch_ssd_chunk_f32(a, p, hshift, ws, s);
+// bf16 activations: ssd_cb_kernel and ssd_chunk_kernel (a, hshift as for the fp32 launch)
+static hipError_t launch_ssd_chunk_bf16(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s) {
   SsdK k{};
   k.x = (const uint16_t*)a.x; k.dt = (const uint16_t*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const uint16_t*)a.B; k.C = (const uint16_t*)a.C; k.D = a.D; k.z = (const uint16_t*)a.z;
@@ -1348,6 +1371,55 @@ hipError_t launch_ssd_chunk(const SSDArgs& a_caller, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);
   else
     hipLaunchKernelGGL(ssd_chunk_kernel<1>, dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+  return hipGetLastError();
+}
+
+static hipError_t launch_ssd_chunk_padded(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s);
+
+hipError_t launch_ssd_chunk(const SSDArgs& a_caller, void* ws, hipStream_t s) {
+  if (a_caller.batch == 0) return hipSuccess;
+  const SSDArgs a = by_64_columns(a_caller);
+  const int hshift = head_shift(a_caller.P);
+  const SsdPlan p = ssd_plan(a);
+  if (a.N < NS) return launch_ssd_chunk_padded(a, p, hshift, ws, s);
+  return a.bf16 ? launch_ssd_chunk_bf16(a, p, hshift, ws, s) : launch_ssd_chunk_f32(a, p, hshift, ws, s);
+}
+
+// state_dim below NS: B, C and the entering state padded with zero states into the
+// workspace (after the C B^T tiles), the chunk kernels run at NS on those copies,
+// and the leaving state's first N entries per row go to the caller.
+static hipError_t launch_ssd_chunk_padded(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s) {
+  char* base = (char*)ws + p.queue_bytes + p.carry_bytes + p.cb_bytes;
+  void* pB = base;
+  void* pC = base + p.pad_bc_bytes;
+  float* pH0 = (float*)(base + 2 * p.pad_bc_bytes);
+  float* pHo = (float*)(base + 2 * p.pad_bc_bytes + p.pad_state_bytes);
+  const int64_t bc_rows = a.batch * a.L * a.G, st_rows = a.batch * a.H * P;
+  auto grid = [](int64_t rows) { return dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(rows, 1 << 16))); };
+  if (a.bf16) {
+    hipLaunchKernelGGL(pad_state_rows_kernel<uint16_t>, grid(bc_rows), dim3(NS), 0, s, (const uint16_t*)a.B,
+                       (uint16_t*)pB, bc_rows, (int)a.N);
+    hipLaunchKernelGGL(pad_state_rows_kernel<uint16_t>, grid(bc_rows), dim3(NS), 0, s, (const uint16_t*)a.C,
+                       (uint16_t*)pC, bc_rows, (int)a.N);
+  } else {
+    hipLaunchKernelGGL(pad_state_rows_kernel<float>, grid(bc_rows), dim3(NS), 0, s, (const float*)a.B, (float*)pB,
+                       bc_rows, (int)a.N);
+    hipLaunchKernelGGL(pad_state_rows_kernel<float>, grid(bc_rows), dim3(NS), 0, s, (const float*)a.C, (float*)pC,
+                       bc_rows, (int)a.N);
+  }
+  if (a.h0)
+    hipLaunchKernelGGL(pad_state_rows_kernel<float>, grid(st_rows), dim3(NS), 0, s, a.h0, pH0, st_rows, (int)a.N);
+  SSDArgs v = a;
+  v.N = NS;
+  v.B = pB;
+  v.C = pC;
+  v.h0 = a.h0 ? pH0 : nullptr;
+  v.h_out = pHo;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = v.bf16 ? launch_ssd_chunk_bf16(v, p, hshift, ws, s) : launch_ssd_chunk_f32(v, p, hshift, ws, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(unpad_state_rows_kernel, grid(st_rows), dim3(NS), 0, s, pHo, a.h_out, st_rows, (int)a.N);
   return hipGetLastError();
 }
 

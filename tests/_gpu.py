@@ -66,9 +66,10 @@ def run_mamba1(inp, want_states=None, state_input=None):
 def ssd_chunk_path(inp, want_states, token_loop=False):
     """Whether sscan_ssd_fwd takes the MFMA chunk path for these inputs (bf16 MFMA for
     bf16 activations, fp32 MFMA for fp32 ones; token_loop: fp32 sent to the token loop):
-    head_dim 64 times a power of two, state_dim 128, no per-token states."""
+    head_dim 64 times a power of two, state_dim 64..128 (below 128 zero-padded), no
+    per-token states."""
     m = inp.head_dim // 64
-    return (inp.head_dim % 64 == 0 and m & (m - 1) == 0 and inp.state_dim == 128 and not want_states
+    return (inp.head_dim % 64 == 0 and m & (m - 1) == 0 and 64 <= inp.state_dim <= 128 and not want_states
             and inp.seqlen > 0 and (inp.act == "bf16" or not token_loop))
 
 

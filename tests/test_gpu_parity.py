@@ -196,12 +196,12 @@ SSD_CASES = [
     (1, 256, 2, 64, 128, 1, "bf16", True, False, False),
     (1, 257, 2, 64, 128, 1, "bf16", True, True, False),
     (2, 1000, 4, 64, 128, 2, "bf16", True, True, False),
-    (1, 300, 3, 32, 64, 1, "f32", True, True, False),
-    (1, 700, 2, 64, 16, 1, "bf16", False, False, False),
+    (1, 300, 3, 32, 64, 1, "f32", True, True, False),    # head_dim 32: the token loop
+    (1, 700, 2, 64, 16, 1, "bf16", False, False, False), # state_dim 16: the token loop
     (1, 2100, 2, 64, 128, 1, "bf16", True, True, False),
     (2, 300, 4, 32, 128, 2, "f32", True, True, True),    # token loop, 16 lanes a channel: groups, slices, states
     (1, 150, 2, 64, 100, 1, "bf16", True, True, True),   # 100 of a padded 128, slices, states
-    (1, 1100, 2, 128, 64, 1, "bf16", True, True, False), # head_dim 128, state_dim 64: the token loop
+    (1, 1100, 2, 128, 64, 1, "bf16", True, True, False), # head_dim 128, state_dim 64 (padded): chunk kernel
     # head_dim and state_dim 128: bf16 with states and groups on the token loop, with
     # slices; head_dim 160 (not 64 times a power of two) and 96 on the token loop
     (1, 500, 2, 128, 128, 2, "bf16", True, True, True),
@@ -215,6 +215,13 @@ SSD_CASES = [
     (2, 300, 4, 128, 128, 4, "f32", True, False, False),
     (1, 1500, 2, 256, 128, 2, "bf16", True, True, False),
     (1, 65, 2, 256, 128, 1, "f32", True, True, False),
+    # state_dim 64..127 on the chunk kernels (B, C and the states zero-padded to 128 in
+    # the workspace); state_dim 64 with per-token states on the token loop
+    (2, 500, 3, 64, 64, 1, "bf16", True, True, False),
+    (2, 65, 2, 64, 64, 1, "f32", True, False, False),
+    (1, 257, 2, 64, 100, 2, "f32", True, True, False),
+    (1, 777, 4, 64, 80, 1, "bf16", False, True, False),
+    (1, 600, 2, 64, 64, 1, "bf16", True, True, True),
     # fp32 activations on the fp32 MFMA chunk kernel: one token, chunk edges, ragged
     # tails, groups, long sequences (segments)
     (1, 1, 2, 64, 128, 1, "f32", True, True, False),
@@ -328,6 +335,37 @@ def test_ssd_wide_heads_equal_their_64_column_heads(case, tuning):
     assert np.array_equal(wide[0].reshape(-1), narrow[0].reshape(-1))
     assert np.array_equal(wide[1].reshape(-1), narrow[1].reshape(-1))
     check_all(inp, wide, oracle.run_inputs(inp), "ssd")
+
+
+NARROW_STATE_CASES = [
+    # state_dim, head_dim, batch, seqlen, H, G, act, h0, segment chunks (0: the plan's)
+    (64, 64, 2, 700, 3, 1, "bf16", True, 0),
+    (64, 128, 1, 900, 2, 2, "bf16", True, 3),
+    (96, 64, 1, 500, 4, 1, "f32", True, 1),
+    (64, 64, 2, 300, 2, 2, "f32", False, 0),
+]
+
+
+@pytest.mark.parametrize("case", NARROW_STATE_CASES, ids=lambda c: "N%d_P%d_b%d_L%d_H%d_G%d_%s_h%d_seg%d" % c)
+def test_ssd_narrow_state_equals_zero_padded(case, tuning):
+    """state_dim below 128 on the chunk kernels: the library pads B, C and the entering
+    state with zero states. The caller padding them itself must give bit-identical y and
+    the same state, whose padded entries come out exactly zero; both against the oracle."""
+    N, P, b, L, H, G, act, h0, seg = case
+    say("ssd narrow state", case)
+    if seg:
+        tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, seg)
+    inp = gen.make_ssd(b, L, H, P, N, G, act=act, seed=N + P + L, gate=True, h0=h0)
+    assert ssd_chunk_path(inp, False)
+    pad = lambda a: None if a is None else np.ascontiguousarray(
+        np.concatenate([a, np.zeros(a.shape[:-1] + (128 - N,), a.dtype)], axis=-1))
+    wide = dataclasses.replace(inp, state_dim=128, B=pad(inp.B), C=pad(inp.C), h0=pad(inp.h0))
+    got = run_ssd(inp)
+    ref = run_ssd(wide)
+    assert np.array_equal(got[0], ref[0])
+    assert np.array_equal(got[1], ref[1][..., :N])
+    assert not np.any(ref[1][..., N:])
+    check_all(inp, got, oracle.run_inputs(inp), "ssd")
 
 
 def test_ssd_f32_chunk_kernel_agrees_with_token_loop():

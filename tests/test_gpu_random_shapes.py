@@ -4,8 +4,8 @@ against the oracle with the same bounds as the other parity tests.
 The shapes are drawn so that the launch plans pick each of their kernels: for
 Mamba-1 the row, quad and general prompt kernels and the token loop (state_dim up to
 256, groups, the B/C norm, slices of long sequences), for the SSD the MFMA chunk
-kernels (bf16 and fp32, head_dim 64 or 128, state_dim 128, with segments) and the token
-loop (other head and state sizes, per-token states). Lengths include 1, chunk and tile
+kernels (bf16 and fp32, head_dim 64 or 128, state_dim 64 to 128, with segments) and the
+token loop (other head and state sizes, per-token states). Lengths include 1, chunk and tile
 edges and ragged tails. Sizes stay small enough for the oracle to take well under a
 second per case."""
 import numpy as np
@@ -56,7 +56,8 @@ def _ssd_cases(n=20, seed=20261204):
     cases = []
     while len(cases) < n:
         if rng.random() < 0.5:  # the MFMA chunk kernels' shapes (bf16, and fp32 a third of the time)
-            P, N, act, states = int(rng.choice([64, 64, 128])), 128, str(rng.choice(["bf16", "bf16", "f32"])), False
+            P, N = int(rng.choice([64, 64, 128])), int(rng.choice([128, 128, 64]))
+            act, states = str(rng.choice(["bf16", "bf16", "f32"])), False
         else:
             P = int(rng.choice([1, 2, 16, 32, 64, 64, 96, 128]))
             N = int(rng.choice([1, 5, 16, 32, 64, 100, 128]))
