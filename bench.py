@@ -631,16 +631,18 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
     (8192 tokens x 80 heads x 64, state 128): the fp32 MFMA chunk kernel, and beside it
     the same call sent to the fp32 token loop (16 lanes per head_dim column) by the
     tuning knob, the path fp32 activations of other shapes take. One batch row has 80
-    chains for 256 compute units; `full_batch` times the layer's whole batch of 4 (320
-    chains) on the chunk kernel."""
+    chains for 256 compute units, so the plan takes two passes (`one_pass`: the same call
+    forced to one pass); `full_batch` times the layer's whole batch of 4 (320 chains, one
+    pass) on the chunk kernel."""
     inp = gen.make_workload(4, batch=1, act="f32")
     base = upload(inp, torch)
     b, L, H, P, N = inp.batch, inp.seqlen, inp.nheads, inp.head_dim, inp.state_dim
     y = torch.empty_like(base["x"])
     h = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
 
-    def run(token_loop):
+    def run(token_loop, one_pass=False):
         prev = bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1 if token_loop else 0)
+        prev_tp = bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 1 if one_pass else 0)
         try:
             ws_n = bd.sscan_ssd_workspace_size(bd.ssd_desc(base["x"], base["B"], inp.chunk))
             ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
@@ -653,8 +655,10 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
             return time_calls(fn, [None], steps, warmup, torch)
         finally:
             bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, prev)
+            bd.set_tuning(bd.TUNE_SSD_TWO_PASS, prev_tp)
 
     wall, ev = run(False)
+    owall, oev = run(False, one_pass=True)
     lwall, lev = run(True)
     del base, y, h
     torch.cuda.empty_cache()
@@ -679,11 +683,28 @@ def bench_ssd_f32(steps, warmup, torch, bd, gen):
                      updates_per_s=b * L * H * P * N / (ev["mean"] * 1e-3),
                      mfma_flops_q64=ssd_flops(inp, 64),
                      mfma_frac_fp32_q64=ssd_flops(inp, 64) / (ev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS,
+                     one_pass=dict(ms_per_step=owall, kernel_ms=oev, tokens_per_s=b * L / (owall * 1e-3)),
                      token_loop=dict(ms_per_step=lwall, kernel_ms=lev, tokens_per_s=b * L / (lwall * 1e-3)),
                      full_batch=dict(workload="4 x 8192 tokens x 80 heads x 64, state 128, fp32", ms_per_step=fwall,
                                      kernel_ms=fev, tokens_per_s=full.batch * L / (fwall * 1e-3),
                                      hbm_frac=ssd_bytes(full) / (fev["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                      mfma_frac_fp32_q64=fq / (fev["mean"] * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS))
+
+
+def bench_ssd_one_row(steps, warmup, torch, bd, gen):
+    """The Mamba-2 2.7B layer's SSD for one batch row (bf16, 8192 tokens x 80 heads): 80
+    chains for 256 compute units, so the plan takes two passes; `one_pass` is the same
+    call forced to one pass (segments handing their states on in turn)."""
+    inp = gen.make_workload(4, batch=1)
+    d, _ = bench_workload(4, steps, warmup, torch, bd, gen, inp)
+    d["workload"] = "mamba2-2.7b layer, one batch row, bf16 (1 x 8192 tokens x 80 heads x 64, state 128)"
+    prev = bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 1)
+    try:
+        o, _ = bench_workload(4, steps, warmup, torch, bd, gen, inp)
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_TWO_PASS, prev)
+    d["one_pass"] = dict(ms_per_step=o["ms_per_step"], kernel_ms=o["kernel_ms"], tokens_per_s=o["tokens_per_s"])
+    return d
 
 
 def bench_ssd_shape(steps, warmup, torch, bd, gen, label, **overrides):
@@ -799,6 +820,8 @@ def main():
         extra["ssd_per_token_states"] = bench_ssd_states(max(5, args.steps // 10), 2, torch, bd, gen)
         log("bench: SSD with fp32 activations")
         extra["ssd_fp32"] = bench_ssd_f32(max(3, args.steps // 10), 1, torch, bd, gen)
+        log("bench: SSD, one batch row")
+        extra["ssd_one_row"] = bench_ssd_one_row(max(5, args.steps // 4), 3, torch, bd, gen)
         log("bench: SSD with head_dim 128, with state_dim 64")
         extra["ssd_head_dim_128"] = bench_ssd_shape(
             max(5, args.steps // 4), 3, torch, bd, gen,

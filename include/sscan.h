@@ -158,12 +158,17 @@ size_t sscan_ssd_workspace_size(const sscan_ssd_desc* desc);
  * workspace (the padded entries stay exactly zero), with the results of that
  * padding, bit for bit. Other shapes take the token loop (fp32 arithmetic).
  * The MFMA chunk path cuts a head's sequence into segments that different
- * workgroups scan, each handing its final state to the next through the
- * workspace. The kernel's own scheduling guarantees every hand-off wait ends;
- * its bound exists only so that the kernel always terminates. A wait that gives
- * up sets the word at SSCAN_SSD_GIVEUP_WORD_OFFSET and starts its segment from a
- * NaN state, so every output that depends on the missing hand-off (the rest of
- * that head's y, and its state_output) is NaN, never silently wrong. */
+ * workgroups scan. In one pass each segment hands its final state to the next
+ * through the workspace. The kernel's own scheduling guarantees every hand-off
+ * wait ends; its bound exists only so that the kernel always terminates. A wait
+ * that gives up sets the word at SSCAN_SSD_GIVEUP_WORD_OFFSET and starts its
+ * segment from a NaN state, so every output that depends on the missing hand-off
+ * (the rest of that head's y, and its state_output) is NaN, never silently wrong.
+ * With fewer heads x batch rows than the GPU has compute units the path takes two
+ * passes instead (SSCAN_TUNE_SSD_TWO_PASS): every segment but the last is first
+ * scanned from a zero state, then every segment runs at once from its entering
+ * state, folded from those (S_in of the next segment = 2^(segment's sum of dt*A,
+ * exp2 domain) S_in + the segment's state from zero); nothing waits. */
 sscan_status sscan_ssd_fwd(const sscan_ssd_desc* desc, const void* x, const void* dt_raw,
                            const float* dt_bias, const float* A_log, const void* B, const void* C,
                            const float* D, const void* z, const float* state_input, void* y,
@@ -279,8 +284,13 @@ typedef enum {
   SSCAN_TUNE_SSD_HEADS_PER_WORKGROUP = 5, /* 2: two neighbouring heads of a group share a workgroup of
                                        the SSD chunk path, with B, C and C.B^T staged once (by
                                        default one head per workgroup; same results; bf16 only) */
-  SSCAN_TUNE_SSD_F32_TOKEN_LOOP = 6 /* nonzero: fp32 activations of sscan_ssd_fwd take the token loop
-                                       instead of the fp32 MFMA chunk path (head_dim 64, state_dim 128) */
+  SSCAN_TUNE_SSD_F32_TOKEN_LOOP = 6, /* nonzero: fp32 activations of sscan_ssd_fwd take the token loop
+                                       instead of the fp32 MFMA chunk path */
+  SSCAN_TUNE_SSD_TWO_PASS = 7       /* the SSD chunk path's form: 1 one pass (a head's segments hand
+                                       their states on in turn), 2 two passes (every segment but the
+                                       last from a zero state, then all segments at once from states
+                                       folded from those); 0 the library's choice (two passes when a
+                                       problem has too few heads x batch rows to fill the GPU) */
 } sscan_tune_knob;
 int64_t sscan_set_tuning(int knob, int64_t value);
 

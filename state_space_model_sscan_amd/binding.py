@@ -29,6 +29,7 @@ EXPORTS = ["sscan_mamba1_workspace_size", "sscan_mamba1_fwd", "sscan_step", "ssc
 TUNE_M1_LANES, TUNE_SSD_SEGMENT_CHUNKS, TUNE_SSD_WORKGROUPS, TUNE_SSD_GIVE_UP = 1, 2, 3, 4
 TUNE_SSD_HEADS_PER_WORKGROUP = 5
 TUNE_SSD_F32_TOKEN_LOOP = 6
+TUNE_SSD_TWO_PASS = 7
 # Byte offset of the give-up word in the workspace of an SSD call on the MFMA chunk path.
 SSD_GIVEUP_WORD_OFFSET = 512
 

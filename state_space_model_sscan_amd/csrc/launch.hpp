@@ -15,7 +15,8 @@ enum Knob {
   kKnobSsdGiveUp = 4,        // nonzero: every state hand-off wait of the chunk kernel gives up at once
   kKnobSsdHeadsPerWorkgroup = 5,  // 2: two heads per workgroup of the chunk kernel where they share a group
   kKnobSsdF32TokenLoop = 6,  // nonzero: fp32 SSD activations take the token loop, not the fp32 chunk kernel
-  kKnobCount = 7
+  kKnobSsdTwoPass = 7,       // SSD chunk kernels: 1 one pass (chained segments), 2 two passes; 0 the plan's choice
+  kKnobCount = 8
 };
 int64_t knob(int which);
 

@@ -130,6 +130,10 @@ struct SsdKT {
                     // [q nchains / nq, (q + 1) nchains / nq): item i of a queue with n chains is
                     // segment i / n of its chain i % n
   int hshift;       // log2(caller's head_dim / 64)
+  // two passes (kLocal, then kFolded): lam[s * nstates + head] is the sum over segment s
+  // of the head's a_t (exp2 domain), carry[s * nstates + head] its state from zero
+  float* lam;
+  int nstates;      // batch * H
 };
 typedef SsdKT<uint16_t> SsdK;
 typedef SsdKT<float> SsdKF;
@@ -220,8 +224,8 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 // hacc: this wave's state slice, S[p = 16 wq + li][n = 16 nt + 4 lg + r] in lane l,
 // register r of tile nt; flag_ix: the chain's flag; state_ix: the head's state; s_lane:
 // the lane's offset in a [P, NS] state; ticket: a word of workgroup memory.
-__device__ __forceinline__ void chain_state_in(f32x4 (&hacc)[8], int tid, int seg, int64_t flag_ix, int64_t state_ix,
-                                               int64_t s_lane, int& ticket) {
+__device__ __forceinline__ void chain_state_in_chained(f32x4 (&hacc)[8], int tid, int seg, int64_t flag_ix,
+                                                       int64_t state_ix, int64_t s_lane, int& ticket) {
   if (seg > 0) {
     if (tid == 0) {
       unsigned* flag = kargs()->queue + 256 + flag_ix;
@@ -253,18 +257,75 @@ __device__ __forceinline__ void chain_state_in(f32x4 (&hacc)[8], int tid, int se
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+}
+
+// The entering state of segment seg in the second of two passes: the first pass
+// left each earlier segment j's state from zero, L_j, and its decay sum lam_j, so
+// S_in(0) = h0 (or zeros) and S_in(j + 1) = 2^lam_j S_in(j) + L_j, the recurrence
+// restated at segment ends (plain loads: the first pass was an earlier kernel).
+__device__ __forceinline__ void chain_state_in_folded(f32x4 (&hacc)[8], int seg, int64_t state_ix, int64_t s_lane) {
+  if (kargs()->h0) {
+    const float* src = kargs()->h0 + state_ix * (P * NS) + s_lane;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int64_t nst = kargs()->nstates;
+  for (int j = 0; j < seg; ++j) {
+    const float d = fast_exp2(kargs()->lam[j * nst + state_ix]);
+    const float* src = kargs()->carry + (j * nst + state_ix) * (P * NS) + s_lane;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const f32x4 v = *(const f32x4*)(src + 16 * nt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hacc[nt][r] = fmaf(d, hacc[nt][r], v[r]);
+    }
+  }
+}
+
+// Work modes of the chunk kernels. kChained: one pass, a segment waits for its
+// predecessor's state (chain_state_in_chained). Two passes for few chains, where
+// the segments of a chain can then run at once: kLocal computes each segment but
+// the last from a zero state, only the state update (no y), and leaves that state
+// and the segment's decay sum; kFolded then runs every segment from its entering
+// state folded from those (chain_state_in_folded), with no waits.
+constexpr int kChained = 0, kLocal = 1, kFolded = 2;
+
+template <int MODE>
+__device__ __forceinline__ void chain_state_in(f32x4 (&hacc)[8], int tid, int seg, int64_t flag_ix, int64_t state_ix,
+                                               int64_t s_lane, int& ticket) {
+  if constexpr (MODE == kLocal) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  } else if constexpr (MODE == kFolded) {
+    chain_state_in_folded(hacc, seg, state_ix, s_lane);
+  } else {
+    chain_state_in_chained(hacc, tid, seg, flag_ix, state_ix, s_lane, ticket);
+  }
   // The loads complete here: otherwise every chunk would wait for them (and
   // for the chunk loads queued behind them) before it first reads the state.
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) asm volatile("" : "+v"(hacc[nt]));
 }
 
-// The leaving state: to the caller after the last segment, else to carry and
-// then the chain's flag. Every thread waits until its stores are complete
-// (visible to the device) before the barrier; thread 0 raises the flag after it.
+// The leaving state. kChained: to the caller after the last segment, else to carry
+// and then the chain's flag (every thread waits until its stores are complete,
+// visible to the device, before the barrier; thread 0 raises the flag after it).
+// kFolded: to the caller after the last segment (the others' went to carry in the
+// first pass). kLocal: to carry[seg], with the decay sum lam (one head per workgroup).
+template <int MODE>
 __device__ __forceinline__ void chain_state_out(const f32x4 (&hacc)[8], int tid, int seg, int64_t flag_ix,
-                                                int64_t state_ix, int64_t s_lane) {
-  if (seg + 1 < kargs()->nseg) {
+                                                int64_t state_ix, int64_t s_lane, float lam = 0.0f) {
+  if constexpr (MODE == kLocal) {
+    const int64_t nst = kargs()->nstates;
+    float* dst = kargs()->carry + (seg * nst + state_ix) * (P * NS) + s_lane;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
+    if (tid == 0) kargs()->lam[seg * nst + state_ix] = lam;
+  } else if (MODE == kChained && seg + 1 < kargs()->nseg) {
     const __amdgpu_buffer_rsrc_t rS = rsrc(kargs()->carry + state_ix * (P * NS), P * NS * 4);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
@@ -273,7 +334,7 @@ __device__ __forceinline__ void chain_state_out(const f32x4 (&hacc)[8], int tid,
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above have completed
     __syncthreads();
     if (tid == 0) __hip_atomic_store(kargs()->queue + 256 + flag_ix, (unsigned)(seg + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
+  } else if (MODE == kChained || seg + 1 == kargs()->nseg) {
     float* dst = kargs()->h_out + state_ix * (P * NS) + s_lane;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) *(f32x4*)(dst + 16 * nt) = hacc[nt];
@@ -300,8 +361,10 @@ struct Prefetch {
 // tile is loaded once, then masked with each head's decays; the two heads' waves
 // share the SIMDs, so one head's MFMA and memory latencies hide behind the other's
 // work.
-template <int HPW>
+template <int HPW, int MODE>
 __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(SsdK k) {
+  static_assert(MODE == kChained || HPW == 1, "two passes: one head per workgroup");
+  constexpr bool Y = MODE != kLocal;  // the pass computes y (kLocal: only the state)
   constexpr int NW = 4 * HPW;      // waves
   constexpr int BCIT = 4 / HPW;    // rows of B (and of C) a thread stages
   constexpr int NT = HPW == 1 ? 3 : 2;  // C B^T tiles a wave masks (some repeated)
@@ -338,7 +401,8 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   // (32-bit: chains < 2^24 and queues <= 8; readfirstlane marks the quotients
   // uniform, so buffer resources built from them stay scalar)
   auto qindex = [&]() { return __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)kargs()->nq)); };
-  auto qcounter = [&]() { return kargs()->queue + 16 * qindex(); };
+  // (kLocal: its own counters, in the words of the chain flags, which two passes do not use)
+  auto qcounter = [&]() { return kargs()->queue + (MODE == kLocal ? 256 : 0) + 16 * qindex(); };
   auto qfirst = [&]() {
     return __builtin_amdgcn_readfirstlane((int)((unsigned)(qindex() * kargs()->nchains) / (unsigned)kargs()->nq));
   };
@@ -346,7 +410,8 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     const unsigned q = (unsigned)qindex(), n = (unsigned)kargs()->nchains, nq = (unsigned)kargs()->nq;
     return __builtin_amdgcn_readfirstlane((int)((q + 1) * n / nq - q * n / nq));
   };
-  auto qitems = [&]() { return kargs()->nseg * qchains(); };
+  // (kLocal: every segment but the last)
+  auto qitems = [&]() { return (MODE == kLocal ? kargs()->nseg - 1 : kargs()->nseg) * qchains(); };
 
   // Work items come from a counter. Each workgroup takes its first item at
   // once and the second after its first chunk is staged (by then every
@@ -466,13 +531,15 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       // states 8 bc_p + e: piece q = bc_p % 4 of the 32 states 32kb.. (kb = bc_p / 4)
       // goes to positions 32kb + 16 (q % 2) + 4 (q / 2) and 8 further on
       const int pk = 32 * (bc_p >> 2) + 16 * (bc_p & 1) + 4 * ((bc_p >> 1) & 1);
-      *(u32x2*)(sCk + row * LDC + pk) = u32x2{pf.c[it][0], pf.c[it][1]};
-      *(u32x2*)(sCk + row * LDC + pk + 8) = u32x2{pf.c[it][2], pf.c[it][3]};
+      if constexpr (Y) {
+        *(u32x2*)(sCk + row * LDC + pk) = u32x2{pf.c[it][0], pf.c[it][1]};
+        *(u32x2*)(sCk + row * LDC + pk + 8) = u32x2{pf.c[it][2], pf.c[it][3]};
+      }
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       *(u32x4*)(sX[hs] + (x_r + 8 * it) * LDX + x_p * 8) = pf.x[it];
-      *(u32x4*)(sZ[hs] + (x_r + 8 * it) * LDX + x_p * 8) = pf.z[it];
+      if constexpr (Y) *(u32x4*)(sZ[hs] + (x_r + 8 * it) * LDX + x_p * 8) = pf.z[it];
     }
     if (wq == kDecayWave) {
       const int nt_valid = max(0, min(Q, L - tt));
@@ -490,11 +557,13 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   f32x4 hacc[8];
   const int64_t s_lane = (int64_t)(16 * wq + li) * NS + 4 * lg;
   // the entering state of the current item and the leaving one (chain_state_in / _out)
+  float lam = 0.0f;  // kLocal: the item's decay sum so far (exp2 domain)
   auto state_in = [&]() {
-    chain_state_in(hacc, tid, seg, (int64_t)b * hpc + hc, (int64_t)b * H + h, s_lane, sTicket[2]);
+    chain_state_in<MODE>(hacc, tid, seg, (int64_t)b * hpc + hc, (int64_t)b * H + h, s_lane, sTicket[2]);
+    lam = 0.0f;
   };
   auto state_out = [&]() {
-    chain_state_out(hacc, tid, seg, (int64_t)b * hpc + hc, (int64_t)b * H + h, s_lane);
+    chain_state_out<MODE>(hacc, tid, seg, (int64_t)b * hpc + hc, (int64_t)b * H + h, s_lane, lam);
   };
 
   // the tiles of M above the diagonal block row stay zero
@@ -504,10 +573,12 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
   tb = b; th = h; tg = g; tt = c * Q;
   Prefetch<HPW> pf;
   load_b(pf);
-  load_c(pf);
-  load_g(pf);
+  if constexpr (Y) {
+    load_c(pf);
+    load_g(pf);
+  }
   load_x(pf);
-  load_z(pf);
+  if constexpr (Y) load_z(pf);
   stage(pf);
   state_in();
   if (tid == 0) sTicket[1] = (int)atomicAdd(qcounter(), 1u);
@@ -535,9 +606,9 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     } else {
       tt = L;
     }
-    store_y();  // the previous chunk's y (sY complete since barrier A)
+    if constexpr (Y) store_y();  // the previous chunk's y (sY complete since barrier A)
     load_b(pf);
-    load_z(pf);
+    if constexpr (Y) load_z(pf);
 
     // x^T fragments (A operand of Y^T += X^T M^T; k = j = 32kb + 8lg + kperm(e)) by
     // two transposing loads each, and the epilogue's x values (8 bytes of row 16it + li)
@@ -550,16 +621,18 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       xa[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
     u32x2 xe[4], zkeep[4];
+    if constexpr (Y) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      xe[it] = lds64(sX[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
-      zkeep[it] = lds64(sZ[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
+      for (int it = 0; it < 4; ++it) {
+        xe[it] = lds64(sX[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
+        zkeep[it] = lds64(sZ[hs] + (16 * it + li) * LDX + 16 * wq + 4 * lg);
+      }
     }
 
     // ---- G tiles -> M (lower triangle), each masked with every head's decays:
     // wave w takes tiles w, w + NW, w + 2 NW. A wave with fewer tiles masks its
     // first tile again, writing the same values again (no branch in the phase).
-    {
+    if constexpr (Y) {
       f32x4 acc[NT];
       int Jt[NT], It[NT];
 #pragma unroll
@@ -601,8 +674,10 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       }
     }
 
-    load_c(pf);
-    load_g(pf);
+    if constexpr (Y) {
+      load_c(pf);
+      load_g(pf);
+    }
     // ---- Y^T = S_in C^T, columns scaled by exp(cs_i). A operand: the state,
     // k = n in {32kb + 4lg + r} U {32kb + 16 + 4lg + r} (the accumulator layout);
     // B operand: C[i][n] for the same n, 16 bytes of row i of sCk.
@@ -619,11 +694,12 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       wj[kb][1] = *(const f32x4*)(sW[hs] + 32 * kb + 8 * lg + 4);
     }
     const float dec_last = sE[hs][Q - 1];
+    if constexpr (!Y) lam += sCS[hs][Q - 1];
     f32x4 yacc[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) yacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < (Y ? 4 : 0); ++kb) {
       u32x4 sv;
       sv[0] = pack2(hacc[2 * kb][0], hacc[2 * kb][1]);
       sv[1] = pack2(hacc[2 * kb][2], hacc[2 * kb][3]);
@@ -672,7 +748,7 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
 
     // ---- Y^T += X^T M^T (M[i][j] = 0 for j > i: skip the upper blocks)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < (Y ? 4 : 0); ++it) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (kb == 1 && it < 2) continue;
@@ -681,7 +757,7 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
       }
     }
     // ---- epilogue: lane holds y[i = 16it + li][16wq + 4lg + r]; y = (Y + D x) silu(z)
-    {
+    if constexpr (Y) {
       const __amdgpu_buffer_rsrc_t rY = rsrc((const char*)(k.y + (uint64_t)b * xz_bat + h * P) + (uint32_t)t0 * xz_row,
                                              (uint32_t)(L - t0) * xz_row - h * P * 2);
 #pragma unroll
@@ -718,7 +794,7 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     __syncthreads();  // ---- barrier A of the next chunk
     if (finished) break;
   }
-  store_y();  // the last chunk's y
+  if constexpr (Y) store_y();  // the last chunk's y
 }
 
 // G = C B^T of every chunk of 64 tokens and every group, once for all the heads
@@ -820,7 +896,9 @@ struct PrefetchF {
   float dt;
 };
 
+template <int MODE>
 __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
+  constexpr bool Y = MODE != kLocal;  // the pass computes y (kLocal: only the state)
   constexpr int NW = 4, NT = 3;
   __shared__ __attribute__((aligned(16))) float sBt[NS * LBT];
   __shared__ __attribute__((aligned(16))) float sCf[Q * LCF];
@@ -838,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
 
   // the work queues, as in ssd_chunk_kernel
   auto qindex = [&]() { return __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)kargs_f()->nq)); };
-  auto qcounter = [&]() { return kargs_f()->queue + 16 * qindex(); };
+  auto qcounter = [&]() { return kargs_f()->queue + (MODE == kLocal ? 256 : 0) + 16 * qindex(); };
   auto qfirst = [&]() {
     return __builtin_amdgcn_readfirstlane((int)((unsigned)(qindex() * kargs_f()->nchains) / (unsigned)kargs_f()->nq));
   };
@@ -846,7 +924,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     const unsigned q = (unsigned)qindex(), n = (unsigned)kargs_f()->nchains, nq = (unsigned)kargs_f()->nq;
     return __builtin_amdgcn_readfirstlane((int)((q + 1) * n / nq - q * n / nq));
   };
-  auto qitems = [&]() { return kargs_f()->nseg * qchains(); };
+  auto qitems = [&]() { return (MODE == kLocal ? kargs_f()->nseg - 1 : kargs_f()->nseg) * qchains(); };
 
   if (tid == 0) sTicket[0] = (int)atomicAdd(qcounter(), 1u);
   __syncthreads();
@@ -938,12 +1016,14 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
       for (int e = 0; e < 4; ++e)
         *(f32x4*)(sBt + bt_at(4 * nb + e, 32 * it + 4 * jq)) =
             f32x4{pf.b[it][0][e], pf.b[it][1][e], pf.b[it][2][e], pf.b[it][3][e]};
+    if constexpr (Y) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it) *(f32x4*)(sCf + (8 * it + jq) * LCF + 4 * nb) = pf.c[it];
+      for (int it = 0; it < 8; ++it) *(f32x4*)(sCf + (8 * it + jq) * LCF + 4 * nb) = pf.c[it];
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       *(f32x4*)(sXf + (16 * it + xr) * LXF + 4 * xp) = pf.x[it];
-      *(f32x4*)(sZf + (16 * it + xr) * LXF + 4 * xp) = pf.z[it];
+      if constexpr (Y) *(f32x4*)(sZf + (16 * it + xr) * LXF + 4 * xp) = pf.z[it];
     }
     if (wq == kDecayWave) {
       const int nt_valid = max(0, min(Q, L - tt));
@@ -961,21 +1041,25 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
   const int64_t s_lane = (int64_t)(16 * wq + li) * NS + 4 * lg;
   // the entering and leaving state, as in ssd_chunk_kernel (chain_state_in / _out: the
   // same flags, give-up word and carry; a chain is one head)
+  float lam = 0.0f;  // kLocal: the item's decay sum so far (exp2 domain)
   auto state_in = [&]() {
-    chain_state_in(hacc, tid, seg, (int64_t)b * H + h, (int64_t)b * H + h, s_lane, sTicket[2]);
+    chain_state_in<MODE>(hacc, tid, seg, (int64_t)b * H + h, (int64_t)b * H + h, s_lane, sTicket[2]);
+    lam = 0.0f;
   };
   auto state_out = [&]() {
-    chain_state_out(hacc, tid, seg, (int64_t)b * H + h, (int64_t)b * H + h, s_lane);
+    chain_state_out<MODE>(hacc, tid, seg, (int64_t)b * H + h, (int64_t)b * H + h, s_lane, lam);
   };
 
   set_item(cur);
   tb = b; th = h; tg = g; tt = c * Q;
   PrefetchF pf;
   load_b(pf);
-  load_c(pf);
-  load_g(pf);
+  if constexpr (Y) {
+    load_c(pf);
+    load_g(pf);
+  }
   load_x(pf);
-  load_z(pf);
+  if constexpr (Y) load_z(pf);
   stage(pf);
   state_in();
   if (tid == 0) sTicket[1] = (int)atomicAdd(qcounter(), 1u);
@@ -1002,9 +1086,9 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     } else {
       tt = L;
     }
-    store_y();
+    if constexpr (Y) store_y();
     load_b(pf);
-    load_z(pf);
+    if constexpr (Y) load_z(pf);
 
     // x[j = 16 jb + 4 lg + kk][p = 16 wq + li]: operand of the state update and of X^T M^T
     float xv[4][4];
@@ -1016,7 +1100,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     // ---- G tiles -> M[i][j] = G[i][j] exp(cs_i - cs_j) dt_j (j <= i), fp32, row-major;
     // wave w takes tiles w, w + 4, w + 8 (a wave with two masks its first again)
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
+    for (int u = 0; u < (Y ? NT : 0); ++u) {
       const int ti = w + NW * u < kTiles ? w + NW * u : w;
       const int It = tile_i(ti), Jt = tile_j(ti);
       const int i = 16 * It + li;
@@ -1033,8 +1117,10 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
       *(f32x4*)(sMf + i * LMF + 16 * Jt + 4 * lg) = m;
     }
 
-    load_c(pf);
-    load_g(pf);
+    if constexpr (Y) {
+      load_c(pf);
+      load_g(pf);
+    }
     float ei[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) ei[it] = sE[16 * it + li];
@@ -1042,6 +1128,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) wv[jb] = *(const f32x4*)(sW + 16 * jb + 4 * lg);
     const float dec_last = sE[Q - 1];
+    if constexpr (!Y) lam += sCS[Q - 1];
 
     // ---- Y^T = S_in C^T, columns scaled by exp(cs_i); per state tile the four rows of
     // C are read first, then the 16 MFMAs go to the four output tiles in turn
@@ -1049,7 +1136,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) yacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < (Y ? 8 : 0); ++nt) {
       f32x4 cv[4];
 #pragma unroll
       for (int it = 0; it < 4; ++it) cv[it] = *(const f32x4*)(sCf + (16 * it + li) * LCF + 16 * nt + 4 * lg);
@@ -1099,7 +1186,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     // reads. (Staging before X^T M^T, beside its MFMAs, measured 2.5% slower.)
     f32x4 gv[4], dxg[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < (Y ? 4 : 0); ++it) {
       const f32x4 xe = *(const f32x4*)(sXf + (16 * it + li) * LXF + 16 * wq + 4 * lg);
       const f32x4 ze = *(const f32x4*)(sZf + (16 * it + li) * LXF + 16 * wq + 4 * lg);
 #pragma unroll
@@ -1110,7 +1197,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     }
     // ---- Y^T += X^T M^T over the blocks jb <= it
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < (Y ? 4 : 0); ++it) {
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
         if (jb > it) continue;
@@ -1120,7 +1207,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
       }
     }
     // ---- epilogue: lane holds y[i = 16 it + li][16 wq + 4 lg + r]
-    {
+    if constexpr (Y) {
       const __amdgpu_buffer_rsrc_t rY = rsrc((const char*)(k.y + (uint64_t)b * xz_bat + h * P) + (uint32_t)t0 * xz_row,
                                              (uint32_t)(L - t0) * xz_row - h * P * 4);
 #pragma unroll
@@ -1151,7 +1238,7 @@ __global__ __launch_bounds__(256, 1) void ssd_chunk_f32_kernel(SsdKF k) {
     __syncthreads();  // ---- barrier A of the next chunk
     if (finished) break;
   }
-  store_y();
+  if constexpr (Y) store_y();
 }
 
 // ssd_cb_kernel for fp32 B and C on fp32 MFMA, in the same tile layout:
@@ -1232,11 +1319,24 @@ SSDArgs by_64_columns(const SSDArgs& a) {
 // time. Cutting every chain into segments that any workgroup may take evens
 // the load: the cost model counts rounds of items over one workgroup per unit,
 // plus one chunk of overhead per item.
+//
+// Few chains (fewer than units, say one batch row of 80 heads) leave units idle in
+// one pass, since a chain's segments wait for each other. Then two passes can win:
+// the first computes every segment but the last from a zero state, only its state
+// update (the kLocal kernel, about kLocalCost of a chunk's time per chunk), and
+// the second runs all segments at once, each from its entering state folded from
+// the first pass's (kFolded). The model counts the rounds of each pass.
 struct SsdPlan {
   int hpw, nchains, seg_chunks, nseg, nq, grid;
-  size_t queue_bytes, carry_bytes, cb_bytes, ws_bytes;
+  bool two_pass;   // kLocal and kFolded passes (else one kChained pass)
+  int grid_local;  // workgroups of the kLocal pass
+  size_t queue_bytes, carry_bytes, lam_bytes, cb_bytes, ws_bytes;
+  size_t cb_off, pad_off;                // workspace offsets of the C B^T tiles and the padded copies
   size_t pad_bc_bytes, pad_state_bytes;  // state_dim < NS: each padded B, C and state copy
 };
+
+// per-chunk time of the kLocal pass relative to a full chunk, in percent (bf16, fp32)
+constexpr int64_t kLocalCostBf16 = 35, kLocalCostF32 = 45;
 
 // (a: the problem in heads of 64 columns)
 SsdPlan ssd_plan(const SSDArgs& a) {
@@ -1258,7 +1358,7 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   // Two workgroups per unit (the occupancy the one-head kernel is built for) with
   // many chains; the two-head kernel and the fp32 kernel fill a unit's LDS with one.
   int64_t grid = (!f32 && p.hpw == 1 && nchains >= 2 * (int64_t)ncu) ? 2 * ncu : ncu;
-  int64_t best_seg = nchunks, best_ns = 1;
+  int64_t best_seg = nchunks, best_ns = 1, best_cost = 0;
   auto queues = [&](int64_t g) { return std::max<int64_t>(1, std::min<int64_t>({8, nchains, g})); };
   {
     // rounds of items in the fullest queue over its workgroups (with many more chains
@@ -1278,6 +1378,38 @@ SsdPlan ssd_plan(const SSDArgs& a) {
         best_ns = ns;
       }
     }
+    best_cost = best;
+  }
+  // Two passes (one head per workgroup, one workgroup per unit): rounds of the first
+  // pass's items (every segment but the last) at kLocalCost per chunk, then of the
+  // second's; in hundredths of a chunk.
+  bool two_pass = false;
+  int64_t seg2 = nchunks, ns2 = 1;
+  const int tp = knob(kKnobSsdTwoPass);  // 1: one pass; 2: two passes
+  if (p.hpw == 1 && tp != 1) {
+    const int64_t g2 = ncu, nq = queues(g2), qch = (nchains + nq - 1) / nq, qwg = std::max<int64_t>(g2 / nq, 1);
+    const int64_t lc = f32 ? kLocalCostF32 : kLocalCostBf16;
+    auto cost2 = [&](int64_t sc, int64_t ns) {
+      const int64_t r1 = ((ns - 1) * qch + qwg - 1) / qwg, r2 = (ns * qch + qwg - 1) / qwg;
+      return r1 * (lc * sc + 100) + r2 * (100 * sc + 100 + 10 * (ns - 1));
+    };
+    int64_t best2 = cost2(nchunks, 1);
+    for (int64_t s = 2; s <= std::min<int64_t>(nchunks, 64) && s * nchains < (int64_t(1) << 30); ++s) {
+      const int64_t sc = (nchunks + s - 1) / s, ns = (nchunks + sc - 1) / sc;
+      const int64_t cst = cost2(sc, ns);
+      if (cst < best2) {
+        best2 = cst;
+        seg2 = sc;
+        ns2 = ns;
+      }
+    }
+    // (the one-pass cost, best_cost, in whole chunks; two passes must win by 3%)
+    two_pass = tp == 2 || (ns2 > 1 && best2 * 100 < best_cost * 100 * 97);
+  }
+  if (two_pass) {
+    best_seg = seg2;
+    best_ns = ns2;
+    grid = ncu;
   }
   // tuning overrides: chunks per segment, workgroups
   if (const int64_t sc = knob(kKnobSsdSegmentChunks); sc > 0) {
@@ -1286,21 +1418,29 @@ SsdPlan ssd_plan(const SSDArgs& a) {
     if (best_ns * nchains >= (int64_t(1) << 30)) best_seg = nchunks, best_ns = 1;
   }
   if (const int64_t wg = knob(kKnobSsdWorkgroups); wg > 0) grid = std::min<int64_t>(wg, 1 << 20);
+  p.two_pass = two_pass;
   p.seg_chunks = (int)best_seg;
   p.nseg = (int)best_ns;
   p.nq = (int)queues(grid);
   // no more workgroups than the fullest queue has items, per queue
-  const int64_t qitems = best_ns * ((nchains + p.nq - 1) / p.nq);
-  p.grid = (int)std::min<int64_t>(grid, (int64_t)p.nq * qitems);
-  p.queue_bytes = ((size_t)(256 + p.nchains) * 4 + 255) / 256 * 256;
-  p.carry_bytes = p.nseg > 1 ? (size_t)(a.batch * a.H) * P * NS * 4 : 0;
+  const int64_t qch = (nchains + p.nq - 1) / p.nq;
+  p.grid = (int)std::min<int64_t>(grid, (int64_t)p.nq * best_ns * qch);
+  p.grid_local = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)p.nq * (best_ns - 1) * qch));
+  // queue words: 8 counters (16 apart), the give-up word at 128, then a flag per
+  // chain from 256 (one pass) or the first pass's 8 counters there (two passes)
+  p.queue_bytes = ((size_t)(256 + std::max(p.nchains, 128)) * 4 + 255) / 256 * 256;
+  const size_t state_bytes = (size_t)(a.batch * a.H) * P * NS * 4;
+  p.carry_bytes = p.nseg > 1 ? (two_pass ? (size_t)(p.nseg - 1) : 1) * state_bytes : 0;
+  p.lam_bytes = two_pass && p.nseg > 1 ? ((size_t)(p.nseg - 1) * (size_t)(a.batch * a.H) * 4 + 255) / 256 * 256 : 0;
   p.cb_bytes = (size_t)a.batch * (size_t)((a.L + Q - 1) / Q) * (size_t)a.G * kTiles * kTileFloats * 4;
+  p.cb_off = p.queue_bytes + p.carry_bytes + p.lam_bytes;
+  p.pad_off = p.cb_off + p.cb_bytes;
   // state_dim below NS: B and C padded to NS states, and the entering and leaving
   // states as [batch, H, P, NS] (after the C B^T tiles, 256-byte aligned)
   const size_t es = f32 ? 4 : 2;
   p.pad_bc_bytes = a.N < NS ? ((size_t)(a.batch * a.L * a.G) * NS * es + 255) / 256 * 256 : 0;
-  p.pad_state_bytes = a.N < NS ? (size_t)(a.batch * a.H) * P * NS * 4 : 0;
-  p.ws_bytes = p.queue_bytes + p.carry_bytes + p.cb_bytes + 2 * p.pad_bc_bytes + 2 * p.pad_state_bytes;
+  p.pad_state_bytes = a.N < NS ? state_bytes : 0;
+  p.ws_bytes = p.pad_off + 2 * p.pad_bc_bytes + 2 * p.pad_state_bytes;
   return p;
 }
 
@@ -1323,6 +1463,20 @@ bool ssd_chunk_supported(const SSDArgs& a) {
 
 size_t ssd_chunk_ws(const SSDArgs& a) { return a.batch == 0 ? 0 : ssd_plan(by_64_columns(a)).ws_bytes; }
 
+// The kernel arguments both chunk kernels share: workspace layout, sizes, plan.
+template <typename K>
+void fill_common(K& k, const SSDArgs& a, const SsdPlan& p, int hshift, void* ws) {
+  k.queue = (unsigned*)ws;
+  k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
+  k.lam = p.lam_bytes ? (float*)((char*)ws + p.queue_bytes + p.carry_bytes) : nullptr;
+  k.cb = (float*)((char*)ws + p.cb_off);
+  k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
+  k.nchunks = (int)((a.L + Q - 1) / Q);
+  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
+  k.hshift = hshift;
+  k.nstates = (int)(a.batch * a.H);
+}
+
 // fp32 activations: ssd_cb_f32_kernel and ssd_chunk_f32_kernel on the same plan
 // (a: the problem in heads of 64 columns; hshift: log2 of the caller's head_dim / 64)
 hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s) {
@@ -1330,20 +1484,18 @@ hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, int hshift, 
   k.x = (const float*)a.x; k.dt = (const float*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const float*)a.B; k.C = (const float*)a.C; k.D = a.D; k.z = (const float*)a.z;
   k.h0 = a.h0; k.y = (float*)a.y; k.h_out = a.h_out;
-  k.queue = (unsigned*)ws;
-  k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
-  float* cb = (float*)((char*)ws + p.queue_bytes + p.carry_bytes);
-  k.cb = cb;
-  k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
-  k.nchunks = (int)((a.L + Q - 1) / Q);
-  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
-  k.hshift = hshift;
-  const int nwords = 256 + p.nchains;
+  fill_common(k, a, p, hshift, ws);
   const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
   hipLaunchKernelGGL(ssd_cb_f32_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(nblk, 1 << 20))),
-                     dim3(640), 0, s, (const float*)a.B, (const float*)a.C, cb, (int)a.L, (int)a.G, k.nchunks, nblk,
-                     k.queue, nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
-  hipLaunchKernelGGL(ssd_chunk_f32_kernel, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+                     dim3(640), 0, s, (const float*)a.B, (const float*)a.C, (float*)k.cb, (int)a.L, (int)a.G, k.nchunks, nblk,
+                     k.queue, (int)(p.queue_bytes / 4), knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
+  if (!p.two_pass) {
+    hipLaunchKernelGGL(ssd_chunk_f32_kernel<kChained>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+  } else {
+    if (p.nseg > 1)
+      hipLaunchKernelGGL(ssd_chunk_f32_kernel<kLocal>, dim3((unsigned)p.grid_local), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(ssd_chunk_f32_kernel<kFolded>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+  }
   return hipGetLastError();
 }
 
@@ -1353,24 +1505,21 @@ static hipError_t launch_ssd_chunk_bf16(const SSDArgs& a, const SsdPlan& p, int 
   k.x = (const uint16_t*)a.x; k.dt = (const uint16_t*)a.dt; k.dt_bias = a.dt_bias; k.A_log = a.A_log;
   k.B = (const uint16_t*)a.B; k.C = (const uint16_t*)a.C; k.D = a.D; k.z = (const uint16_t*)a.z;
   k.h0 = a.h0; k.y = (uint16_t*)a.y; k.h_out = a.h_out;
-  k.queue = (unsigned*)ws;
-  k.carry = p.nseg > 1 ? (float*)((char*)ws + p.queue_bytes) : nullptr;
-  float* cb = (float*)((char*)ws + p.queue_bytes + p.carry_bytes);
-  k.cb = cb;
-  k.L = a.L; k.H = a.H; k.G = a.G; k.heads_per_group = (int)(a.H / a.G);
-  k.nchunks = (int)((a.L + Q - 1) / Q);
-  k.nchains = p.nchains; k.seg_chunks = p.seg_chunks; k.nseg = p.nseg; k.nq = p.nq;
-  k.hshift = hshift;
-  const int nwords = 256 + p.nchains;
+  fill_common(k, a, p, hshift, ws);
   const int64_t nblk = a.batch * (int64_t)k.nchunks * a.G;
   // (at least one workgroup: it also clears the queues)
   hipLaunchKernelGGL(ssd_cb_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(nblk, 1 << 20))), dim3(640),
-                     0, s, (const uint16_t*)a.B, (const uint16_t*)a.C, cb, (int)a.L, (int)a.G, k.nchunks, nblk, k.queue,
-                     nwords, knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
-  if (p.hpw == 2)
-    hipLaunchKernelGGL(ssd_chunk_kernel<2>, dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);
-  else
-    hipLaunchKernelGGL(ssd_chunk_kernel<1>, dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+                     0, s, (const uint16_t*)a.B, (const uint16_t*)a.C, (float*)k.cb, (int)a.L, (int)a.G, k.nchunks, nblk,
+                     k.queue, (int)(p.queue_bytes / 4), knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
+  if (p.two_pass) {
+    if (p.nseg > 1)
+      hipLaunchKernelGGL((ssd_chunk_kernel<1, kLocal>), dim3((unsigned)p.grid_local), dim3(256), kCkBytes, s, k);
+    hipLaunchKernelGGL((ssd_chunk_kernel<1, kFolded>), dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+  } else if (p.hpw == 2) {
+    hipLaunchKernelGGL((ssd_chunk_kernel<2, kChained>), dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);
+  } else {
+    hipLaunchKernelGGL((ssd_chunk_kernel<1, kChained>), dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+  }
   return hipGetLastError();
 }
 
@@ -1389,7 +1538,7 @@ hipError_t launch_ssd_chunk(const SSDArgs& a_caller, void* ws, hipStream_t s) {
 // workspace (after the C B^T tiles), the chunk kernels run at NS on those copies,
 // and the leaving state's first N entries per row go to the caller.
 static hipError_t launch_ssd_chunk_padded(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s) {
-  char* base = (char*)ws + p.queue_bytes + p.carry_bytes + p.cb_bytes;
+  char* base = (char*)ws + p.pad_off;
   void* pB = base;
   void* pC = base + p.pad_bc_bytes;
   float* pH0 = (float*)(base + 2 * p.pad_bc_bytes);

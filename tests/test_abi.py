@@ -255,7 +255,9 @@ def test_tuning_knobs_are_validated_and_restored():
     assert bd.set_tuning(bd.TUNE_M1_LANES, 0) == 4   # the previous value comes back
     assert bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 1) == 0
     assert bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0) == 1
-    assert L.sscan_set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP + 1, 1) == -1   # one past the last knob
+    assert bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 2) == 0
+    assert bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 0) == 2
+    assert L.sscan_set_tuning(bd.TUNE_SSD_TWO_PASS + 1, 1) == -1   # one past the last knob
     with pytest.raises(ValueError):
         bd.set_tuning(42, 1)
 
@@ -305,6 +307,26 @@ def test_launch_plans_are_stable_and_follow_the_knobs():
     assert L.sscan_ssd_workspace_size(ctypes.byref(sdesc(seqlen=0))) == 0
     assert L.sscan_ssd_workspace_size(ctypes.byref(sdesc(seqlen=0, act=0))) == 0
     assert L.sscan_ssd_workspace_size(ctypes.byref(f)) == f0
+    # 16 heads of one batch row (16 chains for 256 units) take two passes: the first
+    # pass's states and decay sums make the workspace larger than one pass's
+    few = sdesc(batch=1, seqlen=16384, nheads=16)
+    w_plan = L.sscan_ssd_workspace_size(ctypes.byref(few))
+    for v, want in ((2, w_plan), (0, w_plan)):
+        bd.set_tuning(bd.TUNE_SSD_TWO_PASS, v)
+        assert L.sscan_ssd_workspace_size(ctypes.byref(few)) == want
+    bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 1)
+    try:
+        assert L.sscan_ssd_workspace_size(ctypes.byref(few)) < w_plan
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 0)
+    # four batch rows (320 chains) keep one pass
+    many = sdesc(batch=4, seqlen=8192, nheads=80)
+    w4 = L.sscan_ssd_workspace_size(ctypes.byref(many))
+    bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 1)
+    try:
+        assert L.sscan_ssd_workspace_size(ctypes.byref(many)) == w4
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 0)
     # a head of 128 or 256 columns is planned as 2 or 4 heads of 64 columns
     for act in (1, 0):
         for P, m in ((128, 2), (256, 4)):

@@ -259,6 +259,7 @@ SEGMENT_CASES = [
 def test_ssd_forced_segments(case, tuning):
     sc, wg, b, L, H, G, gate, h0 = case
     say("ssd forced segments", case)
+    tuning(bd.TUNE_SSD_TWO_PASS, 1)  # one pass: the hand-offs between segments
     tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, sc)
     tuning(bd.TUNE_SSD_WORKGROUPS, wg)
     inp = gen.make_ssd(b, L, H, 64, 128, G, act="bf16", seed=L + 7 * sc + wg, gate=gate, h0=h0)
@@ -284,6 +285,7 @@ def test_ssd_f32_forced_segments(case, tuning):
     grids, against the oracle and bit-identical to the library's own cut."""
     sc, wg, b, L, H, G, gate, h0 = case
     say("ssd f32 forced segments", case)
+    tuning(bd.TUNE_SSD_TWO_PASS, 1)
     tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, sc)
     tuning(bd.TUNE_SSD_WORKGROUPS, wg)
     inp = gen.make_ssd(b, L, H, 64, 128, G, act="f32", seed=L + 7 * sc + wg, gate=gate, h0=h0)
@@ -368,6 +370,44 @@ def test_ssd_narrow_state_equals_zero_padded(case, tuning):
     check_all(inp, got, oracle.run_inputs(inp), "ssd")
 
 
+TWO_PASS_CASES = [
+    # chunks per segment (0: the plan's), workgroups (0: the plan's), batch, seqlen, H, P, N, G, act, h0
+    (1, 0, 1, 300, 2, 64, 128, 1, "bf16", True),
+    (3, 5, 2, 1000, 4, 64, 128, 2, "bf16", False),
+    (0, 0, 1, 4000, 2, 64, 128, 1, "bf16", True),
+    (2, 0, 1, 700, 2, 128, 128, 1, "bf16", True),
+    (2, 3, 1, 600, 3, 64, 64, 1, "bf16", True),
+    (1, 0, 2, 257, 2, 64, 128, 1, "f32", True),
+    (4, 7, 1, 1500, 4, 64, 128, 2, "f32", False),
+    (0, 0, 1, 3000, 2, 128, 128, 1, "f32", True),
+    (3, 0, 1, 900, 2, 64, 96, 1, "f32", True),
+]
+
+
+@pytest.mark.parametrize("case", TWO_PASS_CASES, ids=lambda c: "seg%d_wg%d_b%d_L%d_H%d_P%d_N%d_G%d_%s_h%d" % c)
+def test_ssd_two_pass(case, tuning):
+    """The chunk path in two passes: every segment but the last scanned from a zero state
+    (its state and decay sum kept), then every segment from its entering state folded
+    from those. Against the oracle; fp32 also against the one-pass form at the fp32
+    bound (the fold rounds differently, so the two are close, not identical)."""
+    sc, wg, b, L, H, P, N, G, act, h0 = case
+    say("ssd two passes", case)
+    inp = gen.make_ssd(b, L, H, P, N, G, act=act, seed=L + H + P + N, gate=True, h0=h0)
+    assert ssd_chunk_path(inp, False)
+    tuning(bd.TUNE_SSD_TWO_PASS, 2)
+    if sc:
+        tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, sc)
+    if wg:
+        tuning(bd.TUNE_SSD_WORKGROUPS, wg)
+    two = run_ssd(inp)
+    check_all(inp, two, oracle.run_inputs(inp), "ssd")
+    bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 1)
+    one = run_ssd(inp)
+    if act == "f32":
+        check(two[0], one[0], "f32", "y (two passes vs one)")
+        check(two[1], one[1], "f32", "state (two passes vs one)")
+
+
 def test_ssd_f32_chunk_kernel_agrees_with_token_loop():
     """fp32 activations: the fp32 MFMA chunk kernel and the token loop restate the same
     recurrence in fp32, so both meet the oracle and each other at the fp32 bound."""
@@ -388,6 +428,7 @@ def test_ssd_handoff_give_up_poisons_dependent_outputs(tuning, act):
     behind: the first segment of every head is exact, everything after it is NaN, and the
     word reads back nonzero. No wait blocks and no kernel faults. Both chunk kernels."""
     inp = gen.make_ssd(2, 700, 4, 64, 128, act=act, seed=83, gate=True, h0=True)
+    tuning(bd.TUNE_SSD_TWO_PASS, 1)            # one pass: segments hand their states on in turn
     tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, 2)      # segments of 128 tokens
     good_y, good_h, _ = run_ssd(inp)
     tuning(bd.TUNE_SSD_GIVE_UP, 1)
@@ -703,6 +744,7 @@ def test_ssd_two_heads_per_workgroup_equals_one(case, tuning):
     results are bit-identical; both against the oracle."""
     b, L, H, G, gate, h0, seg = case
     say("ssd heads per workgroup", case)
+    tuning(bd.TUNE_SSD_TWO_PASS, 1)  # (two heads per workgroup run in one pass only)
     if seg:
         tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, seg)
     inp = gen.make_ssd(b, L, H, 64, 128, G, act="bf16", seed=L + H + G, gate=gate, h0=h0)
