@@ -206,7 +206,7 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
   return x;
 }
 
-// The entering state of the current item: the caller's (or zeros) for a first
+// One pass: the entering state of the current item: the caller's (or zeros) for a first
 // segment, else the one the previous segment left in carry, once its chain's
 // flag says so. The producer of that segment holds an item dequeued earlier
 // than this one, so it is running and never waits on this workgroup: the wait
@@ -259,29 +259,51 @@ __device__ __forceinline__ void chain_state_in_chained(f32x4 (&hacc)[8], int tid
   }
 }
 
-// The entering state of segment seg in the second of two passes: the first pass
-// left each earlier segment j's state from zero, L_j, and its decay sum lam_j, so
-// S_in(0) = h0 (or zeros) and S_in(j + 1) = 2^lam_j S_in(j) + L_j, the recurrence
-// restated at segment ends (plain loads: the first pass was an earlier kernel).
+// The entering state of segment seg in the second of two passes: h0 (or zeros) for
+// the first segment, else carry[seg - 1], where ssd_fold_states_kernel left S_in(seg)
+// (plain loads: it was an earlier kernel).
 __device__ __forceinline__ void chain_state_in_folded(f32x4 (&hacc)[8], int seg, int64_t state_ix, int64_t s_lane) {
-  if (kargs()->h0) {
-    const float* src = kargs()->h0 + state_ix * (P * NS) + s_lane;
+  const float* src = seg > 0 ? kargs()->carry + ((int64_t)(seg - 1) * kargs()->nstates + state_ix) * (P * NS)
+                             : kargs()->h0 ? kargs()->h0 + state_ix * (P * NS) : nullptr;
+  if (src) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + 16 * nt);
+    for (int nt = 0; nt < 8; ++nt) hacc[nt] = *(const f32x4*)(src + s_lane + 16 * nt);
   } else {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) hacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int64_t nst = kargs()->nstates;
-  for (int j = 0; j < seg; ++j) {
-    const float d = fast_exp2(kargs()->lam[j * nst + state_ix]);
-    const float* src = kargs()->carry + (j * nst + state_ix) * (P * NS) + s_lane;
+}
+
+// Between the two passes: the first left each segment j's state from zero, L_j, in
+// carry[j] and its decay sum lam_j (exp2 domain). S_in(0) = h0 (or zeros) and
+// S_in(j + 1) = 2^lam_j S_in(j) + L_j, the recurrence restated at segment ends; each
+// carry[j] is replaced by S_in(j + 1). One thread per 4 entries of a state, a step per
+// segment; four segments' loads are issued before their updates.
+__global__ __launch_bounds__(256) void ssd_fold_states_kernel(float* __restrict__ carry, const float* __restrict__ lam,
+                                                              const float* __restrict__ h0, int nstates, int nfold) {
+  constexpr int64_t per = P * NS / 4;  // threads per state
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nstates * per) return;
+  const int64_t st = i / per, e = (i % per) * 4;
+  const int64_t stride = (int64_t)nstates * (P * NS);  // from segment j to j + 1
+  float* base = carry + st * (P * NS) + e;
+  f32x4 s = h0 ? *(const f32x4*)(h0 + st * (P * NS) + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nfold; j += 4) {
+    f32x4 v[4];
+    float d[4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const f32x4 v = *(const f32x4*)(src + 16 * nt);
+    for (int u = 0; u < 4; ++u)
+      if (j + u < nfold) {
+        v[u] = *(const f32x4*)(base + (j + u) * stride);
+        d[u] = fast_exp2(lam[(int64_t)(j + u) * nstates + st]);
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hacc[nt][r] = fmaf(d, hacc[nt][r], v[r]);
-    }
+    for (int u = 0; u < 4; ++u)
+      if (j + u < nfold) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = fmaf(d[u], s[r], v[u][r]);
+        *(f32x4*)(base + (j + u) * stride) = s;
+      }
   }
 }
 
@@ -289,8 +311,9 @@ __device__ __forceinline__ void chain_state_in_folded(f32x4 (&hacc)[8], int seg,
 // predecessor's state (chain_state_in_chained). Two passes for few chains, where
 // the segments of a chain can then run at once: kLocal computes each segment but
 // the last from a zero state, only the state update (no y), and leaves that state
-// and the segment's decay sum; kFolded then runs every segment from its entering
-// state folded from those (chain_state_in_folded), with no waits.
+// and the segment's decay sum; ssd_fold_states_kernel turns those into the segments'
+// entering states; kFolded then runs every segment from its entering state
+// (chain_state_in_folded), with no waits.
 constexpr int kChained = 0, kLocal = 1, kFolded = 2;
 
 template <int MODE>
@@ -1381,27 +1404,39 @@ SsdPlan ssd_plan(const SSDArgs& a) {
     }
     best_cost = best;
   }
-  // Two passes (one head per workgroup, one workgroup per unit): rounds of the first
-  // pass's items (every segment but the last) at kLocalCost per chunk, then of the
-  // second's; in hundredths of a chunk.
+  // Two passes (one head per workgroup): rounds of the first pass's items (every
+  // segment but the last) at kLocalCost per chunk, then of the second's; in hundredths
+  // of a chunk. bf16 may also run two workgroups per unit (the kernel is built for
+  // that occupancy): a pass whose items fit one per unit costs one round as before;
+  // otherwise each round of up to two items per unit costs 1.5 rounds (two
+  // workgroups sharing a unit each run at about two thirds of the speed: measured
+  // 1.49-1.55 at one and two batch rows of the Mamba-2 2.7B layer).
   bool two_pass = false;
-  int64_t seg2 = nchunks, ns2 = 1;
+  int64_t seg2 = nchunks, ns2 = 1, grid2 = ncu;
   const int tp = knob(kKnobSsdTwoPass);  // 1: one pass; 2: two passes
   if (p.hpw == 1 && tp != 1) {
-    const int64_t g2 = ncu, nq = queues(g2), qch = (nchains + nq - 1) / nq, qwg = std::max<int64_t>(g2 / nq, 1);
     const int64_t lc = f32 ? kLocalCostF32 : kLocalCostBf16;
-    auto cost2 = [&](int64_t sc, int64_t ns) {
-      const int64_t r1 = ((ns - 1) * qch + qwg - 1) / qwg, r2 = (ns * qch + qwg - 1) / qwg;
-      return r1 * (lc * sc + 100) + r2 * (100 * sc + 100 + 10 * (ns - 1));
-    };
-    int64_t best2 = cost2(nchunks, 1);
-    for (int64_t s = 2; s <= std::min<int64_t>(nchunks, 64) && s * nchains < (int64_t(1) << 30); ++s) {
-      const int64_t sc = (nchunks + s - 1) / s, ns = (nchunks + sc - 1) / sc;
-      const int64_t cst = cost2(sc, ns);
-      if (cst < best2) {
-        best2 = cst;
-        seg2 = sc;
-        ns2 = ns;
+    int64_t best2 = -1;
+    for (int per_cu = 1; per_cu <= (f32 ? 1 : 2); ++per_cu) {
+      const int64_t g2 = per_cu * (int64_t)ncu, nq = queues(g2), qch = (nchains + nq - 1) / nq;
+      const int64_t cu_q = std::max<int64_t>(ncu / nq, 1);  // units per queue
+      auto pass = [&](int64_t items, int64_t chunk_cost) {
+        if (items <= cu_q) return items > 0 ? chunk_cost : int64_t(0);
+        const int64_t slots = per_cu * cu_q, rounds = (items + slots - 1) / slots;
+        return per_cu == 1 ? rounds * chunk_cost : rounds * chunk_cost * 3 / 2;
+      };
+      for (int64_t s = 1; s <= std::min<int64_t>(nchunks, 64) && s * nchains < (int64_t(1) << 30); ++s) {
+        const int64_t sc = (nchunks + s - 1) / s, ns = (nchunks + sc - 1) / sc;
+        // the fold between the passes: a launch (about 1.3 chunks) and, per chain and
+        // segment, a state read and written (64 KB: 0.007 of a chunk at 4 TB/s)
+        const int64_t fold = ns > 1 ? 130 + (ns - 1) * nchains * 71 / 100 : 0;
+        const int64_t cst = pass((ns - 1) * qch, lc * sc + 100) + fold + pass(ns * qch, 100 * sc + 100);
+        if (best2 < 0 || cst < best2) {
+          best2 = cst;
+          seg2 = sc;
+          ns2 = ns;
+          grid2 = g2;
+        }
       }
     }
     // (the one-pass cost, best_cost, in whole chunks; two passes must win by 3%)
@@ -1410,7 +1445,7 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   if (two_pass) {
     best_seg = seg2;
     best_ns = ns2;
-    grid = ncu;
+    grid = grid2;
   }
   // tuning overrides: chunks per segment, workgroups
   if (const int64_t sc = knob(kKnobSsdSegmentChunks); sc > 0) {
@@ -1478,6 +1513,14 @@ void fill_common(K& k, const SSDArgs& a, const SsdPlan& p, int hshift, void* ws)
   k.nstates = (int)(a.batch * a.H);
 }
 
+// Between the two passes: the segments' entering states (ssd_fold_states_kernel)
+template <typename K>
+void launch_fold(const K& k, hipStream_t s) {
+  const int64_t threads = (int64_t)k.nstates * (P * NS / 4);
+  hipLaunchKernelGGL(ssd_fold_states_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, k.carry, k.lam,
+                     k.h0, k.nstates, k.nseg - 1);
+}
+
 // fp32 activations: ssd_cb_f32_kernel and ssd_chunk_f32_kernel on the same plan
 // (a: the problem in heads of 64 columns; hshift: log2 of the caller's head_dim / 64)
 hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, int hshift, void* ws, hipStream_t s) {
@@ -1493,8 +1536,10 @@ hipError_t launch_ssd_chunk_f32(const SSDArgs& a, const SsdPlan& p, int hshift, 
   if (!p.two_pass) {
     hipLaunchKernelGGL(ssd_chunk_f32_kernel<kChained>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
   } else {
-    if (p.nseg > 1)
+    if (p.nseg > 1) {
       hipLaunchKernelGGL(ssd_chunk_f32_kernel<kLocal>, dim3((unsigned)p.grid_local), dim3(256), 0, s, k);
+      launch_fold(k, s);
+    }
     hipLaunchKernelGGL(ssd_chunk_f32_kernel<kFolded>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
   }
   return hipGetLastError();
@@ -1513,8 +1558,10 @@ static hipError_t launch_ssd_chunk_bf16(const SSDArgs& a, const SsdPlan& p, int 
                      0, s, (const uint16_t*)a.B, (const uint16_t*)a.C, (float*)k.cb, (int)a.L, (int)a.G, k.nchunks, nblk,
                      k.queue, (int)(p.queue_bytes / 4), knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
   if (p.two_pass) {
-    if (p.nseg > 1)
+    if (p.nseg > 1) {
       hipLaunchKernelGGL((ssd_chunk_kernel<1, kLocal>), dim3((unsigned)p.grid_local), dim3(256), kCkBytes, s, k);
+      launch_fold(k, s);
+    }
     hipLaunchKernelGGL((ssd_chunk_kernel<1, kFolded>), dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
   } else if (p.hpw == 2) {
     hipLaunchKernelGGL((ssd_chunk_kernel<2, kChained>), dim3((unsigned)p.grid), dim3(512), kCkBytes, s, k);

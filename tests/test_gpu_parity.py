@@ -373,6 +373,8 @@ def test_ssd_narrow_state_equals_zero_padded(case, tuning):
 TWO_PASS_CASES = [
     # chunks per segment (0: the plan's), workgroups (0: the plan's), batch, seqlen, H, P, N, G, act, h0
     (1, 0, 1, 300, 2, 64, 128, 1, "bf16", True),
+    (0, 0, 1, 1, 2, 64, 128, 1, "bf16", True),    # one chunk: the second pass alone
+    (0, 0, 2, 5000, 6, 64, 128, 2, "bf16", True), # the plan's cut and grid
     (3, 5, 2, 1000, 4, 64, 128, 2, "bf16", False),
     (0, 0, 1, 4000, 2, 64, 128, 1, "bf16", True),
     (2, 0, 1, 700, 2, 128, 128, 1, "bf16", True),
