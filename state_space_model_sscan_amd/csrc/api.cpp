@@ -282,6 +282,7 @@ sscan_status ssd_fwd(const sscan_ssd_desc* d, const void* x, const void* dt_raw,
   sscan_status st = check_ssd_desc(d, false);
   if (st != SSCAN_OK) return st;
   sscan::SSDArgs a = ssd_args(d);
+  if (noalloc) a.ws_cap = sscan::kScratchBytes;  // the plan fits the static scratch where it can
   const int64_t b = a.batch, L = a.L, H = a.H, P = a.P, N = a.N, G = a.G;
   const size_t es = a.bf16 ? 2 : 4;
   const size_t act_bytes = (size_t)(b * L * H * P) * es, bc_bytes = (size_t)(b * L * G * N) * es;

@@ -74,6 +74,7 @@ struct SSDArgs {
   void* y;
   float* h_out;
   float* states;
+  size_t ws_cap;  // nonzero: the chunk path's plan keeps its workspace within this (else one pass)
 };
 
 // Token-loop SSD (tokenloop.hip): any dtype, state_dim <= 128, per-token states.

@@ -1362,8 +1362,8 @@ struct SsdPlan {
 // measured at one batch row of the Mamba-2 2.7B layer: 0.57 and 0.42)
 constexpr int64_t kLocalCostBf16 = 55, kLocalCostF32 = 45;
 
-// (a: the problem in heads of 64 columns)
-SsdPlan ssd_plan(const SSDArgs& a) {
+// (a: the problem in heads of 64 columns; allow_two: two passes may be chosen)
+SsdPlan ssd_plan(const SSDArgs& a, bool allow_two = true) {
   const bool f32 = !a.bf16;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1413,7 +1413,7 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   // 1.49-1.55 at one and two batch rows of the Mamba-2 2.7B layer).
   bool two_pass = false;
   int64_t seg2 = nchunks, ns2 = 1, grid2 = ncu;
-  const int tp = knob(kKnobSsdTwoPass);  // 1: one pass; 2: two passes
+  const int tp = allow_two ? knob(kKnobSsdTwoPass) : 1;  // 1: one pass; 2: two passes
   if (p.hpw == 1 && tp != 1) {
     const int64_t lc = f32 ? kLocalCostF32 : kLocalCostBf16;
     int64_t best2 = -1;
@@ -1477,6 +1477,9 @@ SsdPlan ssd_plan(const SSDArgs& a) {
   p.pad_bc_bytes = a.N < NS ? ((size_t)(a.batch * a.L * a.G) * NS * es + 255) / 256 * 256 : 0;
   p.pad_state_bytes = a.N < NS ? state_bytes : 0;
   p.ws_bytes = p.pad_off + 2 * p.pad_bc_bytes + 2 * p.pad_state_bytes;
+  // a capped workspace (the allocation-free entry point's scratch) that two passes
+  // would overflow: one pass, which needs less
+  if (two_pass && a.ws_cap && p.ws_bytes > a.ws_cap) return ssd_plan(a, false);
   return p;
 }
 

@@ -2,8 +2,9 @@
 against sscan_ssd_fwd with a caller's workspace, through the C ABI: the same kernels
 and plan, so the results must be bit-identical. Two calls in a row, the second on a
 smaller problem, for the MFMA chunk paths, bf16 and fp32 (with state hand-offs between
-segments in the scratch), and for the token-loop path (slice carries in the scratch); a problem
-that needs more scratch than there is is refused before any launch."""
+segments in the scratch), and for the token-loop path (slice carries in the scratch); where
+two passes would not fit the scratch the call takes one; a problem that needs more scratch
+than there is is refused before any launch."""
 import numpy as np
 import pytest
 import torch
@@ -86,6 +87,25 @@ def test_noalloc_token_loop_path_two_calls():
     finally:
         bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0)
     _both(gen.make_ssd(1, 100, 2, 64, 128, act="bf16", seed=95, gate=True, h0=True), want_states=True)
+
+
+def test_noalloc_takes_one_pass_where_two_would_not_fit():
+    """8 chains of 1024 chunks: the plan takes two passes, whose first-pass states and
+    C B^T tiles need more than the static scratch; the allocation-free call takes one
+    pass instead (C B^T tiles only: 10.5 MB), bit-identical to the workspace call forced
+    to one pass, and is not refused."""
+    inp = gen.make_ssd(1, 65536, 8, 64, 128, act="bf16", seed=98, gate=True, h0=True)
+    args = _args(inp)
+    say("noalloc one-pass fallback", inp.x.shape)
+    try:
+        bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 1)
+        y1, h1, _ = bd.sscan_ssd_fwd(*args)
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 0)
+    y2, h2, _ = bd.sscan_ssd_fwd_noalloc(*args)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1.float()).all() and torch.isfinite(h1).all()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
 def test_noalloc_refuses_a_problem_larger_than_the_scratch():
