@@ -623,6 +623,35 @@ def test_ssd_zero_length_sequence_passes_state_through(act):
             assert not hg.any()
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_batch_zero_calls_are_no_ops(act):
+    """batch 0 (every tensor empty) through every entry point: each call succeeds and
+    launches nothing that reads or writes (the outputs have no elements)."""
+    m = gen.make_mamba1(0, 7, 64, 16, act=act, seed=30, gate=True, h0=True)
+    x, dt, z, B, C = (dev(a, act) for a in (m.x, m.dt_raw, m.z, m.B, m.C))
+    y, h, _ = bd.sscan_mamba1_fwd(x, dt, par(m.dt_bias), par(m.A_log), B, C, par(m.D), z, par(m.h0))
+    assert y.numel() == 0 and h.numel() == 0
+    one = lambda t: t[:, :1].contiguous()
+    y, h = bd.sscan_step(par(m.h0), one(x), one(dt), par(m.dt_bias), par(m.A_log), one(B), one(C), par(m.D), one(z))
+    assert y.numel() == 0 and h.numel() == 0
+    s = gen.make_ssd(0, 70, 4, 64, 128, act=act, seed=30, gate=True, h0=True)
+    x, dt, z, B, C = (dev(a, act) for a in (s.x, s.dt_raw, s.z, s.B, s.C))
+    for fwd in (bd.sscan_ssd_fwd, bd.sscan_ssd_fwd_noalloc):
+        y, h, _ = fwd(x, dt, par(s.dt_bias), par(s.A_log), B, C, par(s.D), z, par(s.h0))
+        assert y.numel() == 0 and h.numel() == 0
+    y, h = bd.sscan_ssd_step(par(s.h0), one(x), one(dt), par(s.dt_bias), par(s.A_log), one(B), one(C),
+                             par(s.D), one(z))
+    assert y.numel() == 0 and h.numel() == 0
+    alpha = bd.sscan_ssd_attention(dt, par(s.dt_bias), par(s.A_log), B, C)
+    assert alpha.numel() == 0
+    w = torch.ones(64, 4, device="cuda")
+    out, st = bd.sscan_conv1d_silu(dev(m.x, act), w, conv_state_out=torch.empty(0, 64, 3, device="cuda"))
+    assert out.numel() == 0 and st.numel() == 0
+    out = bd.sscan_gated_rmsnorm(dev(m.x, act), dev(m.z, act), torch.ones(64, device="cuda"), 1e-5)
+    assert out.numel() == 0
+    torch.cuda.synchronize()
+
+
 def test_host_tensors_are_refused():
     inp = gen.make_mamba1(1, 4, 64, 16, act="f32", seed=28)
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32))
