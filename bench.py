@@ -47,6 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+VALU_CLOCK_HZ = 2.4e9            # MI355X peak engine clock, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, published
 F32_MFMA_PEAK_TFLOPS = 157.3     # dense fp32 MFMA, published
 MFMA_FLOPS_PER_MOP = 512         # SQ_INSTS_VALU_MFMA_MOPS_* counts units of 512 FLOPs
@@ -433,7 +434,17 @@ def attach_counters(d, cs):
         r["traffic_over_algorithmic"] = cs["traffic_bytes"] / r["algorithmic_bytes"]
         r["counter_kernel"] = cs.get("kernel")
     if "valu" in cs:
-        r["valu"] = cs["valu"]
+        r["valu"] = dict(cs["valu"])
+        # VALU issue against its peak: a wave64 VALU instruction occupies a SIMD for 4
+        # cycles and a transcendental for 8 (measured), so the counted instructions
+        # need (all + transcendental) * 4 SIMD-cycles; the chip has 256 CUs x 4 SIMDs at
+        # 2.4 GHz over the kernel's time
+        ksec = d["kernel_ms"]["mean"] * 1e-3
+        need = (cs["valu"]["wave_instructions"] + cs["valu"]["transcendental"]) * 4
+        have = NUM_CU * 4 * VALU_CLOCK_HZ * ksec
+        r["valu"]["issue_frac"] = need / have
+        r["valu"]["issue_note"] = ("(SQ_INSTS_VALU + SQ_INSTS_VALU_TRANS_F32) x 4 SIMD-cycles over "
+                                   "256 CUs x 4 SIMDs x 2.4 GHz x the kernel time")
     if "mfma" in d and "mfma_flops" in cs:
         ksec = d["kernel_ms"]["mean"] * 1e-3
         m = d["mfma"]
