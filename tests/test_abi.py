@@ -387,3 +387,61 @@ def test_binding_refuses_misshaped_tensors():
         bd.sscan_gated_rmsnorm(_cpu(4, 64), _cpu(4, 65), _cpu(64), 1e-5)
     with pytest.raises(ValueError, match="weight"):
         bd.sscan_gated_rmsnorm(_cpu(4, 64), _cpu(4, 64), _cpu(63), 1e-5)
+
+
+# A C consumer of the header: prints the descriptor layouts, the constants and what
+# the library answers without a GPU (version, status text, a workspace query).
+_C_CONSUMER = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "sscan.h"
+#define OFF(T, f) (long)offsetof(T, f)
+int main(void) {
+  sscan_mamba1_desc m = {8, 2048, 1536, 16, 1, SSCAN_BF16, 0.0f};
+  printf("mamba1 %ld %ld %ld %ld\n", (long)sizeof(sscan_mamba1_desc), OFF(sscan_mamba1_desc, ngroups),
+         OFF(sscan_mamba1_desc, act), OFF(sscan_mamba1_desc, bc_rms_eps));
+  printf("ssd %ld %ld %ld %ld\n", (long)sizeof(sscan_ssd_desc), OFF(sscan_ssd_desc, chunk),
+         OFF(sscan_ssd_desc, act), OFF(sscan_ssd_desc, reserved));
+  printf("conv %ld %ld %ld %ld\n", (long)sizeof(sscan_conv_desc), OFF(sscan_conv_desc, width),
+         OFF(sscan_conv_desc, act), OFF(sscan_conv_desc, reserved));
+  printf("consts %d %d %u\n", SSCAN_ABI_VERSION, SSCAN_SSD_GIVEUP_WORD_OFFSET, (unsigned)SSCAN_NOALLOC_SCRATCH_BYTES);
+  printf("version %d\n", sscan_abi_version());
+  printf("status %s\n", sscan_status_string(SSCAN_ERR_ALIGN));
+  printf("workspace %zu\n", sscan_mamba1_workspace_size(&m));
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_is_plain_c_and_matches_the_binding(tmp_path, lang):
+    """include/sscan.h compiles on its own as strict C99 and as C++ (extern "C"), a
+    program built against it links to libsscan.so and runs without a GPU, and the
+    descriptor layouts it sees are the ones the ctypes binding passes."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / ("consumer.c" if lang == "c" else "consumer.cpp")
+    src.write_text(_C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(bd.LIB_PATH)
+    std = ["-std=c99", "-pedantic"] if lang == "c" else ["-std=c++17"]
+    cmd = [cc, *std, "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+           "-L" + libdir, "-l:libsscan.so", "-Wl,-rpath," + libdir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    out = dict(line.split(" ", 1) for line in r.stdout.strip().splitlines())
+    for name, cls, fields in (("mamba1", bd.Mamba1Desc, ("ngroups", "act", "bc_rms_eps")),
+                              ("ssd", bd.SSDDesc, ("chunk", "act", "reserved")),
+                              ("conv", bd.ConvDesc, ("width", "act", "reserved"))):
+        want = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
+        assert [int(v) for v in out[name].split()] == want, (name, out[name], want)
+    assert out["consts"].split() == ["3", str(bd.SSD_GIVEUP_WORD_OFFSET), str(16 << 20)]
+    assert out["version"] == "3"
+    assert out["status"] == bd.lib().sscan_status_string(6).decode()
+    d = bd.Mamba1Desc(8, 2048, 1536, 16, 1, bd.BF16, 0.0)
+    assert int(out["workspace"]) == bd.sscan_mamba1_workspace_size(d)
