@@ -429,7 +429,7 @@ def test_header_is_plain_c_and_matches_the_binding(tmp_path, lang):
     libdir = os.path.dirname(bd.LIB_PATH)
     std = ["-std=c99", "-pedantic"] if lang == "c" else ["-std=c++17"]
     cmd = [cc, *std, "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
-           "-L" + libdir, "-l:libsscan.so", "-Wl,-rpath," + libdir]
+           bd.LIB_PATH, "-Wl,-rpath," + libdir]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
