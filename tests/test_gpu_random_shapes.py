@@ -6,7 +6,8 @@ Mamba-1 the row, quad and general prompt kernels and the token loop (state_dim u
 256, groups, the B/C norm, slices of long sequences), for the SSD the MFMA chunk
 kernels (bf16 and fp32, head_dim 64 or 128, state_dim 64 to 128, with segments) and the
 token loop (other head and state sizes, per-token states). Lengths include 1, chunk and tile
-edges and ragged tails. Sizes stay small enough for the oracle to take well under a
+edges and ragged tails; some cases drop 5% of the tokens to a zero step (dt_raw = -inf) and
+some SSD cases draw A over the pages' whole span (ln 4e-4 .. ln 36316). Sizes stay small enough for the oracle to take well under a
 second per case."""
 import numpy as np
 import pytest
@@ -30,7 +31,7 @@ def _need_gpu():
     bd.lib()
 
 
-def _mamba1_cases(n=20, seed=20261203):
+def _mamba1_cases(n=32, seed=20261203):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -47,11 +48,12 @@ def _mamba1_cases(n=20, seed=20261203):
                           gate=bool(rng.random() < 0.7), h0=bool(rng.random() < 0.5),
                           bc_eps=float(rng.choice([0.0, 0.0, 1e-6, 1e-3])),
                           want_states=bool(rng.random() < 0.25 and b * L * Dc * N < 4_000_000),
+                          zero_step_frac=float(rng.choice([0.0, 0.0, 0.0, 0.05])),
                           seed=int(rng.integers(1 << 30))))
     return cases
 
 
-def _ssd_cases(n=20, seed=20261204):
+def _ssd_cases(n=32, seed=20261204):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -75,6 +77,8 @@ def _ssd_cases(n=20, seed=20261204):
             continue
         cases.append(dict(batch=b, seqlen=L, nheads=H, head_dim=P, state_dim=N, ngroups=G, act=act,
                           gate=bool(rng.random() < 0.7), h0=bool(rng.random() < 0.5), want_states=states,
+                          zero_step_frac=float(rng.choice([0.0, 0.0, 0.0, 0.05])),
+                          A_log_mode=str(rng.choice(["random", "random", "random", "wide"])),
                           seed=int(rng.integers(1 << 30))))
     return cases
 
