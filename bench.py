@@ -730,6 +730,19 @@ def bench_ssd_shape(steps, warmup, torch, bd, gen, label, **overrides):
     return d
 
 
+def bench_ssd_split(steps, warmup, torch, bd, gen):
+    """The Mamba-2 2.7B layer's SSD (bf16, 4 x 8192 tokens) in the precise form of the
+    bf16 chunk path (SSCAN_TUNE_SSD_SPLIT_STATE: the state as C reads it and w x as two
+    bf16 parts each, twice the MFMAs of those two products)."""
+    prev = bd.set_tuning(bd.TUNE_SSD_SPLIT_STATE, 1)
+    try:
+        d, _ = bench_workload(4, steps, warmup, torch, bd, gen, gen.make_workload(4))
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_SPLIT_STATE, prev)
+    d["workload"] = "mamba2-2.7b layer, bf16, precise form (state and w x as two bf16 parts)"
+    return d
+
+
 def bench_attention(steps, warmup, torch, bd, gen, L=2048):
     """The hidden attention map of the first L tokens of one batch row of the Mamba-2 2.7B
     workload's distributions (80 heads, one group, state 128): alpha [1, L, L, 80] fp32,
@@ -840,6 +853,8 @@ def main():
         extra["ssd_state_dim_64"] = bench_ssd_shape(
             max(5, args.steps // 4), 3, torch, bd, gen,
             "mamba2-2.7b layer with state_dim 64, bf16 (4 x 8192 tokens x 80 heads x 64)", state_dim=64)
+        log("bench: SSD, precise form")
+        extra["ssd_split_state"] = bench_ssd_split(max(5, args.steps // 4), 3, torch, bd, gen)
 
     cfg = gen.WORKLOADS[MAIN]
     roof = dict(main_d["roofline"])

@@ -286,11 +286,17 @@ typedef enum {
                                        default one head per workgroup; same results; bf16 only) */
   SSCAN_TUNE_SSD_F32_TOKEN_LOOP = 6, /* nonzero: fp32 activations of sscan_ssd_fwd take the token loop
                                        instead of the fp32 MFMA chunk path */
-  SSCAN_TUNE_SSD_TWO_PASS = 7       /* the SSD chunk path's form: 1 one pass (a head's segments hand
+  SSCAN_TUNE_SSD_TWO_PASS = 7,      /* the SSD chunk path's form: 1 one pass (a head's segments hand
                                        their states on in turn), 2 two passes (every segment but the
                                        last from a zero state, then all segments at once from states
                                        folded from those); 0 the library's choice (two passes when a
                                        problem has too few heads x batch rows to fill the GPU) */
+  SSCAN_TUNE_SSD_SPLIT_STATE = 8    /* nonzero: the bf16 SSD chunk path carries the state as C reads
+                                       it and the weighted inputs w x that update it as two bf16 parts
+                                       each (hi, and the rounding hi leaves out), about 16 significant
+                                       bits instead of 8: closer results for heads whose slow decays
+                                       make the state sum thousands of tokens, at twice the MFMA work of
+                                       those two products (one head per workgroup) */
 } sscan_tune_knob;
 int64_t sscan_set_tuning(int knob, int64_t value);
 

@@ -30,6 +30,7 @@ TUNE_M1_LANES, TUNE_SSD_SEGMENT_CHUNKS, TUNE_SSD_WORKGROUPS, TUNE_SSD_GIVE_UP = 
 TUNE_SSD_HEADS_PER_WORKGROUP = 5
 TUNE_SSD_F32_TOKEN_LOOP = 6
 TUNE_SSD_TWO_PASS = 7
+TUNE_SSD_SPLIT_STATE = 8
 # Byte offset of the give-up word in the workspace of an SSD call on the MFMA chunk path.
 SSD_GIVEUP_WORD_OFFSET = 512
 

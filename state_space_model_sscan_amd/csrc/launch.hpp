@@ -16,7 +16,8 @@ enum Knob {
   kKnobSsdHeadsPerWorkgroup = 5,  // 2: two heads per workgroup of the chunk kernel where they share a group
   kKnobSsdF32TokenLoop = 6,  // nonzero: fp32 SSD activations take the token loop, not the fp32 chunk kernel
   kKnobSsdTwoPass = 7,       // SSD chunk kernels: 1 one pass (chained segments), 2 two passes; 0 the plan's choice
-  kKnobCount = 8
+  kKnobSsdSplitState = 8,    // nonzero: the bf16 SSD chunk kernel carries the state and w x as two bf16 parts
+  kKnobCount = 9
 };
 int64_t knob(int which);
 

@@ -384,9 +384,13 @@ struct Prefetch {
 // tile is loaded once, then masked with each head's decays; the two heads' waves
 // share the SIMDs, so one head's MFMA and memory latencies hide behind the other's
 // work.
-template <int HPW, int MODE>
+// SPLIT: the state as C reads it and the weighted inputs w x that update it are each
+// carried as two bf16 parts (hi = RNE(v), lo = RNE(v - hi)), about 16 significant bits
+// instead of 8, at twice the MFMAs of those two products (the precise form, on request).
+template <int HPW, int MODE, bool SPLIT = false>
 __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(SsdK k) {
   static_assert(MODE == kChained || HPW == 1, "two passes: one head per workgroup");
+  static_assert(!SPLIT || HPW == 1, "the precise form: one head per workgroup");
   constexpr bool Y = MODE != kLocal;  // the pass computes y (kLocal: only the state)
   constexpr int NW = 4 * HPW;      // waves
   constexpr int BCIT = 4 / HPW;    // rows of B (and of C) a thread stages
@@ -723,15 +727,19 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     for (int it = 0; it < 4; ++it) yacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < (Y ? 4 : 0); ++kb) {
-      u32x4 sv;
-      sv[0] = pack2(hacc[2 * kb][0], hacc[2 * kb][1]);
-      sv[1] = pack2(hacc[2 * kb][2], hacc[2 * kb][3]);
-      sv[2] = pack2(hacc[2 * kb + 1][0], hacc[2 * kb + 1][1]);
-      sv[3] = pack2(hacc[2 * kb + 1][2], hacc[2 * kb + 1][3]);
+      u32x4 sv, sl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = hacc[2 * kb + (q >> 1)][2 * (q & 1)], a1 = hacc[2 * kb + (q >> 1)][2 * (q & 1) + 1];
+        sv[q] = pack2(a0, a1);
+        if constexpr (SPLIT) sl[q] = pack2(a0 - lo_f(sv[q]), a1 - hi_f(sv[q]));  // what hi leaves out
+      }
       const bf16x8 aop = as_bf16x8(sv);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        yacc[it] = mfma(aop, as_bf16x8(lds128(sCk + (16 * it + li) * LDC + 32 * kb + 8 * lg)), yacc[it]);
+        const bf16x8 cop = as_bf16x8(lds128(sCk + (16 * it + li) * LDC + 32 * kb + 8 * lg));
+        yacc[it] = mfma(aop, cop, yacc[it]);
+        if constexpr (SPLIT) yacc[it] = mfma(as_bf16x8(sl), cop, yacc[it]);
       }
     }
 #pragma unroll
@@ -744,15 +752,21 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
     // ---- S = exp(cs_last) S + B^T (w x). A operand: B^T rows n = 16nt + li, k = j
     // (transposing loads of B); B operand: w_j x[j][16wq + li] from the x^T fragments
     // (both in k order; sW holds w in k order).
-    bf16x8 wxb[2];
+    bf16x8 wxb[2], wxl[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x4 w0 = wj[kb][0], w1 = wj[kb][1];
       const u32x4 v = xa[kb];
-      wxb[kb] = as_bf16x8(u32x4{pack2(lo_f(v[0]) * w0[0], hi_f(v[0]) * w0[1]),
-                                pack2(lo_f(v[1]) * w0[2], hi_f(v[1]) * w0[3]),
-                                pack2(lo_f(v[2]) * w1[0], hi_f(v[2]) * w1[1]),
-                                pack2(lo_f(v[3]) * w1[2], hi_f(v[3]) * w1[3])});
+      const float p[8] = {lo_f(v[0]) * w0[0], hi_f(v[0]) * w0[1], lo_f(v[1]) * w0[2], hi_f(v[1]) * w0[3],
+                          lo_f(v[2]) * w1[0], hi_f(v[2]) * w1[1], lo_f(v[3]) * w1[2], hi_f(v[3]) * w1[3]};
+      u32x4 hv, lv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hv[q] = pack2(p[2 * q], p[2 * q + 1]);
+        if constexpr (SPLIT) lv[q] = pack2(p[2 * q] - lo_f(hv[q]), p[2 * q + 1] - hi_f(hv[q]));
+      }
+      wxb[kb] = as_bf16x8(hv);
+      if constexpr (SPLIT) wxl[kb] = as_bf16x8(lv);
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
@@ -763,7 +777,9 @@ __global__ __launch_bounds__(256 * HPW, HPW == 1 ? 2 : 1) void ssd_chunk_kernel(
         const int k0 = 32 * kb + 8 * lg;
         const u32x2 lo = lds_tr(sB + (k0 + 2 * (li >> 2)) * LDB + 16 * nt + 4 * (li & 3));
         const u32x2 hi = lds_tr(sB + (k0 + 1 + 2 * (li >> 2)) * LDB + 16 * nt + 4 * (li & 3));
-        hacc[nt] = mfma(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), wxb[kb], hacc[nt]);
+        const bf16x8 bop = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        hacc[nt] = mfma(bop, wxb[kb], hacc[nt]);
+        if constexpr (SPLIT) hacc[nt] = mfma(bop, wxl[kb], hacc[nt]);
       }
     }
 
@@ -1351,6 +1367,7 @@ SSDArgs by_64_columns(const SSDArgs& a) {
 // the first pass's (kFolded). The model counts the rounds of each pass.
 struct SsdPlan {
   int hpw, nchains, seg_chunks, nseg, nq, grid;
+  bool split;      // bf16: the precise form (state and w x as two bf16 parts each)
   bool two_pass;   // kLocal and kFolded passes (else one kChained pass)
   int grid_local;  // workgroups of the kLocal pass
   size_t queue_bytes, carry_bytes, lam_bytes, cb_bytes, ws_bytes;
@@ -1376,7 +1393,9 @@ SsdPlan ssd_plan(const SSDArgs& a, bool allow_two = true) {
   // than hiding latency.
   const int64_t hpg = a.H / a.G;
   // (fp32 activations: one head per workgroup, the only form of that kernel)
-  p.hpw = (!f32 && knob(kKnobSsdHeadsPerWorkgroup) == 2 && a.H % 2 == 0 && hpg % 2 == 0) ? 2 : 1;
+  // The precise form on request (bf16; one head per workgroup).
+  p.split = !f32 && knob(kKnobSsdSplitState) != 0;
+  p.hpw = (!f32 && !p.split && knob(kKnobSsdHeadsPerWorkgroup) == 2 && a.H % 2 == 0 && hpg % 2 == 0) ? 2 : 1;
   const int64_t nchains = a.batch * a.H / p.hpw, nchunks = std::max<int64_t>((a.L + Q - 1) / Q, 1);
   p.nchains = (int)nchains;
   // Two workgroups per unit (the occupancy the one-head kernel is built for) with
@@ -1560,7 +1579,18 @@ static hipError_t launch_ssd_chunk_bf16(const SSDArgs& a, const SsdPlan& p, int 
   hipLaunchKernelGGL(ssd_cb_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(nblk, 1 << 20))), dim3(640),
                      0, s, (const uint16_t*)a.B, (const uint16_t*)a.C, (float*)k.cb, (int)a.L, (int)a.G, k.nchunks, nblk,
                      k.queue, (int)(p.queue_bytes / 4), knob(kKnobSsdGiveUp) != 0 ? 1u : 0u);
-  if (p.two_pass) {
+  if (p.split) {
+    if (p.two_pass) {
+      if (p.nseg > 1) {
+        hipLaunchKernelGGL((ssd_chunk_kernel<1, kLocal, true>), dim3((unsigned)p.grid_local), dim3(256), kCkBytes, s,
+                           k);
+        launch_fold(k, s);
+      }
+      hipLaunchKernelGGL((ssd_chunk_kernel<1, kFolded, true>), dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+    } else {
+      hipLaunchKernelGGL((ssd_chunk_kernel<1, kChained, true>), dim3((unsigned)p.grid), dim3(256), kCkBytes, s, k);
+    }
+  } else if (p.two_pass) {
     if (p.nseg > 1) {
       hipLaunchKernelGGL((ssd_chunk_kernel<1, kLocal>), dim3((unsigned)p.grid_local), dim3(256), kCkBytes, s, k);
       launch_fold(k, s);

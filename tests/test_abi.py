@@ -257,7 +257,9 @@ def test_tuning_knobs_are_validated_and_restored():
     assert bd.set_tuning(bd.TUNE_SSD_F32_TOKEN_LOOP, 0) == 1
     assert bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 2) == 0
     assert bd.set_tuning(bd.TUNE_SSD_TWO_PASS, 0) == 2
-    assert L.sscan_set_tuning(bd.TUNE_SSD_TWO_PASS + 1, 1) == -1   # one past the last knob
+    assert bd.set_tuning(bd.TUNE_SSD_SPLIT_STATE, 1) == 0
+    assert bd.set_tuning(bd.TUNE_SSD_SPLIT_STATE, 0) == 1
+    assert L.sscan_set_tuning(bd.TUNE_SSD_SPLIT_STATE + 1, 1) == -1   # one past the last knob
     with pytest.raises(ValueError):
         bd.set_tuning(42, 1)
 

@@ -12,7 +12,7 @@ import oracle
 from state_space_model_sscan_amd import binding as bd
 from state_space_model_sscan_amd import inputs as gen
 
-from _gpu import check, check_all, dev, host, par, run_mamba1, run_ssd, say, ssd_chunk_path
+from _gpu import BF16_RELL2, check, check_all, dev, host, par, rel_l2, run_mamba1, run_ssd, say, ssd_chunk_path
 
 pytestmark = pytest.mark.gpu
 
@@ -162,6 +162,48 @@ def test_workload4_ssd_full_size():
     got = run_ssd(inp)
     say("  oracle")
     check_all(inp, got, oracle.run_inputs(inp), "ssd")
+
+
+SPLIT_CASES = [
+    # two passes (the plan's, 0) or one pass (1), chunks per segment, batch, seqlen, H, G, h0
+    (0, 0, 1, 8192, 8, 1, True),     # few chains: two passes
+    (1, 0, 2, 1000, 6, 2, True),     # one pass, whole chains
+    (1, 2, 2, 700, 4, 1, False),     # one pass, segments of two chunks handing their states on
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "tp%d_seg%d_b%d_L%d_H%d_G%d_h%d" % c)
+def test_ssd_split_state_parity(case, tuning):
+    """The precise form of the bf16 chunk path (state and w x as two bf16 parts each)
+    against the oracle, in one pass and in two."""
+    tp, seg, b, L, H, G, h0 = case
+    say("ssd split state", case)
+    tuning(bd.TUNE_SSD_SPLIT_STATE, 1)
+    if tp:
+        tuning(bd.TUNE_SSD_TWO_PASS, tp)
+    if seg:
+        tuning(bd.TUNE_SSD_SEGMENT_CHUNKS, seg)
+    inp = gen.make_ssd(b, L, H, 64, 128, G, act="bf16", seed=L + H, gate=True, h0=h0)
+    check_all(inp, run_ssd(inp), oracle.run_inputs(inp), "ssd")
+
+
+def test_ssd_split_state_long_memory(tuning):
+    """With slow decays the state sums thousands of tokens and its bf16 rounding as C reads
+    it, with that of w x, sets y's error. The precise form keeps both to about 16
+    significant bits: y and the final state come out closer to the oracle than on the
+    default form, within half the bf16 budget."""
+    inp = gen.make_ssd(1, 8192, 8, 64, 128, act="bf16", seed=81, gate=True, h0=True)
+    inp.A_log = np.log(np.geomspace(4e-4, 1e-2, 8)).astype(np.float32)
+    ref = oracle.run_inputs(inp)
+    fast = run_ssd(inp)
+    tuning(bd.TUNE_SSD_SPLIT_STATE, 1)
+    precise = run_ssd(inp)
+    check_all(inp, precise, ref, "ssd")
+    e_fast = [rel_l2(fast[i], ref[i]) for i in (0, 1)]
+    e_precise = [rel_l2(precise[i], ref[i]) for i in (0, 1)]
+    say("  rel_l2 y, state: default %.3e %.3e, precise %.3e %.3e" % (*e_fast, *e_precise))
+    assert e_precise[0] < e_fast[0] and e_precise[1] < e_fast[1]
+    assert max(e_precise) <= BF16_RELL2 / 2
 
 
 @pytest.mark.parametrize("act", ["bf16", "f32"])
