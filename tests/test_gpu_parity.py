@@ -187,6 +187,18 @@ def test_ssd_split_state_parity(case, tuning):
     check_all(inp, run_ssd(inp), oracle.run_inputs(inp), "ssd")
 
 
+@pytest.mark.parametrize("split", [0, 1])
+def test_ssd_long_memory_65536_tokens(split, tuning):
+    """The long-memory heads over 65,536 tokens, in both forms of the bf16 chunk path: the
+    roundings are relative to the terms they round, so the error does not grow with the
+    length (measured: the same as at 8192 tokens)."""
+    inp = gen.make_ssd(1, 65536, 8, 64, 128, act="bf16", seed=81, gate=True, h0=True)
+    inp.A_log = np.log(np.geomspace(4e-4, 1e-2, 8)).astype(np.float32)
+    tuning(bd.TUNE_SSD_SPLIT_STATE, split)
+    say("ssd long memory, 65536 tokens, precise form" if split else "ssd long memory, 65536 tokens")
+    check_all(inp, run_ssd(inp), oracle.run_inputs(inp), "ssd")
+
+
 def test_ssd_split_state_long_memory(tuning):
     """With slow decays the state sums thousands of tokens and its bf16 rounding as C reads
     it, with that of w x, sets y's error. The precise form keeps both to about 16
