@@ -248,13 +248,16 @@ def _read_counters(outdir):
     return {k: {c: list(d.values()) for c, d in v.items()} for k, v in rec.items()}
 
 
-def collect_counters(timeout_s=240):
-    """The four counter passes of the workloads, each in a child process under rocprofv3.
-    Must run before this process touches the GPU. Returns {pass: records} or an error."""
+def collect_counters(top=None, timeout_s=240):
+    """The four counter passes of the workloads, each in a child process under rocprofv3,
+    writing their csv files under `top` (a new temporary directory when None). Must run
+    before this process touches the GPU. Returns {pass: records} or an error."""
     prof = shutil.which("rocprofv3")
     if not prof:
         return {"error": "rocprofv3 not found"}
-    top = os.path.join(ROOT, "gpurun_out", "bench_counters")
+    if top is None:
+        import tempfile
+        top = tempfile.mkdtemp(prefix="sscan_bench_counters_")
     out = {}
     for name, counters in COUNTER_PASSES:
         d = os.path.join(top, name)
@@ -770,6 +773,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-counters", action="store_true", help="skip the rocprofv3 counter passes")
     ap.add_argument("--only-main", action="store_true", help="time only the main workload")
+    ap.add_argument("--counter-dir", default=None, help="where the counter passes write their csv files "
+                    "(default: a new temporary directory)")
     ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -787,7 +792,7 @@ def main():
     # Child processes first (the counter passes), before this process touches the GPU.
     cnt = None
     if not args.no_counters and not args.only_main:
-        cnt = collect_counters()
+        cnt = collect_counters(args.counter_dir)
         if "error" in cnt:
             log("bench: counters unavailable: %s" % cnt["error"])
 
