@@ -7,7 +7,8 @@ Mamba-1 the row, quad and general prompt kernels and the token loop (state_dim u
 kernels (bf16 and fp32, head_dim 64 or 128, state_dim 64 to 128, with segments) and the
 token loop (other head and state sizes, per-token states). Lengths include 1, chunk and tile
 edges and ragged tails; some cases drop 5% of the tokens to a zero step (dt_raw = -inf) and
-some SSD cases draw A over the pages' whole span (ln 4e-4 .. ln 36316). Sizes stay small enough for the oracle to take well under a
+some SSD cases draw A over the pages' whole span (ln 4e-4 .. ln 36316), and some bf16 SSD cases
+take the chunk path's precise form. Sizes stay small enough for the oracle to take well under a
 second per case."""
 import numpy as np
 import pytest
@@ -79,6 +80,7 @@ def _ssd_cases(n=32, seed=20261204):
                           gate=bool(rng.random() < 0.7), h0=bool(rng.random() < 0.5), want_states=states,
                           zero_step_frac=float(rng.choice([0.0, 0.0, 0.0, 0.05])),
                           A_log_mode=str(rng.choice(["random", "random", "random", "wide"])),
+                          split=bool(act == "bf16" and rng.random() < 0.3),
                           seed=int(rng.integers(1 << 30))))
     return cases
 
@@ -99,7 +101,13 @@ def test_mamba1_random_shape(case):
 def test_ssd_random_shape(case):
     say("ssd random", case)
     c = dict(case)
+    split = c.pop("split")  # bf16: the chunk path's precise form (state and w x in two parts)
     inp = gen.make_ssd(c.pop("batch"), c.pop("seqlen"), c.pop("nheads"), c.pop("head_dim"), c.pop("state_dim"),
                        c.pop("ngroups"), **c)
     path = "ssd" if ssd_chunk_path(inp, inp.want_states) else "mamba1"  # the token loop computes in fp32
-    check_all(inp, run_ssd(inp), oracle.run_inputs(inp), path, states=inp.want_states)
+    prev = bd.set_tuning(bd.TUNE_SSD_SPLIT_STATE, 1 if split else 0)
+    try:
+        got = run_ssd(inp)
+    finally:
+        bd.set_tuning(bd.TUNE_SSD_SPLIT_STATE, prev)
+    check_all(inp, got, oracle.run_inputs(inp), path, states=inp.want_states)
