@@ -298,14 +298,17 @@ __device__ __forceinline__ void step_st(float* row, int q, const float (&v)[NP /
 }
 
 // Sum over the K lanes of a channel (xor butterfly inside the lane group).
+// (K = 16: the lane group is one DPP row of the wave; after the quad sums, rotating the
+// row by 4 and then by 8 lanes adds the other three quads, so every lane of the row ends
+// with the row's sum, with no round trip through the LDS crossbar)
 template <int K>
 __device__ __forceinline__ float step_sum(float v) {
-  if constexpr (K == 4) {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  } else {
-#pragma unroll
-    for (int off = K / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  static_assert(K == 4 || K == 16, "lane groups of 4 or 16");
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  if constexpr (K == 16) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
   }
   return v;
 }
