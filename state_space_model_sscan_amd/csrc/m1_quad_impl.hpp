@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void m1_quad_kernel(M1F k) {
     load_raw(raw, t0 + TILE);
     __syncthreads();
     if (t0 + TILE <= t_end) {  // uniform: every token of the tile is in the slice
-#pragma unroll 2
+#pragma unroll 4
       for (int j = 0; j < TILE / 4; ++j) compute_group(t0, j, std::false_type{});
     } else {
       for (int j = 0; j < TILE / 4; ++j) compute_group(t0, j, std::true_type{});
